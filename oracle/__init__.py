@@ -1,0 +1,43 @@
+"""Plain float64 CPU oracle for routed block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers or tables) and imports nothing from it;
+it is written directly from the source pages:
+
+* "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" (maple.link) -- 3D tiling,
+  per-block mean pooling, the routing matrix, TopK with a keep budget, the
+  index-table format and exact sparse attention over the selected blocks.
+* "NSA 算子解析（Torch/Tilelang）" (devpress.csdn.net) -- the selected-attention
+  branch with externally supplied block indices/counts and GQA.
+* "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top) -- the
+  K1 local partials and the exact LSE combine of the KV-outer schedule.
+
+Every function computes the plain definition in float64 with NumPy: no online
+softmax, no blocking, no reverse index.  Each one is pinned by the ``not gpu``
+tests in ``tests/test_oracle_*.py`` against values printed on the pages,
+closed forms, brute force and library routines.
+"""
+
+from .tiling import tile_dims, tile_index, keep_budget
+from .routing import pool_blocks, routing_matrix, select_topk
+from .attention import (
+    vsa_attention,
+    nsa_attention,
+    kvouter_partials,
+    lse_combine,
+)
+
+__all__ = [
+    "tile_dims",
+    "tile_index",
+    "keep_budget",
+    "pool_blocks",
+    "routing_matrix",
+    "select_topk",
+    "vsa_attention",
+    "nsa_attention",
+    "kvouter_partials",
+    "lse_combine",
+]

@@ -1,0 +1,204 @@
+"""Throughput of routed block-sparse attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa] [--no-cpu-baseline]
+
+A step is one pass of the routed block-sparse attention hot path over one
+batch of synthetic input already resident in HBM:
+
+  video  (default) tiling tables -> per-block mean pooling -> routing scores ->
+         TopK index table -> exact block-sparse attention, on the video-DiT
+         workload (115200 tokens = 30x48x80 grid in 4x4x4 blocks, 24 heads,
+         D=128, keep 192 of 1920 blocks).
+  nsa    NSA selected-branch attention (32768 tokens, 64 query / 4 KV heads,
+         blocks of 64, up to 16 selected), query-outer.
+  msa    KV-outer schedule + combine (65536 tokens, 64 query / 4 KV heads,
+         KV blocks of 128, 16 selected blocks), when built.
+
+Prints one JSON line.  ``value`` is the effective attention throughput of the
+whole step, 4*h*N*D*k*M / step time (the pages' FLOP count), in TFLOP/s.
+``roofline`` describes the dominant kernel, timed with HIP events on the
+stream it is launched on.  ``cpu_baseline`` times the float64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn effective TFLOP/s + ms/layer at 1 GPU; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_video(args):
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import vsa_inputs, workload
+
+    cfg = workload("video")
+    dev = torch.device("cuda:0")
+    T, H, W = cfg["grid"]
+    B, h, D, R = cfg["B"], cfg["h"], cfg["D"], cfg["R"]
+    N = T * H * W
+    x = vsa_inputs(cfg, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    J, M = bsa.tile_dims(T, H, W, *cfg["block"])
+    perm = torch.empty(J * M, dtype=torch.int32, device=dev)
+    block_len = torch.empty(J, dtype=torch.int32, device=dev)
+    inv = torch.empty(N, dtype=torch.int32, device=dev)
+    q2k_idx = torch.empty((B, h, J, R), dtype=torch.int32, device=dev)
+    q2k_num = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(bsa.route_workspace_bytes(q, J, M, R), dtype=torch.uint8, device=dev)
+
+    L = bsa._lib
+    lib = L.load()
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = bsa.api._stream(dev)
+
+    import ctypes
+    def tile():
+        L.check(lib.vsa_tile_index(T, H, W, *cfg["block"], bsa.api._ptr(perm), bsa.api._ptr(block_len),
+                                   bsa.api._ptr(inv), s_ptr))
+
+    ra = bsa.api._route_args(q, k, perm, block_len, J, M, R, R, 1.0 / D ** 0.5, q2k_idx, q2k_num, None, None, None)
+    nws = ws.numel()
+
+    def route():
+        L.check(lib.vsa_pool_route_topk(ctypes.byref(ra), bsa.api._ptr(ws), nws, s_ptr))
+
+    qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
+    qa.perm, qa.block_len, qa.J, qa.M = bsa.api._ptr(perm), bsa.api._ptr(block_len), J, M
+    qa.q2k_idx, qa.q2k_num, qa.kmax = bsa.api._ptr(q2k_idx), bsa.api._ptr(q2k_num), R
+
+    def attend():
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+
+    ev = {n: [_events() for _ in range(args.steps)] for n in ("tile", "route", "attn")}
+
+    def step(i=None):
+        for name, fn in (("tile", tile), ("route", route), ("attn", attend)):
+            if i is not None:
+                ev[name][i][0].record(stream)
+            fn()
+            if i is not None:
+                ev[name][i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in ev}
+
+    flops = 4.0 * B * h * N * D * R * M             # nominal, the pages' formula
+    pairs = bsa.metrics.vsa_valid_pairs(block_len, q2k_idx, q2k_num)
+    valid_flops = 4.0 * D * pairs
+    attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
+    # pool/route/TopK algorithmic bytes: read Q and K once, write pooled means and the index table
+    route_bytes = 2 * q.numel() * q.element_size() + 2 * B * h * J * D * 4 + B * h * J * (R + 1) * 4
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + per-cell offsets, no dataset or weights)",
+        "config": {"workload": "video_dit_vsa", "B": B, "heads": h, "grid": list(cfg["grid"]),
+                   "block": list(cfg["block"]), "D": D, "J": J, "M": M, "R": R, "tokens": N},
+        "ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "attn_tflops_nominal": round(attn_tflops, 2),
+        "attn_tflops_valid": round(valid_flops / (ms["attn"] * 1e-3) / 1e12, 2),
+        "pct_bf16_peak_attn": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "route_gbps": round(route_bytes / (ms["route"] * 1e-3) / 1e9, 1),
+        "pct_hbm_route": round(100 * route_bytes / (ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "roofline": {"kernel": "vsa_attn_kernel (bsa_forward_qouter, block mode)", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    ctx = dict(cfg=cfg, x=x, perm=perm, block_len=block_len, q2k_idx=q2k_idx, q2k_num=q2k_num, J=J, M=M)
+    return res, ctx
+
+
+def cpu_baseline_video(ctx, budget_s):
+    """Oracle on a bounded sample: pool + route + TopK of one head, and exact
+    attention of as many of that head's query blocks as fit the budget."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg, J, M = ctx["cfg"], ctx["J"], ctx["M"]
+    T, H, W = cfg["grid"]
+    D, R = cfg["D"], cfg["R"]
+    head = 0
+    Q = ctx["x"]["q"][:, :, head:head + 1].float().cpu().numpy().astype(np.float64)
+    K = ctx["x"]["k"][:, :, head:head + 1].float().cpu().numpy().astype(np.float64)
+    V = ctx["x"]["v"][:, :, head:head + 1].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    tab = oracle.tile_index(T, H, W, *cfg["block"])
+    qbar = oracle.pool_blocks(Q, tab["perm"], tab["block_len"], M)
+    kbar = oracle.pool_blocks(K, tab["perm"], tab["block_len"], M)
+    idx, num, _ = oracle.select_topk(oracle.routing_matrix(qbar, kbar), R)
+    t_route = time.perf_counter() - t0
+    done, t_attn = 0, 0.0
+    t1 = time.perf_counter()
+    while done < J and time.perf_counter() - t1 < budget_s:
+        items = [(0, 0, i) for i in range(done, min(J, done + 32))]
+        oracle.vsa_attention(Q, K, V, tab["perm"], tab["block_len"], M, idx, num, items=items)
+        done += len(items)
+    t_attn = time.perf_counter() - t1
+    # per head: route once + J query blocks of attention
+    per_head_s = t_route + t_attn * J / done
+    flops_head = 4.0 * (T * H * W) * D * R * M
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops_head / per_head_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "head 0 of the video workload: float64 pool+route+TopK over all %d blocks (%.1f s) "
+                      "and exact attention for %d of %d query blocks (%.1f s), scaled to one head"
+                      % (J, t_route, done, J, t_attn),
+            "ms_per_head": round(per_head_s * 1e3, 1)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video", choices=["video"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the routed attention shards by heads with no exchange, "
+              "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        return 2
+    res, ctx = bench_video(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_video(ctx, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

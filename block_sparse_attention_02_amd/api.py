@@ -1,0 +1,235 @@
+"""PyTorch-facing binding of libbsa (argument marshalling only).
+
+Every function takes device tensors, fills the C structs of include/bsa.h and
+enqueues the library call on the current HIP stream.  All arithmetic happens
+in the library's kernels; torch only provides memory and streams.  Outputs are
+allocated with torch when the caller does not pass them.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "tile_dims", "tile_index", "keep_budget", "pool_route_topk", "route_workspace_bytes",
+    "attention_vsa", "attention_nsa", "kvouter", "combine", "VsaGeometry", "vsa_forward",
+]
+
+
+def _lib():
+    return L.load()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _desc(t):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D [B, N, H, D] tensor")
+    if t.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    B, N, H, D = t.shape
+    return L.TDesc(B, N, H, D, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return L.BSA_BF16
+    if t.dtype == torch.float32:
+        return L.BSA_F32
+    raise TypeError("unsupported dtype %s (bf16 or float32)" % t.dtype)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libbsa works on device tensors only")
+
+
+def tile_dims(T, H, W, bT, bH, bW):
+    """(J, M) of a (T, H, W) token grid cut into (bT, bH, bW) blocks."""
+    J, M = ctypes.c_int(), ctypes.c_int()
+    L.check(_lib().bsa_tile_dims(T, H, W, bT, bH, bW, ctypes.byref(J), ctypes.byref(M)))
+    return J.value, M.value
+
+
+def tile_index(T, H, W, bT, bH, bW, device="cuda"):
+    """perm [J*M], block_len [J], inv [T*H*W] int32 tensors on ``device``."""
+    J, M = tile_dims(T, H, W, bT, bH, bW)
+    perm = torch.empty(J * M, dtype=torch.int32, device=device)
+    block_len = torch.empty(J, dtype=torch.int32, device=device)
+    inv = torch.empty(T * H * W, dtype=torch.int32, device=device)
+    L.check(_lib().vsa_tile_index(T, H, W, bT, bH, bW, _ptr(perm), _ptr(block_len), _ptr(inv),
+                                  _stream(perm.device)))
+    return perm, block_len, inv
+
+
+def keep_budget(drop_ratio, J):
+    r = _lib().vsa_budget(float(drop_ratio), int(J))
+    if r < 0:
+        raise ValueError("drop ratio must lie in [0, 1] and J >= 1")
+    return r
+
+
+def _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E):
+    return L.RouteArgs(_ptr(q), _ptr(k), _desc(q), _dtype(q), _ptr(perm), _ptr(block_len), J, M, R, kmax,
+                       scale, _ptr(q2k_idx), _ptr(q2k_num), _ptr(qbar), _ptr(kbar), _ptr(E))
+
+
+def route_workspace_bytes(q, J, M, R, kmax=None, debug=False):
+    """Workspace size of pool_route_topk for these shapes."""
+    kmax = R if kmax is None else kmax
+    placeholder = ctypes.c_void_p(256)
+    a = L.RouteArgs(placeholder, placeholder, _desc(q), _dtype(q), placeholder, placeholder, J, M, R, kmax,
+                    1.0, placeholder, placeholder, placeholder if debug else None,
+                    placeholder if debug else None, None)
+    n = ctypes.c_size_t()
+    L.check(_lib().vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug=False,
+                    out=None, workspace=None):
+    """Per-block means, routing scores and TopK index table.
+
+    q, k: [B, N, H, D] (bf16 or float32).  Returns (q2k_idx [B,H,J,kmax],
+    q2k_num [B,H,J]) and, with ``debug``, also (qbar, kbar, E) in float32.
+    """
+    _need_cuda(q, k, perm, block_len)
+    B, N, H, D = q.shape
+    kmax = R if kmax is None else int(kmax)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        q2k_idx = torch.empty((B, H, J, kmax), dtype=torch.int32, device=dev)
+        q2k_num = torch.empty((B, H, J), dtype=torch.int32, device=dev)
+    else:
+        q2k_idx, q2k_num = out
+    qbar = kbar = E = None
+    if debug:
+        qbar = torch.empty((B, H, J, D), dtype=torch.float32, device=dev)
+        kbar = torch.empty_like(qbar)
+        E = torch.empty((B, H, J, J), dtype=torch.float32, device=dev)
+    a = _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E)
+    n = ctypes.c_size_t()
+    L.check(_lib().vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    L.check(_lib().vsa_pool_route_topk(ctypes.byref(a), _ptr(workspace), n.value, _stream(dev)))
+    if debug:
+        return q2k_idx, q2k_num, qbar, kbar, E
+    return q2k_idx, q2k_num
+
+
+def _qouter_args(q, k, v, out, scale, mode, lse):
+    return L.QOuterArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), out=_ptr(out), dq=_desc(q), dkv=_desc(k),
+                        dout=_desc(out), dt=_dtype(q), scale=scale, mode=mode, lse=_ptr(lse))
+
+
+def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None):
+    """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D]."""
+    _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    B, N, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if need_lse else None
+    a = _qouter_args(q, k, v, out, scale, L.BSA_SEL_BLOCK, lse)
+    a.perm, a.block_len, a.J, a.M = _ptr(perm), _ptr(block_len), J, M
+    a.q2k_idx, a.q2k_num, a.kmax = _ptr(q2k_idx), _ptr(q2k_num), q2k_idx.shape[-1]
+    L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
+    return (out, lse) if need_lse else out
+
+
+def attention_nsa(q, k, v, block_indices, block_counts, block_size, causal=True, scale=None,
+                  need_lse=False, out=None):
+    """NSA selected-branch attention with GQA.  q [B,T,HQ,D], k/v [B,T,H,D]."""
+    _need_cuda(q, k, v, block_indices, block_counts)
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    B, T, HQ, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, HQ, T), dtype=torch.float32, device=q.device) if need_lse else None
+    a = _qouter_args(q, k, v, out, scale, L.BSA_SEL_TOKEN, lse)
+    a.blk_idx, a.blk_cnt = _ptr(block_indices), _ptr(block_counts)
+    a.S, a.BS, a.causal = block_indices.shape[-1], int(block_size), int(bool(causal))
+    L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
+    return (out, lse) if need_lse else out
+
+
+def _kv_args(q, k, v, q2k, block_size, causal, q2k_cnt, scale, chunk_cap, o_buf, lse_buf, nslot):
+    return L.KvOuterArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), dq=_desc(q), dkv=_desc(k), dt=_dtype(q),
+                         scale=scale, causal=int(bool(causal)), q2k=_ptr(q2k), q2k_cnt=_ptr(q2k_cnt),
+                         k_sel=q2k.shape[-1], BK=int(block_size), o_buf=_ptr(o_buf),
+                         lse_buf=_ptr(lse_buf), nslot=_ptr(nslot), chunk_cap=int(chunk_cap))
+
+
+def kvouter(q, k, v, q2k, block_size, causal=True, q2k_cnt=None, scale=None, chunk_cap=0,
+            workspace=None, bufs=None):
+    """KV-outer K1: returns (o_buf [B,ks,N,Hq,D] bf16, lse_buf [B,ks,N,Hq], nslot [B,N,Hkv])."""
+    _need_cuda(q, k, v, q2k, q2k_cnt)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ks = q2k.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    if bufs is None:
+        o_buf = torch.empty((B, ks, N, Hq, D), dtype=torch.bfloat16, device=dev)
+        lse_buf = torch.empty((B, ks, N, Hq), dtype=torch.float32, device=dev)
+        nslot = torch.empty((B, N, Hkv), dtype=torch.int32, device=dev)
+    else:
+        o_buf, lse_buf, nslot = bufs
+    a = _kv_args(q, k, v, q2k, block_size, causal, q2k_cnt, scale, chunk_cap, o_buf, lse_buf, nslot)
+    n = ctypes.c_size_t()
+    L.check(_lib().bsa_kvouter_ws(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    L.check(_lib().bsa_forward_kvouter(ctypes.byref(a), _ptr(workspace), n.value, _stream(dev)))
+    return o_buf, lse_buf, nslot
+
+
+def combine(o_buf, lse_buf, nslot, Hkv, need_lse=False, out=None):
+    """KV-outer K2: exact LSE merge of the partials into out [B, N, Hq, D] (bf16)."""
+    _need_cuda(o_buf, lse_buf, nslot)
+    B, ks, N, Hq, D = o_buf.shape
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=o_buf.device) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=o_buf.device) if need_lse else None
+    a = L.CombineArgs(o_buf=_ptr(o_buf), lse_buf=_ptr(lse_buf), nslot=_ptr(nslot), k_sel=ks, Hkv=Hkv,
+                      dout=_desc(out), out=_ptr(out), lse=_ptr(lse))
+    L.check(_lib().bsa_combine(ctypes.byref(a), _stream(o_buf.device)))
+    return (out, lse) if need_lse else out
+
+
+class VsaGeometry:
+    """Tiling tables of one (grid, block) geometry, built once on a device."""
+
+    def __init__(self, grid, block, device="cuda"):
+        T, H, W = grid
+        bT, bH, bW = block
+        self.grid, self.block = tuple(grid), tuple(block)
+        self.J, self.M = tile_dims(T, H, W, bT, bH, bW)
+        self.N = T * H * W
+        self.perm, self.block_len, self.inv = tile_index(T, H, W, bT, bH, bW, device=device)
+
+
+def vsa_forward(q, k, v, geom, R, kmax=None, scale=None, need_lse=False, workspace=None, index_out=None):
+    """Routed block-sparse attention: pool -> route -> TopK -> exact attention.
+
+    Returns (out, q2k_idx, q2k_num) (plus lse with ``need_lse``)."""
+    q2k_idx, q2k_num = pool_route_topk(q, k, geom.perm, geom.block_len, geom.J, geom.M, R, kmax=kmax,
+                                       scale=scale, workspace=workspace, out=index_out)
+    res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
+                        need_lse=need_lse)
+    if need_lse:
+        return res[0], q2k_idx, q2k_num, res[1]
+    return res, q2k_idx, q2k_num

@@ -1,0 +1,81 @@
+"""Build libbsa.so in-tree with hipcc for gfx950.
+
+    python -m block_sparse_attention_02_amd.build [--jobs N]
+
+Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` at the
+repository root, then linked into ``block_sparse_attention_02_amd/libbsa.so``.
+"""
+
+import argparse
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libbsa.so")
+ARCH = "gfx950"
+
+CXXFLAGS = [
+    "-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
+    "-I" + INCLUDE, "-I" + CSRC,
+    # keep the compiler from forming packed fp32 instructions by itself
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [_hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+                     if "packed-fp32-ops" not in line and line.strip())
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, msgs))
+    if verbose and msgs:
+        print(msgs, flush=True)
+    return obj
+
+
+def build(verbose=False, jobs=None):
+    """Compile every HIP source and link libbsa.so.  Returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(8, len(srcs), os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), "-shared", "--offload-arch=" + ARCH, "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(verbose=args.verbose, jobs=args.jobs))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,227 @@
+// C-ABI entry points of libbsa: argument validation on the host, then
+// stream-ordered kernel launches.  The contract is documented in include/bsa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bsa.h"
+#include "bsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bsa_status ok() {
+  g_err.clear();
+  return BSA_OK;
+}
+
+bsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a strided [B,N,H,D] view.  `vec` elements per 16-byte vector must
+// divide every stride (and D) when `need_vec` is set.
+bsa_status check_desc(const bsa_tdesc& d, const char* name, int vec, bool need_vec) {
+  if (d.B < 1 || d.N < 1 || d.H < 1 || d.D < 1)
+    return fail(BSA_ERR_SHAPE, "%s: sizes must be positive (B=%lld N=%lld H=%lld D=%lld)", name,
+                (long long)d.B, (long long)d.N, (long long)d.H, (long long)d.D);
+  if (d.sB < 0 || d.sN < 0 || d.sH < 0) return fail(BSA_ERR_SHAPE, "%s: negative stride", name);
+  if (need_vec && (d.D % vec || d.sB % vec || d.sN % vec || d.sH % vec))
+    return fail(BSA_ERR_SHAPE, "%s: D and strides must be multiples of %d elements", name, vec);
+  if (d.N >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "%s: N must be below 2^31", name);
+  return BSA_OK;
+}
+
+int elem_bytes(bsa_dtype dt) { return dt == BSA_F32 ? 4 : 2; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+const char* bsa_version(void) { return "libbsa 0.1 (gfx950)"; }
+
+bsa_status bsa_check(void* stream) {
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "stream synchronize");
+  return hip_status(hipGetLastError(), "asynchronous error");
+}
+
+// ---------------------------------------------------------------------------- tiling
+bsa_status bsa_tile_dims(int T, int H, int W, int bT, int bH, int bW, int* J, int* M) {
+  if (!J || !M) return fail(BSA_ERR_ARG, "bsa_tile_dims: null output pointer");
+  if (T < 1 || H < 1 || W < 1 || bT < 1 || bH < 1 || bW < 1)
+    return fail(BSA_ERR_SHAPE, "bsa_tile_dims: grid and block sizes must be positive");
+  const int64_t n = (int64_t)T * H * W;
+  const int64_t jt = (T + bT - 1) / bT, jh = (H + bH - 1) / bH, jw = (W + bW - 1) / bW;
+  const int64_t jj = jt * jh * jw, mm = (int64_t)bT * bH * bW;
+  if (n >= (int64_t)1 << 31 || jj * mm >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_tile_dims: grid too large for int32 tables");
+  *J = (int)jj;
+  *M = (int)mm;
+  return ok();
+}
+
+bsa_status vsa_tile_index(int T, int H, int W, int bT, int bH, int bW, int32_t* perm, int32_t* block_len,
+                          int32_t* inv, void* stream) {
+  int J = 0, M = 0;
+  bsa_status st = bsa_tile_dims(T, H, W, bT, bH, bW, &J, &M);
+  if (st != BSA_OK) return st;
+  if (!perm || !block_len) return fail(BSA_ERR_ARG, "vsa_tile_index: perm and block_len are required");
+  return hip_status(bsa::launch_tile_index(T, H, W, bT, bH, bW, J, M, perm, block_len, inv, (hipStream_t)stream),
+                    "vsa_tile_index launch");
+}
+
+int vsa_budget(double drop_ratio, int J) {
+  if (J < 1 || !(drop_ratio >= 0.0 && drop_ratio <= 1.0)) return -1;
+  const double keep = std::ceil((1.0 - drop_ratio) * J - 1e-9);
+  int r = (int)keep;
+  if (r > J) r = J;
+  if (r < 1) r = 1;
+  return r;
+}
+
+// ------------------------------------------------------------------ pool / route / TopK
+static bsa_status check_route(const vsa_route_args* a) {
+  if (!a) return fail(BSA_ERR_ARG, "vsa_pool_route_topk: null args");
+  if (!a->q || !a->k || !a->perm || !a->block_len || !a->q2k_idx || !a->q2k_num)
+    return fail(BSA_ERR_ARG, "vsa_pool_route_topk: q, k, perm, block_len, q2k_idx and q2k_num are required");
+  if (a->dt != BSA_BF16 && a->dt != BSA_F32) return fail(BSA_ERR_ARG, "vsa_pool_route_topk: bad dtype");
+  bsa_status st = check_desc(a->d, "q/k", 1, false);
+  if (st != BSA_OK) return st;
+  if (a->d.D > 256) return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: D must be <= 256");
+  if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "vsa_pool_route_topk: J and M must be positive");
+  if (a->J > bsa::kRouteMaxJ)
+    return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: J=%d exceeds %d blocks", a->J, bsa::kRouteMaxJ);
+  if (a->R < 1 || a->R > a->J) return fail(BSA_ERR_SHAPE, "vsa_pool_route_topk: R must lie in [1, J]");
+  if (a->kmax < a->R) return fail(BSA_ERR_SHAPE, "vsa_pool_route_topk: kmax must be >= R");
+  if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "vsa_pool_route_topk: scale must be finite");
+  if ((int64_t)a->d.B * a->d.H > 65535)
+    return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: B*H must be <= 65535");
+  return BSA_OK;
+}
+
+bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "vsa_pool_route_topk_ws: null output");
+  bsa_status st = check_route(a);
+  if (st != BSA_OK) return st;
+  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  *bytes = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  return ok();
+}
+
+bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  bsa_status st = vsa_pool_route_topk_ws(a, &need);
+  if (st != BSA_OK) return st;
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "vsa_pool_route_topk: workspace of %zu bytes required", need);
+  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  char* w = static_cast<char*>(ws);
+  float* qbar = a->qbar;
+  float* kbar = a->kbar;
+  if (!qbar) { qbar = reinterpret_cast<float*>(w); w += one; }
+  if (!kbar) { kbar = reinterpret_cast<float*>(w); w += one; }
+  const int vec = 16 / elem_bytes(a->dt);
+  const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
+                      aligned16(a->q) && aligned16(a->k);
+  bsa::PoolParams pp{a->q, a->k, a->d.sB, a->d.sN, a->d.sH, (int)a->d.B, (int)a->d.H, (int)a->d.D, a->J, a->M,
+                     a->perm, a->block_len, qbar, kbar};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  bsa::RouteParams rp{qbar, kbar, (int)a->d.B, (int)a->d.H, a->J, (int)a->d.D, a->R, a->kmax, a->scale,
+                      a->q2k_idx, a->q2k_num, a->E};
+  return hip_status(bsa::launch_route_topk(rp, s), "route/topk launch");
+}
+
+// ------------------------------------------------------------------- query-outer attention
+static bsa_status check_attn_common(const bsa_qouter_args* a) {
+  if (!a) return fail(BSA_ERR_ARG, "bsa_forward_qouter: null args");
+  if (!a->q || !a->k || !a->v || !a->out) return fail(BSA_ERR_ARG, "bsa_forward_qouter: q, k, v, out are required");
+  if (a->dt != BSA_BF16 && a->dt != BSA_F32) return fail(BSA_ERR_ARG, "bsa_forward_qouter: bad dtype");
+  const int vec = 16 / elem_bytes(a->dt);
+  bsa_status st = check_desc(a->dq, "q", vec, true);
+  if (st != BSA_OK) return st;
+  if ((st = check_desc(a->dkv, "k/v", vec, true)) != BSA_OK) return st;
+  if ((st = check_desc(a->dout, "out", vec, true)) != BSA_OK) return st;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+    return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: q, k, v, out must be 16-byte aligned");
+  if (a->dq.D != a->dkv.D || a->dq.D != a->dout.D) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: D mismatch");
+  if (a->dq.D != 64 && a->dq.D != 128) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: D must be 64 or 128");
+  if (a->dq.B != a->dkv.B || a->dq.B != a->dout.B) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: B mismatch");
+  if (a->dq.N != a->dkv.N || a->dq.N != a->dout.N) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: N mismatch");
+  if (a->dq.H != a->dout.H) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: q and out heads differ");
+  if (a->dq.H % a->dkv.H) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: Hq must be a multiple of Hkv");
+  if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "bsa_forward_qouter: scale must be finite");
+  return BSA_OK;
+}
+
+bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
+  bsa_status st = check_attn_common(a);
+  if (st != BSA_OK) return st;
+  const float scale_log2 = a->scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->mode == BSA_SEL_BLOCK) {
+    if (a->dq.H != a->dkv.H) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block mode needs Hq == Hkv");
+    if (!a->perm || !a->block_len || !a->q2k_idx || !a->q2k_num)
+      return fail(BSA_ERR_ARG, "bsa_forward_qouter: perm, block_len, q2k_idx, q2k_num are required");
+    if (a->J < 1 || a->kmax < 1) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: J and kmax must be positive");
+    if (a->M != 16 && a->M != 32 && a->M != 64)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block capacity M must be 16, 32 or 64");
+    if ((int64_t)a->dq.B * a->dq.H * a->J >= (int64_t)1 << 31)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks");
+    bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
+                         a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
+                         a->dout.sB, a->dout.sN, a->dout.sH,
+                         a->perm, a->block_len, a->q2k_idx, a->q2k_num,
+                         (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
+                         scale_log2, a->lse};
+    return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
+  }
+  if (a->mode == BSA_SEL_TOKEN) {
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: token-selection mode is not built yet");
+  }
+  return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
+}
+
+// ------------------------------------------------------------------------ KV-outer
+bsa_status bsa_kvouter_ws(const bsa_kvouter_args* a, size_t* bytes) {
+  (void)a;
+  (void)bytes;
+  return fail(BSA_ERR_UNSUPPORTED, "bsa_kvouter_ws: not built yet");
+}
+
+bsa_status bsa_forward_kvouter(const bsa_kvouter_args* a, void* ws, size_t ws_bytes, void* stream) {
+  (void)a;
+  (void)ws;
+  (void)ws_bytes;
+  (void)stream;
+  return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: not built yet");
+}
+
+bsa_status bsa_combine(const bsa_combine_args* a, void* stream) {
+  (void)a;
+  (void)stream;
+  return fail(BSA_ERR_UNSUPPORTED, "bsa_combine: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Host-side declarations shared between the C-ABI layer (api.hip) and the
+// kernel translation units.  Every launcher enqueues on `stream` and returns
+// the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// ---- tiling -----------------------------------------------------------------
+hipError_t launch_tile_index(int T, int H, int W, int bT, int bH, int bW, int J, int M,
+                             int32_t* perm, int32_t* block_len, int32_t* inv, hipStream_t s);
+
+// ---- pool / route / TopK ------------------------------------------------------
+struct PoolParams {
+  const void* q;
+  const void* k;
+  int64_t sB, sN, sH;
+  int B, H, D, J, M;
+  const int32_t* perm;
+  const int32_t* block_len;
+  float* qbar;  // [B, H, J, D]
+  float* kbar;
+};
+// `vec`: D, strides and base pointers allow 16-byte vector loads.
+hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s);
+
+struct RouteParams {
+  const float* qbar;  // [B, H, J, D]
+  const float* kbar;
+  int B, H, J, D, R, kmax;
+  float scale;
+  int32_t* q2k_idx;  // [B, H, J, kmax]
+  int32_t* q2k_num;  // [B, H, J]
+  float* E;          // optional [B, H, J, J]
+};
+// Largest J the fused route + TopK kernel handles.
+constexpr int kRouteMaxJ = 4096;
+hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
+
+// ---- query-outer attention -----------------------------------------------------
+struct VsaAttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sB, q_sN, q_sH;
+  int64_t kv_sB, kv_sN, kv_sH;
+  int64_t o_sB, o_sN, o_sH;
+  const int32_t* perm;
+  const int32_t* block_len;
+  const int32_t* q2k_idx;
+  const int32_t* q2k_num;
+  int B, H, J, M, kmax, D;
+  int64_t N;
+  float scale_log2;  // softmax scale * log2(e)
+  float* lse;        // optional [B, H, N]
+};
+hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
+
+struct NsaAttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sB, q_sN, q_sH;
+  int64_t kv_sB, kv_sN, kv_sH;
+  int64_t o_sB, o_sN, o_sH;
+  const int32_t* blk_idx;  // [B, N, Hkv, S]
+  const int32_t* blk_cnt;  // [B, N, Hkv] or null
+  int B, Hq, Hkv, S, BS, causal, D;
+  int64_t N;
+  float scale_log2;
+  float* lse;  // optional [B, Hq, N]
+};
+hipError_t launch_nsa_attention(const NsaAttnParams& p, bool f32_io, hipStream_t s);
+
+// ---- KV-outer schedule -----------------------------------------------------------
+struct KvOuterParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sB, q_sN, q_sH;
+  int64_t kv_sB, kv_sN, kv_sH;
+  const int32_t* q2k;      // [B, N, Hkv, ks]
+  const int32_t* q2k_cnt;  // [B, N, Hkv] or null
+  int B, Hq, Hkv, ks, BK, D, causal, chunk_cap;
+  int64_t N;
+  float scale_log2;
+  __bf16* o_buf;   // [B, ks, N, Hq, D]
+  float* lse_buf;  // [B, ks, N, Hq]
+  int32_t* nslot;  // [B, N, Hkv]
+};
+size_t kvouter_ws_bytes(const KvOuterParams& p);
+hipError_t launch_kvouter(const KvOuterParams& p, void* ws, hipStream_t s);
+
+struct CombineParams {
+  const __bf16* o_buf;
+  const float* lse_buf;
+  const int32_t* nslot;
+  int B, Hq, Hkv, ks, D;
+  int64_t N;
+  __bf16* out;
+  int64_t o_sB, o_sN, o_sH;
+  float* lse;  // optional [B, Hq, N]
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,411 @@
+// Tiling tables, per-block mean pooling and the fused routing-score + TopK
+// kernel for gfx950.
+//
+// Source: "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" -- section 1
+// (3D blocks, token numbering, true lengths of edge blocks), section 2.1
+// (per-block means of Q and K per batch and head, divided by the true length),
+// section 2.2 (E = Q_bar K_bar^T / sqrt(D), per-row TopK on the logits) and
+// section 4 (kept block ids in increasing order, -1 fill, separate count).
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+// ============================================================================
+// Tiling: one thread per packed slot p = b*M + r.
+// ============================================================================
+__global__ void tile_index_kernel(int T, int H, int W, int bT, int bH, int bW, int JH, int JW, int M,
+                                  int J, int32_t* __restrict__ perm, int32_t* __restrict__ block_len,
+                                  int32_t* __restrict__ inv) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= (int64_t)J * M) return;
+  const int b = (int)(p / M), r = (int)(p % M);
+  const int bt = b / (JH * JW), rem = b % (JH * JW), by = rem / JW, bx = rem % JW;
+  const int t0 = bt * bT, y0 = by * bH, x0 = bx * bW;
+  const int nt = min(bT, T - t0), ny = min(bH, H - y0), nx = min(bW, W - x0);
+  const int n = nt * ny * nx;
+  if (r == 0) block_len[b] = n;
+  if (r < n) {
+    // members listed with t slowest and x fastest over the block's valid extent
+    const int dt = r / (ny * nx), rr = r % (ny * nx), dy = rr / nx, dx = rr % nx;
+    const int tok = ((t0 + dt) * H + (y0 + dy)) * W + (x0 + dx);
+    perm[p] = tok;
+    if (inv) inv[tok] = (int32_t)p;
+  } else {
+    perm[p] = -1;
+  }
+}
+
+hipError_t launch_tile_index(int T, int H, int W, int bT, int bH, int bW, int J, int M, int32_t* perm,
+                             int32_t* block_len, int32_t* inv, hipStream_t s) {
+  const int JH = (H + bH - 1) / bH, JW = (W + bW - 1) / bW;
+  const int64_t total = (int64_t)J * M;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  tile_index_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(T, H, W, bT, bH, bW, JH, JW, M, J,
+                                                                      perm, block_len, inv);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Pool: one workgroup per (block i, batch b, tensor).  Each token row of all
+// heads is read with 16-byte loads (VW elements) and accumulated in fp32; the
+// sum is divided by the block's true length.
+// ============================================================================
+template <typename T, int VW, int CPT>
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(blockIdx.z ? p.k : p.q);
+  float* __restrict__ out = blockIdx.z ? p.kbar : p.qbar;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int n = p.block_len[i];
+  const int cpr = p.D / VW;  // vector chunks per head row
+  const int nch = p.H * cpr;
+  const int32_t* __restrict__ members = p.perm + (int64_t)i * p.M;
+  const T* __restrict__ xb = x + (int64_t)b * p.sB;
+  for (int c0 = 0; c0 < nch; c0 += 256 * CPT) {
+    float acc[CPT][VW];
+    int64_t off[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = c0 + threadIdx.x + 256 * u;
+      const int hh = c / cpr, dc = c % cpr;
+      off[u] = (c < nch) ? (int64_t)hh * p.sH + (int64_t)dc * VW : -1;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[u][e] = 0.f;
+    }
+    int r = 0;
+    for (; r + 4 <= n; r += 4) {
+      T v[4][CPT][VW];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const T* row = xb + (int64_t)members[r + rr] * p.sN;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          if (off[u] >= 0) {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) v[rr][u][e] = row[off[u] + e];
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+          if (off[u] >= 0)
+#pragma unroll
+            for (int e = 0; e < VW; ++e) acc[u][e] += (float)v[rr][u][e];
+    }
+    for (; r < n; ++r) {
+      const T* row = xb + (int64_t)members[r] * p.sN;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u)
+        if (off[u] >= 0)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[u][e] += (float)row[off[u] + e];
+    }
+    const float fn = (float)n;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = c0 + threadIdx.x + 256 * u;
+      if (c < nch) {
+        const int hh = c / cpr, dc = c % cpr;
+        float* dst = out + (((int64_t)b * p.H + hh) * p.J + i) * p.D + dc * VW;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) dst[e] = acc[u][e] / fn;
+      }
+    }
+  }
+}
+
+template <typename T, int VW>
+static hipError_t launch_pool_t(const PoolParams& p, hipStream_t s) {
+  const int nch = p.H * (p.D / VW);
+  const int cpt = (nch + 255) / 256;
+  dim3 grid(p.J, p.B, 2);
+  if (cpt <= 1)
+    pool_kernel<T, VW, 1><<<grid, 256, 0, s>>>(p);
+  else if (cpt <= 2)
+    pool_kernel<T, VW, 2><<<grid, 256, 0, s>>>(p);
+  else if (cpt <= 3)
+    pool_kernel<T, VW, 3><<<grid, 256, 0, s>>>(p);
+  else
+    pool_kernel<T, VW, 4><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s) {
+  if (f32_input) {
+    if (vec) return launch_pool_t<float, 4>(p, s);
+    return launch_pool_t<float, 1>(p, s);
+  }
+  if (vec) return launch_pool_t<__bf16, 8>(p, s);
+  return launch_pool_t<__bf16, 1>(p, s);
+}
+
+// ============================================================================
+// Fused routing scores + TopK.
+//
+// Workgroup = (batch*head, band of 16*RT query blocks), 8 waves.  Wave w owns
+// the 16*NT key-block columns [w*16*NT, (w+1)*16*NT) of the band's score rows
+// and keeps them in registers.  Scores E^T = K_bar Q_bar^T come from the
+// 16x16x32 bf16 matrix cores with every fp32 operand split as hi + lo bf16
+// (hi*hi + hi*lo + lo*hi), which keeps E at fp32 accuracy.  In the output
+// layout lane l owns query rows 16*rt + l%16 and columns 4*(l/16) + v of each
+// 16-column tile.
+//
+// TopK per row: an exact search for the R-th largest order-preserving key,
+// one bit per round (count keys >= candidate across the row), then every key
+// above the threshold is kept plus the lowest-index keys equal to it, and the
+// kept ids are emitted in increasing order from per-row bit masks.
+// ============================================================================
+constexpr int kRouteWaves = 8;
+
+__device__ __forceinline__ int wave_excl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  return incl - x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <int NT, int RT>
+__global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
+  constexpr int BM = 16 * RT;              // query blocks per workgroup
+  constexpr int CW = 16 * NT;              // columns per wave
+  constexpr int MW = kRouteWaves * CW / 32;  // 32-bit mask words per row
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * BM;
+  const int J = p.J, D = p.D;
+  const int KS = (D + 31) / 32;
+  const int DP = KS * 32 + 8;  // padded LDS row (bf16 elements)
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* qhi = reinterpret_cast<__bf16*>(smem);
+  __bf16* qlo = qhi + BM * DP;
+  uint32_t* gtm = reinterpret_cast<uint32_t*>(qlo + BM * DP);
+  uint32_t* eqm = gtm + BM * MW;
+  int* red = reinterpret_cast<int*>(eqm + BM * MW);  // [2][8][BM]
+
+  const float* __restrict__ qb = p.qbar + (int64_t)bh * J * D;
+  const float* __restrict__ kb = p.kbar + (int64_t)bh * J * D;
+
+  // ---- stage the band's pooled queries as hi/lo bf16 (zero padded) -------------
+  for (int e = threadIdx.x; e < BM * KS * 32; e += 512) {
+    const int r = e / (KS * 32), d = e % (KS * 32);
+    const int i = i0 + r;
+    const float x = (i < J && d < D) ? qb[(int64_t)i * D + d] : 0.f;
+    const __bf16 hi = (__bf16)x;
+    qhi[r * DP + d] = hi;
+    qlo[r * DP + d] = (__bf16)(x - (float)hi);
+  }
+  for (int e = threadIdx.x; e < 2 * BM * MW; e += 512) gtm[e] = 0u;
+  __syncthreads();
+
+  // ---- scores: E^T tiles for this wave's columns -----------------------------
+  float sc[RT][NT][4];
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int j0 = w * CW + 16 * t;
+    const int jr = j0 + l16;  // A-operand row (key block)
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j0 < J) {
+      for (int s = 0; s < KS; ++s) {
+        const int d0 = 32 * s + 8 * g;
+        float kv[8];
+        if (jr < J && d0 + 8 <= D) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(kb + (int64_t)jr * D + d0);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(kb + (int64_t)jr * D + d0 + 4);
+          kv[0] = a[0]; kv[1] = a[1]; kv[2] = a[2]; kv[3] = a[3];
+          kv[4] = b[0]; kv[5] = b[1]; kv[6] = b[2]; kv[7] = b[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[e] = (jr < J && d0 + e < D) ? kb[(int64_t)jr * D + d0 + e] : 0.f;
+        }
+        bf16x8 khi, klo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          khi[e] = (__bf16)kv[e];
+          klo[e] = (__bf16)(kv[e] - (float)khi[e]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int row = 16 * rt + l16;
+          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi + row * DP + d0);
+          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo + row * DP + d0);
+          acc[rt] = mfma16(klo, qh, acc[rt]);
+          acc[rt] = mfma16(khi, ql, acc[rt]);
+          acc[rt] = mfma16(khi, qh, acc[rt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
+  }
+
+  // optional debug copy of the scores
+  if (p.E) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int i = i0 + 16 * rt + l16;
+      if (i >= J) continue;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = w * CW + 16 * t + 4 * g + v;
+          if (j < J) p.E[((int64_t)bh * J + i) * J + j] = sc[rt][t][v];
+        }
+    }
+  }
+
+  // ---- order-preserving keys; padding columns get key 0 (below every float) ----
+  uint32_t key[RT][NT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = w * CW + 16 * t + 4 * g + v;
+        key[rt][t][v] = (j < J) ? float_key(sc[rt][t][v]) : 0u;
+      }
+
+  // ---- exact threshold: the R-th largest key of every row ------------------------
+  uint32_t thr[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) thr[rt] = 0u;
+  int par = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    int cnt[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint32_t cand = thr[rt] | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c += (key[rt][t][v] >= cand) ? 1 : 0;
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      cnt[rt] = c;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) red[(par * kRouteWaves + w) * BM + 16 * rt + lane] = cnt[rt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      int tot = 0;
+#pragma unroll
+      for (int ww = 0; ww < kRouteWaves; ++ww) tot += red[(par * kRouteWaves + ww) * BM + 16 * rt + l16];
+      if (tot >= p.R) thr[rt] |= (1u << bit);
+    }
+    par ^= 1;
+  }
+
+  // ---- bit masks of keys above / equal to the threshold ------------------------
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + l16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        gt |= (key[rt][t][v] > thr[rt] ? 1u : 0u) << (4 * g + v);
+        eq |= (key[rt][t][v] == thr[rt] ? 1u : 0u) << (4 * g + v);
+      }
+      gt |= __shfl_xor(gt, 16, 64);
+      gt |= __shfl_xor(gt, 32, 64);
+      eq |= __shfl_xor(eq, 16, 64);
+      eq |= __shfl_xor(eq, 32, 64);
+      const int j0 = w * CW + 16 * t;
+      if (g == 0 && j0 < J) {
+        const int word = j0 >> 5, sh = j0 & 31;
+        if (gt) atomicOr(&gtm[row * MW + word], gt << sh);
+        if (eq) atomicOr(&eqm[row * MW + word], eq << sh);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- emit kept ids in increasing order, one wave per row ----------------------
+  for (int row = w; row < BM; row += kRouteWaves) {
+    const int i = i0 + row;
+    if (i >= J) continue;
+    int32_t* __restrict__ out = p.q2k_idx + ((int64_t)bh * J + i) * p.kmax;
+    int ngt = 0;
+    for (int wb = 0; wb < MW; wb += 64) {
+      const int word = wb + lane;
+      ngt += wave_sum(word < MW ? __popc(gtm[row * MW + word]) : 0);
+    }
+    const int need_eq = p.R - ngt;
+    int eq_carry = 0, sel_carry = 0;
+    for (int wb = 0; wb < MW; wb += 64) {
+      const int word = wb + lane;
+      const uint32_t gw = word < MW ? gtm[row * MW + word] : 0u;
+      uint32_t ew = word < MW ? eqm[row * MW + word] : 0u;
+      const int ne = __popc(ew);
+      const int eq_before = eq_carry + wave_excl_scan(ne);
+      int take = min(max(need_eq - eq_before, 0), ne);
+      uint32_t takebits = 0u;
+      while (take-- > 0) {
+        const uint32_t low = ew & (0u - ew);
+        takebits |= low;
+        ew ^= low;
+      }
+      uint32_t sel = gw | takebits;
+      const int ns = __popc(sel);
+      int pos = sel_carry + wave_excl_scan(ns);
+      while (sel) {
+        const int bitpos = __ffs(sel) - 1;
+        out[pos++] = word * 32 + bitpos;
+        sel &= sel - 1u;
+      }
+      eq_carry += wave_sum(ne);
+      sel_carry += wave_sum(ns);
+    }
+    for (int q = p.R + lane; q < p.kmax; q += 64) out[q] = -1;
+    if (lane == 0) p.q2k_num[(int64_t)bh * J + i] = p.R;
+  }
+}
+
+template <int NT, int RT>
+static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
+  constexpr int BM = 16 * RT;
+  constexpr int MW = kRouteWaves * 16 * NT / 32;
+  const int KS = (p.D + 31) / 32, DP = KS * 32 + 8;
+  const size_t smem = (size_t)2 * BM * DP * sizeof(__bf16) + (size_t)2 * BM * MW * 4 +
+                      (size_t)2 * kRouteWaves * BM * 4;
+  dim3 grid((p.J + BM - 1) / BM, p.B * p.H);
+  route_topk_kernel<NT, RT><<<grid, 512, smem, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_topk(const RouteParams& p, hipStream_t s) {
+  const int cols_per_wave = (p.J + kRouteWaves - 1) / kRouteWaves;
+  if (cols_per_wave <= 16) return launch_route_t<1, 2>(p, s);
+  if (cols_per_wave <= 32) return launch_route_t<2, 2>(p, s);
+  if (cols_per_wave <= 64) return launch_route_t<4, 2>(p, s);
+  if (cols_per_wave <= 128) return launch_route_t<8, 2>(p, s);
+  if (cols_per_wave <= 256) return launch_route_t<16, 2>(p, s);
+  return launch_route_t<32, 1>(p, s);
+}
+
+}  // namespace bsa

@@ -1,0 +1,268 @@
+/*
+ * bsa.h -- routed block-sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsa.so.  Every operation here is one stage of VSA-style routed
+ * block-sparse attention, or of its two alternative index modes:
+ *
+ *   vsa_tile_index       3D spatio-temporal tiling tables
+ *   vsa_pool_route_topk  per-block mean pooling, routing scores, TopK + index table
+ *   bsa_forward_qouter   exact sparse attention, one query block (VSA) or one
+ *                        query token (NSA) at a time over its selected KV blocks
+ *   bsa_forward_kvouter  KV-outer schedule: reverse index, scheduler, K1 partials
+ *   bsa_combine          K2: exact log-sum-exp merge of the K1 partials
+ *
+ * Sources (page title, section):
+ *   [VSA]  "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" (maple.link)
+ *   [NSA]  "NSA 算子解析（Torch/Tilelang）" (devpress.csdn.net)
+ *   [MSA]  "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array argument is device memory owned by the caller.  The
+ *           library keeps no global state and never allocates: calls that need
+ *           scratch take a caller-supplied workspace whose size comes from the
+ *           matching *_ws query.
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *           Every call only enqueues work on that stream and returns; results
+ *           are ready when the stream is synchronised.
+ * Errors.   Shapes, strides, dtypes, sizes and null pointers are validated on
+ *           the host before anything is enqueued; on failure nothing is
+ *           written and the status says why (bsa_last_error() gives a message
+ *           for the calling thread).  Launch failures map to BSA_ERR_HIP.
+ *           Index entries < 0, and entries at positions >= their row count,
+ *           are skipped and never dereferenced.  Entries >= the number of
+ *           blocks are a caller error that the kernels do not check.
+ *           Nothing aborts, throws or prints.
+ * Tensors.  A bsa_tdesc describes a 4-D view [B, N, H, D] (batch, token,
+ *           head, channel) with element strides sB, sN, sH and D contiguous
+ *           (stride 1).  Both BSHD ([B,N,H,D] contiguous) and BHSD
+ *           ([B,H,N,D] contiguous, described with sH = N*D, sN = D) are
+ *           accepted: the layout changes the memory order, not the tiling
+ *           ([VSA] section 5.4).  Base pointers must be 16-byte aligned and,
+ *           for bf16, strides must be multiples of 8 elements.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_ARG = 1,          /* null pointer, negative size, bad enum        */
+  BSA_ERR_SHAPE = 2,        /* inconsistent shapes / strides / alignment    */
+  BSA_ERR_UNSUPPORTED = 3,  /* valid request outside the supported envelope */
+  BSA_ERR_WORKSPACE = 4,    /* workspace null or smaller than required      */
+  BSA_ERR_INDEX = 5,        /* index table inconsistent with its shapes     */
+  BSA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed   */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
+
+/* Strided 4-D tensor view [B, N, H, D]; strides in elements, D contiguous. */
+typedef struct {
+  int64_t B, N, H, D;
+  int64_t sB, sN, sH;
+} bsa_tdesc;
+
+/* Selection modes of bsa_forward_qouter. */
+enum { BSA_SEL_BLOCK = 0, BSA_SEL_TOKEN = 1 };
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* bsa_last_error(void);
+
+/* Library version string. */
+const char* bsa_version(void);
+
+/* Synchronise `stream` and report any asynchronous HIP error as BSA_ERR_HIP. */
+bsa_status bsa_check(void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Tiling ([VSA] sections 1 and 3).
+ *
+ * bsa_tile_dims (host only): J = ceil(T/bT)*ceil(H/bH)*ceil(W/bW) blocks of
+ * capacity M = bT*bH*bW.
+ *
+ * vsa_tile_index: block b = (bt*JH + by)*JW + bx covers t in
+ * [bt*bT, min(T,(bt+1)*bT)) and likewise y, x; its n_b valid members are listed
+ * with t slowest and x fastest, token id = t*H*W + y*W + x.
+ *   perm      int32 [J*M]  token id held by packed slot b*M + r, or -1 for r >= n_b
+ *   block_len int32 [J]    n_b
+ *   inv       int32 [N]    packed slot of each token (inv[perm[p]] = p); may be NULL
+ * N = T*H*W must be below 2^31.
+ * ------------------------------------------------------------------------- */
+bsa_status bsa_tile_dims(int T, int H, int W, int bT, int bH, int bW, int* J, int* M);
+bsa_status vsa_tile_index(int T, int H, int W, int bT, int bH, int bW,
+                          int32_t* perm, int32_t* block_len, int32_t* inv, void* stream);
+
+/* Keep budget R = max(1, min(ceil((1 - s) * J), J)) ([VSA] section 2.2), with
+ * 1e-9 subtracted before the ceiling so that (1-0.7)*10 gives 3.  Host only;
+ * returns -1 when J < 1 or s lies outside [0, 1]. */
+int vsa_budget(double drop_ratio, int J);
+
+/* ----------------------------------------------------------------------------
+ * Pool -> route -> TopK ([VSA] sections 2.1, 2.2 and 4).
+ *
+ * For every batch b, head h and query block i:
+ *   qbar_i = (1/n_i) * sum_{r < n_i} Q[b, perm[i*M + r], h, :]   (likewise kbar)
+ *   E[i, j] = scale * qbar_i . kbar_j           (scale is normally 1/sqrt(D))
+ *   the R largest E[i, :] (ties: lower j first) are written to
+ *   q2k_idx[b,h,i,0:R] in increasing order, q2k_idx[b,h,i,R:kmax] = -1, and
+ *   q2k_num[b,h,i] = R.
+ * Pooled means are accumulated in fp32 and E is formed to fp32 accuracy
+ * (a three-product bf16 split on the matrix cores).
+ *
+ * q, k      strided views (dtype dt) of the same [B, N, H, D] shape
+ * perm, block_len   tiling tables of J blocks of capacity M (vsa_tile_index)
+ * q2k_idx   int32 [B, H, J, kmax] contiguous, kmax >= R
+ * q2k_num   int32 [B, H, J] contiguous
+ * qbar, kbar  optional fp32 [B, H, J, D] outputs (NULL: kept in the workspace)
+ * E         optional fp32 [B, H, J, J] output of the scores (debug; NULL: none)
+ * Supported: 1 <= R <= J <= 4096, D <= 256, any N.  The workspace holds the
+ * pooled means: vsa_pool_route_topk_ws() bytes.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  bsa_tdesc d;
+  bsa_dtype dt;
+  const int32_t* perm;
+  const int32_t* block_len;
+  int J, M;
+  int R, kmax;
+  float scale;
+  int32_t* q2k_idx;
+  int32_t* q2k_num;
+  float* qbar;
+  float* kbar;
+  float* E;
+} vsa_route_args;
+
+bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes);
+bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Exact sparse attention, query-outer order.
+ *
+ * mode BSA_SEL_BLOCK (VSA; [VSA] sections 4, 6.2, 6.3, 6.5): every valid query
+ *   token a of block i (a = perm[i*M + r], r < n_i) attends, with one softmax,
+ *   to the union of the valid tokens of blocks q2k_idx[b,h,i,p] for
+ *   p < q2k_num[b,h,i] (entries < 0 skipped).  No causal mask.  Output rows are
+ *   written at the tokens' original positions; padding rows are never written.
+ *   Requires Hq == Hkv.  Fields: perm, block_len, J, M, q2k_idx [B,H,J,kmax],
+ *   q2k_num [B,H,J], kmax.
+ *
+ * mode BSA_SEL_TOKEN (NSA; [NSA] "Torch朴素实现"): query head hq of token t
+ *   reads KV head hq / G (G = Hq / Hkv) and attends to the tokens
+ *   blk*BS + u (u < BS, < N, and <= t when causal) of the blocks
+ *   blk_idx[b,t,hkv,p] for p < blk_cnt[b,t,hkv] with blk >= 0.  blk_cnt may be
+ *   NULL (all S entries count).  Fields: blk_idx int32 [B,N,Hkv,S] contiguous,
+ *   blk_cnt int32 [B,N,Hkv] contiguous, S, BS, causal.
+ *
+ * Both modes: out = softmax(scale * q k^T) v over the allowed keys, a row with
+ * no allowed key gives 0 (and lse = -inf).  lse (optional, NULL: none) is fp32
+ * [B, Hq, N] contiguous, natural log.  q/out use dq/dout, k/v use dkv.
+ * Supported: D in {64, 128}.  dt = BF16 runs on the matrix cores (bf16
+ * products, fp32 accumulation and softmax, bf16 output); dt = F32 (block mode
+ * only) is computed entirely in fp32 on the vector ALUs and meant for small
+ * problems.  VSA block capacity M in {16, 32, 64}; NSA (bf16 only) block size
+ * BS in {32, 64, 128}, S <= 64.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  bsa_tdesc dq, dkv, dout;
+  bsa_dtype dt;
+  float scale;
+  int mode;
+  /* BSA_SEL_BLOCK */
+  const int32_t* perm;
+  const int32_t* block_len;
+  int J, M;
+  const int32_t* q2k_idx;
+  const int32_t* q2k_num;
+  int kmax;
+  /* BSA_SEL_TOKEN */
+  const int32_t* blk_idx;
+  const int32_t* blk_cnt;
+  int S, BS, causal;
+  /* optional */
+  float* lse;
+} bsa_qouter_args;
+
+bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * KV-outer schedule ([MSA] sections 5-8).
+ *
+ * Selections q2k int32 [B, N, Hkv, k_sel] contiguous (entries < 0 skipped;
+ * with q2k_cnt int32 [B, N, Hkv], only p < q2k_cnt[...] count).  For query
+ * position i and KV head r, the valid entries taken in increasing block order
+ * get slots s = 0, 1, ...; nslot[b,i,r] is their number.
+ *
+ * bsa_forward_kvouter:
+ *   1. reverse index: for every (b, r, kv block) the list of (i, s) selecting it
+ *      (count, exclusive scan, scatter);
+ *   2. scheduler: each list is cut into chunks of at most chunk_cap query
+ *      positions (0: 2 * k_sel * BK), so hot blocks spread over workgroups;
+ *   3. K1: per chunk, the K/V tile of the block is staged once and the gathered
+ *      queries (G heads per position) attend to it with a local softmax:
+ *        L_s = log sum_{j in J_s} exp S_j,  O_s = sum_{j in J_s} exp(S_j - L_s) v_j,
+ *      S_j = scale * q . k_j over the block's keys (<= i when causal).  Results
+ *      go to the preassigned slot: o_buf[b,s,i,hq,:] (bf16) and
+ *      lse_buf[b,s,i,hq] (fp32), so no accumulation and no atomics touch them.
+ *      An empty J_s gives L_s = -inf and O_s = 0.
+ *   q [B,N,Hq,D] and k/v [B,N,Hkv,D] strided, bf16, D = 128 or 64, BK in {64, 128}.
+ *   o_buf bf16 [B, k_sel, N, Hq, D], lse_buf fp32 [B, k_sel, N, Hq] and
+ *   nslot int32 [B, N, Hkv], all contiguous, live until bsa_combine.  Slots at
+ *   or beyond nslot are left untouched.
+ *
+ * bsa_combine (K2, [MSA] section 6.2): for every (b, i, hq), over s < nslot:
+ *   a = max L_s, L = a + log sum exp(L_s - a), out = sum_s exp(L_s - L) O_s;
+ *   out = 0 and L = -inf when there is no slot or all L_s are -inf.
+ *   out is a bf16 strided view [B, N, Hq, D]; lse (optional) fp32 [B, Hq, N].
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  bsa_tdesc dq, dkv;
+  bsa_dtype dt;
+  float scale;
+  int causal;
+  const int32_t* q2k;
+  const int32_t* q2k_cnt;
+  int k_sel, BK;
+  void* o_buf;
+  float* lse_buf;
+  int32_t* nslot;
+  int chunk_cap;
+} bsa_kvouter_args;
+
+bsa_status bsa_kvouter_ws(const bsa_kvouter_args* a, size_t* bytes);
+bsa_status bsa_forward_kvouter(const bsa_kvouter_args* a, void* ws, size_t ws_bytes, void* stream);
+
+typedef struct {
+  const void* o_buf;
+  const float* lse_buf;
+  const int32_t* nslot;
+  int k_sel;
+  int Hkv;
+  bsa_tdesc dout;
+  void* out;
+  float* lse;
+} bsa_combine_args;
+
+bsa_status bsa_combine(const bsa_combine_args* a, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

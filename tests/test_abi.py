@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+bsa = pytest.importorskip("block_sparse_attention_02_amd")
+from block_sparse_attention_02_amd import _lib as L  # noqa: E402
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "bsa.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), "libbsa.so does not export %s" % n
+    assert set(names) == set(L.PROTOTYPES), "binding prototypes differ from include/bsa.h"
+
+
+def test_version_and_dims():
+    lib = L.load()
+    assert b"gfx950" in lib.bsa_version()
+    assert bsa.tile_dims(4, 4, 4, 4, 2, 2) == (4, 16)
+    assert bsa.tile_dims(30, 48, 80, 4, 4, 4) == (1920, 64)
+    assert bsa.tile_dims(5, 3, 4, 4, 2, 2) == (8, 16)
+    with pytest.raises(L.BsaError) as e:
+        bsa.tile_dims(0, 4, 4, 4, 2, 2)
+    assert e.value.status == L.BSA_ERR_SHAPE
+
+
+def test_budget():
+    assert bsa.keep_budget(0.75, 256) == 64
+    assert bsa.keep_budget(0.7, 10) == 3
+    assert bsa.keep_budget(0.9, 1920) == 192
+    assert bsa.keep_budget(1.0, 5) == 1 and bsa.keep_budget(0.0, 5) == 5
+    assert L.load().vsa_budget(1.5, 4) == -1 and L.load().vsa_budget(0.5, 0) == -1
+
+
+def _route_args(**kw):
+    d = L.TDesc(1, 64, 1, 64, 64 * 64, 64, 64)
+    a = L.RouteArgs(ctypes.c_void_p(256), ctypes.c_void_p(256), d, L.BSA_F32, ctypes.c_void_p(256),
+                    ctypes.c_void_p(256), 4, 16, 2, 4, 0.125, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                    None, None, None)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", None, L.BSA_ERR_ARG),
+    ("q2k_idx", None, L.BSA_ERR_ARG),
+    ("R", 5, L.BSA_ERR_SHAPE),
+    ("R", 0, L.BSA_ERR_SHAPE),
+    ("kmax", 1, L.BSA_ERR_SHAPE),
+    ("J", 5000, L.BSA_ERR_UNSUPPORTED),
+    ("dt", 7, L.BSA_ERR_ARG),
+])
+def test_route_validation(field, value, status):
+    lib = L.load()
+    a = _route_args(**{field: value})
+    n = ctypes.c_size_t()
+    assert lib.vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    assert lib.bsa_last_error()
+    assert lib.vsa_pool_route_topk(ctypes.byref(a), None, 0, None) == status
+
+
+def test_route_workspace_size_and_short_workspace():
+    lib = L.load()
+    a = _route_args()
+    n = ctypes.c_size_t()
+    assert lib.vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    assert n.value == 2 * 1024   # two [1,1,4,64] fp32 pooled-mean buffers
+    assert lib.vsa_pool_route_topk(ctypes.byref(a), None, 0, None) == L.BSA_ERR_WORKSPACE
+
+
+def _qouter_args(**kw):
+    d = L.TDesc(1, 64, 2, 128, 64 * 2 * 128, 2 * 128, 128)
+    a = L.QOuterArgs(q=ctypes.c_void_p(256), k=ctypes.c_void_p(256), v=ctypes.c_void_p(256),
+                     out=ctypes.c_void_p(256), dq=d, dkv=d, dout=d, dt=L.BSA_BF16, scale=0.088,
+                     mode=L.BSA_SEL_BLOCK, perm=ctypes.c_void_p(256), block_len=ctypes.c_void_p(256),
+                     J=1, M=64, q2k_idx=ctypes.c_void_p(256), q2k_num=ctypes.c_void_p(256), kmax=1)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("v", None, L.BSA_ERR_ARG),
+    ("perm", None, L.BSA_ERR_ARG),
+    ("M", 128, L.BSA_ERR_UNSUPPORTED),
+    ("M", 48, L.BSA_ERR_UNSUPPORTED),
+    ("mode", 9, L.BSA_ERR_ARG),
+    ("q", ctypes.c_void_p(258), L.BSA_ERR_SHAPE),
+    ("dt", 3, L.BSA_ERR_ARG),
+    ("scale", float("inf"), L.BSA_ERR_ARG),
+])
+def test_qouter_validation(field, value, status):
+    a = _qouter_args(**{field: value})
+    assert L.load().bsa_forward_qouter(ctypes.byref(a), None) == status
+
+
+def test_qouter_shape_checks():
+    lib = L.load()
+    d64 = L.TDesc(1, 64, 2, 96, 64 * 2 * 96, 2 * 96, 96)
+    a = _qouter_args(dq=d64, dkv=d64, dout=d64)
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_UNSUPPORTED   # D = 96
+    dkv = L.TDesc(1, 64, 1, 128, 64 * 128, 128, 128)
+    a = _qouter_args(dkv=dkv)
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_UNSUPPORTED   # VSA needs Hq == Hkv
+    bad = L.TDesc(1, 64, 2, 128, 64 * 2 * 128, 2 * 128 + 4, 128)
+    a = _qouter_args(dq=bad)
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_SHAPE         # stride % 8

@@ -198,30 +198,92 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   if (a->mode == BSA_SEL_TOKEN) {
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: token-selection mode is not built yet");
+    if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: token mode needs bf16");
+    if (!a->blk_idx) return fail(BSA_ERR_ARG, "bsa_forward_qouter: blk_idx is required");
+    if (a->S < 1 || a->S > 64) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: S must lie in [1, 64]");
+    if (a->BS != 32 && a->BS != 64 && a->BS != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block size BS must be 32, 64 or 128");
+    const int64_t G = a->dq.H / a->dkv.H;
+    const int64_t items = a->dq.B * a->dq.N * a->dkv.H * ((G + 15) / 16);
+    if (items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many tokens");
+    bsa::NsaAttnParams p{a->q, a->k, a->v, a->out,
+                         a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
+                         a->dout.sB, a->dout.sN, a->dout.sH,
+                         a->blk_idx, a->blk_cnt,
+                         (int)a->dq.B, (int)a->dq.H, (int)a->dkv.H, a->S, a->BS, a->causal ? 1 : 0,
+                         (int)a->dq.D, a->dq.N, scale_log2, a->lse};
+    return hip_status(bsa::launch_nsa_attention(p, false, s), "nsa attention launch");
   }
   return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
 }
 
 // ------------------------------------------------------------------------ KV-outer
+static bsa_status check_kvouter(const bsa_kvouter_args* a, bsa::KvOuterParams* out) {
+  if (!a) return fail(BSA_ERR_ARG, "bsa_forward_kvouter: null args");
+  if (!a->q || !a->k || !a->v || !a->q2k || !a->o_buf || !a->lse_buf || !a->nslot)
+    return fail(BSA_ERR_ARG, "bsa_forward_kvouter: q, k, v, q2k, o_buf, lse_buf and nslot are required");
+  if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: bf16 only");
+  bsa_status st = check_desc(a->dq, "q", 8, true);
+  if (st != BSA_OK) return st;
+  if ((st = check_desc(a->dkv, "k/v", 8, true)) != BSA_OK) return st;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o_buf))
+    return fail(BSA_ERR_SHAPE, "bsa_forward_kvouter: q, k, v, o_buf must be 16-byte aligned");
+  if (a->dq.D != a->dkv.D || (a->dq.D != 64 && a->dq.D != 128))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: D must be 64 or 128 for q and k/v");
+  if (a->dq.B != a->dkv.B || a->dq.N != a->dkv.N) return fail(BSA_ERR_SHAPE, "bsa_forward_kvouter: B/N mismatch");
+  if (a->dq.H % a->dkv.H) return fail(BSA_ERR_SHAPE, "bsa_forward_kvouter: Hq must be a multiple of Hkv");
+  if (a->BK != 64 && a->BK != 128) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: BK must be 64 or 128");
+  if (a->k_sel < 1 || a->k_sel > 64) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: k_sel must lie in [1, 64]");
+  if (a->chunk_cap < 0) return fail(BSA_ERR_ARG, "bsa_forward_kvouter: chunk_cap must be >= 0");
+  if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "bsa_forward_kvouter: scale must be finite");
+  const int64_t threads = a->dq.B * a->dq.N * a->dkv.H;
+  if (threads * a->k_sel >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: B*N*Hkv*k_sel must be below 2^31");
+  *out = bsa::KvOuterParams{a->q, a->k, a->v, a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
+                            a->q2k, a->q2k_cnt, (int)a->dq.B, (int)a->dq.H, (int)a->dkv.H, a->k_sel, a->BK,
+                            (int)a->dq.D, a->causal ? 1 : 0, a->chunk_cap, a->dq.N,
+                            a->scale * 1.4426950408889634f, reinterpret_cast<__bf16*>(a->o_buf), a->lse_buf,
+                            a->nslot};
+  return BSA_OK;
+}
+
 bsa_status bsa_kvouter_ws(const bsa_kvouter_args* a, size_t* bytes) {
-  (void)a;
-  (void)bytes;
-  return fail(BSA_ERR_UNSUPPORTED, "bsa_kvouter_ws: not built yet");
+  if (!bytes) return fail(BSA_ERR_ARG, "bsa_kvouter_ws: null output");
+  bsa::KvOuterParams p{};
+  bsa_status st = check_kvouter(a, &p);
+  if (st != BSA_OK) return st;
+  *bytes = bsa::kvouter_ws_bytes(p);
+  return ok();
 }
 
 bsa_status bsa_forward_kvouter(const bsa_kvouter_args* a, void* ws, size_t ws_bytes, void* stream) {
-  (void)a;
-  (void)ws;
-  (void)ws_bytes;
-  (void)stream;
-  return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: not built yet");
+  bsa::KvOuterParams p{};
+  bsa_status st = check_kvouter(a, &p);
+  if (st != BSA_OK) return st;
+  const size_t need = bsa::kvouter_ws_bytes(p);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "bsa_forward_kvouter: workspace of %zu bytes required", need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(BSA_ERR_WORKSPACE, "bsa_forward_kvouter: workspace must be 256-byte aligned");
+  return hip_status(bsa::launch_kvouter(p, ws, (hipStream_t)stream), "kv-outer launch");
 }
 
 bsa_status bsa_combine(const bsa_combine_args* a, void* stream) {
-  (void)a;
-  (void)stream;
-  return fail(BSA_ERR_UNSUPPORTED, "bsa_combine: not built yet");
+  if (!a) return fail(BSA_ERR_ARG, "bsa_combine: null args");
+  if (!a->o_buf || !a->lse_buf || !a->nslot || !a->out)
+    return fail(BSA_ERR_ARG, "bsa_combine: o_buf, lse_buf, nslot and out are required");
+  bsa_status st = check_desc(a->dout, "out", 8, true);
+  if (st != BSA_OK) return st;
+  if (!aligned16(a->o_buf) || !aligned16(a->out))
+    return fail(BSA_ERR_SHAPE, "bsa_combine: o_buf and out must be 16-byte aligned");
+  if (a->Hkv < 1 || a->dout.H % a->Hkv) return fail(BSA_ERR_SHAPE, "bsa_combine: Hq must be a multiple of Hkv");
+  if (a->k_sel < 1 || a->k_sel > 64) return fail(BSA_ERR_UNSUPPORTED, "bsa_combine: k_sel must lie in [1, 64]");
+  if (a->dout.D > 256) return fail(BSA_ERR_UNSUPPORTED, "bsa_combine: D must be <= 256");
+  if (a->dout.B * a->dout.N >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "bsa_combine: too many positions");
+  bsa::CombineParams p{reinterpret_cast<const __bf16*>(a->o_buf), a->lse_buf, a->nslot, (int)a->dout.B,
+                       (int)a->dout.H, a->Hkv, a->k_sel, (int)a->dout.D, a->dout.N,
+                       reinterpret_cast<__bf16*>(a->out), a->dout.sB, a->dout.sN, a->dout.sH, a->lse};
+  return hip_status(bsa::launch_combine(p, (hipStream_t)stream), "combine launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,411 @@
+// KV-outer schedule for gfx950: reverse index, scheduler, K1 partial attention
+// and the K2 log-sum-exp combine.
+//
+// Source: "MSA 为什么采用 KV-outer Sparse Attention Forward" -- section 5 (the
+// reverse sparse index: count queries per (KV head, KV block), prefix sum into
+// row pointers, scatter query ids), section 7 (hot KV tiles are cut into query
+// chunks of bounded size; every (query, block) partial gets a preassigned slot
+// s in [0, k) so no atomic accumulation is needed and the result is
+// deterministic), section 6.1 (K1: per slot, L_s = log sum_j exp S_j and
+// O_s = sum_j exp(S_j - L_s) V_j over the block's visible keys, written to
+// O_buf[s, i, h] and LSE_buf[s, i, h]), section 6.2 (K2: a = max_s L_s,
+// L = a + log sum_s exp(L_s - a), O = sum_s exp(L_s - L) O_s) and section 4
+// (queries selecting the same block are concatenated into 128-row tiles that
+// share one K/V tile).
+//
+// Slot rule (the page leaves it open): slot s of (query i, KV head r) is the
+// rank of the block among the row's valid selections in increasing block order
+// (ties by position), which also fixes the summation order of the combine.
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+#define BSA_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+namespace {
+
+struct KvLayout {
+  int rows;          // B * Hkv * NB reverse-index rows
+  int64_t emax;      // upper bound of edges
+  int max_chunks;    // upper bound of K1 work items
+  size_t off_count, off_cursor, off_rowptr, off_nchunk, off_chunks, off_edges, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+KvLayout kv_layout(const KvOuterParams& p) {
+  KvLayout L{};
+  const int64_t NB = (p.N + p.BK - 1) / p.BK;
+  L.rows = (int)(p.B * p.Hkv * NB);
+  L.emax = (int64_t)p.B * p.N * p.Hkv * p.ks;
+  const int cap = p.chunk_cap > 0 ? p.chunk_cap : 2 * p.ks * p.BK;
+  L.max_chunks = (int)(L.rows + (L.emax + cap - 1) / cap);
+  size_t o = 0;
+  L.off_count = o;  o += align256((size_t)L.rows * 4);
+  L.off_cursor = o; o += align256((size_t)L.rows * 4);
+  L.off_rowptr = o; o += align256((size_t)(L.rows + 1) * 4);
+  L.off_nchunk = o; o += align256(4);
+  L.off_chunks = o; o += align256((size_t)L.max_chunks * 16);
+  L.off_edges = o;  o += align256((size_t)L.emax * 8);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t kvouter_ws_bytes(const KvOuterParams& p) { return kv_layout(p).total; }
+
+// ----------------------------------------------------------------------------
+__global__ void kv_clear_kernel(int32_t* __restrict__ a, int32_t* __restrict__ b, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    a[i] = 0;
+    b[i] = 0;
+  }
+}
+
+// Slot of entry p of a selection row: rank among the valid entries in
+// increasing block order, ties by position.
+__device__ __forceinline__ int kv_slot(const int32_t* row, int cnt, int NB, int p, int blk) {
+  int s = 0;
+  for (int q = 0; q < cnt; ++q) {
+    const int o = row[q];
+    if (o < 0 || o >= NB) continue;
+    s += (o < blk || (o == blk && q < p)) ? 1 : 0;
+  }
+  return s;
+}
+
+// One thread per (b, i, r): count edges per reverse-index row, write nslot,
+// and write the empty partial (L = -inf, O = 0) of blocks that lie entirely
+// after the query when causal.
+__global__ void kv_count_kernel(KvOuterParams p, int NB, int32_t* __restrict__ count) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.N * p.Hkv;
+  if (tid >= total) return;
+  const int r = (int)(tid % p.Hkv);
+  const int64_t bi = tid / p.Hkv;
+  const int64_t i = bi % p.N;
+  const int b = (int)(bi / p.N);
+  const int32_t* row = p.q2k + tid * p.ks;
+  const int cnt = p.q2k_cnt ? min(p.q2k_cnt[tid], p.ks) : p.ks;
+  const int G = p.Hq / p.Hkv;
+  int nvalid = 0;
+  for (int q = 0; q < cnt; ++q) {
+    const int blk = row[q];
+    if (blk < 0 || blk >= NB) continue;
+    ++nvalid;
+    if (p.causal && (int64_t)blk * p.BK > i) {
+      const int s = kv_slot(row, cnt, NB, q, blk);
+      const int64_t base = (((int64_t)b * p.ks + s) * p.N + i) * p.Hq + (int64_t)r * G;
+      for (int h = 0; h < G; ++h) {
+        p.lse_buf[base + h] = -INFINITY;
+        for (int d = 0; d < p.D; ++d) p.o_buf[(base + h) * p.D + d] = (__bf16)0.f;
+      }
+    } else {
+      atomicAdd(&count[((int64_t)b * p.Hkv + r) * NB + blk], 1);
+    }
+  }
+  p.nslot[tid] = nvalid;
+}
+
+// Single workgroup: exclusive scan of the counts into row pointers, then the
+// chunk list.  Each row is cut into ceil(count / cap) chunks of at most `cap`
+// edges; chunks[c] = {row, begin, end, 0}; nchunk = number of chunks.
+__global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict__ count, int rows, int cap,
+                                                       int32_t* __restrict__ rowptr, int32_t* __restrict__ nchunk,
+                                                       int4* __restrict__ chunks) {
+  __shared__ int part[1024];
+  __shared__ int cpart[1024];
+  const int tid = threadIdx.x;
+  const int per = (rows + 1023) / 1024;
+  const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+  int s = 0, sc = 0;
+  for (int r = r0; r < r1; ++r) {
+    s += count[r];
+    sc += (count[r] + cap - 1) / cap;
+  }
+  part[tid] = s;
+  cpart[tid] = sc;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int a = tid >= o ? part[tid - o] : 0;
+    const int c = tid >= o ? cpart[tid - o] : 0;
+    __syncthreads();
+    part[tid] += a;
+    cpart[tid] += c;
+    __syncthreads();
+  }
+  int e = part[tid] - s;    // exclusive prefix of this thread's first row
+  int ce = cpart[tid] - sc;
+  for (int r = r0; r < r1; ++r) {
+    rowptr[r] = e;
+    const int n = count[r];
+    for (int c0 = 0; c0 < n; c0 += cap) chunks[ce++] = make_int4(r, e + c0, e + min(n, c0 + cap), 0);
+    e += n;
+  }
+  if (tid == 1023) {
+    rowptr[rows] = part[1023];
+    *nchunk = cpart[1023];
+  }
+}
+
+// One thread per (b, i, r): scatter (position, slot) edges into the rows.
+__global__ void kv_scatter_kernel(KvOuterParams p, int NB, const int32_t* __restrict__ rowptr,
+                                  int32_t* __restrict__ cursor, int2* __restrict__ edges) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.N * p.Hkv;
+  if (tid >= total) return;
+  const int r = (int)(tid % p.Hkv);
+  const int64_t bi = tid / p.Hkv;
+  const int64_t i = bi % p.N;
+  const int b = (int)(bi / p.N);
+  const int32_t* row = p.q2k + tid * p.ks;
+  const int cnt = p.q2k_cnt ? min(p.q2k_cnt[tid], p.ks) : p.ks;
+  for (int q = 0; q < cnt; ++q) {
+    const int blk = row[q];
+    if (blk < 0 || blk >= NB) continue;
+    if (p.causal && (int64_t)blk * p.BK > i) continue;
+    const int s = kv_slot(row, cnt, NB, q, blk);
+    const int64_t rid = ((int64_t)b * p.Hkv + r) * NB + blk;
+    const int at = rowptr[rid] + atomicAdd(&cursor[rid], 1);
+    edges[at] = make_int2((int)i, s);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// K1.  One workgroup (4 waves) per chunk of a reverse-index row (b, r, blk):
+// the block's K and V tiles (BK keys x D) are staged in LDS once; the chunk's
+// edges x G heads form a flat list of query rows processed 128 at a time, 32
+// rows per wave:
+//   S^T (keys x rows) = K Q^T     32x32x16 bf16 MFMA, all BK keys at once
+//   single-pass local softmax per row (causal mask per query position)
+//   O^T (chans x rows) = V^T P^T  32x32x16 bf16 MFMA
+// and every row writes its normalised partial O_s (bf16) and L_s (fp32) to the
+// edge's preassigned slot.
+// ----------------------------------------------------------------------------
+template <int D, int BK>
+struct K1Shape {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int LPT = BK * CPR / 256;      // tile copies per thread
+  static constexpr int KT = BK / 32;              // 32-key tiles of S^T
+  static constexpr int KS = D / 16;               // k-steps of QK^T
+  static constexpr int DT = D / 32;               // 32-channel tiles of O^T
+  static constexpr int US = BK / 16;              // 16-key steps of PV
+};
+
+template <int CPR>
+__device__ __forceinline__ int k1_k_swz(int r, int c) { return c ^ (r & 7); }
+template <int CPR>
+__device__ __forceinline__ int k1_v_swz(int r, int c) {
+  if constexpr (CPR >= 16) {
+    constexpr int f[4] = {0, 6, 10, 12};
+    return c ^ f[r & 3];
+  } else {
+    return c ^ (2 * (r & 3));
+  }
+}
+
+template <int D, int BK>
+__global__ __launch_bounds__(256) void kv_k1_kernel(KvOuterParams p, int NB, const int32_t* __restrict__ nchunk,
+                                                    const int4* __restrict__ chunks, const int2* __restrict__ edges) {
+  using SH = K1Shape<D, BK>;
+  __shared__ __align__(1024) __bf16 Ks[BK * D];
+  __shared__ __align__(1024) __bf16 Vs[BK * D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h2 = lane >> 5;
+  if ((int)blockIdx.x >= *nchunk) return;
+  const int4 ck = chunks[blockIdx.x];
+  const int rid = ck.x, e0 = ck.y, e1 = ck.z;
+  const int blk = rid % NB;
+  const int r = (rid / NB) % p.Hkv;
+  const int b = rid / (NB * p.Hkv);
+  const int G = p.Hq / p.Hkv;
+  const int64_t k0 = (int64_t)blk * BK;
+  const int nkeys = (int)min((int64_t)BK, p.N - k0);
+
+  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + r * p.kv_sH;
+  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + r * p.kv_sH;
+  // ---- stage the K and V tiles once (rows past N clamped to valid memory) ----
+#pragma unroll
+  for (int kk = 0; kk < SH::LPT; ++kk) {
+    const int chunk = (kk * 4 + w) * 64 + lane;
+    const int row = chunk / SH::CPR, pc = chunk % SH::CPR;
+    const int64_t pos = k0 + min(row, nkeys - 1);
+    global_to_lds16(kg + pos * p.kv_sN + k1_k_swz<SH::CPR>(row, pc) * 8, Ks + (size_t)(kk * 4 + w) * 64 * 8);
+    global_to_lds16(vg + pos * p.kv_sN + k1_v_swz<SH::CPR>(row, pc) * 8, Vs + (size_t)(kk * 4 + w) * 64 * 8);
+  }
+  wait_vmcnt<0>();
+  BSA_BARRIER();
+
+  const int64_t nrows = (int64_t)(e1 - e0) * G;
+  const __bf16* __restrict__ qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB;
+  for (int64_t t0 = 0; t0 < nrows; t0 += 128) {
+    // ---- this lane's query row: flat index t0 + 32w + l%32 -> (edge, head) ----
+    const int64_t fr = t0 + 32 * w + (lane & 31);
+    const bool row_ok = fr < nrows;
+    const int64_t frc = row_ok ? fr : nrows - 1;
+    const int2 ed = edges[e0 + frc / G];
+    const int hq = r * G + (int)(frc % G);
+    const int64_t qpos = ed.x;
+    const __bf16* qrow = qbase + qpos * p.q_sN + (int64_t)hq * p.q_sH;
+    bf16x8 qop[SH::KS];
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * h2);
+
+    // ---- S^T over all BK keys ----
+    f32x16 sacc[SH::KT];
+#pragma unroll
+    for (int kt = 0; kt < SH::KT; ++kt) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sacc[kt][x] = 0.f;
+      const int krow = 32 * kt + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Ks + krow * D + k1_k_swz<SH::CPR>(krow, 2 * s + h2) * 8);
+        sacc[kt] = mfma32(a, qop[s], sacc[kt]);
+      }
+    }
+    // ---- local softmax (log2 domain) with the causal / tail mask ----
+    const int64_t last = p.causal ? min(qpos, p.N - 1) : p.N - 1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < SH::KT; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int key = 32 * kt + 8 * (x >> 2) + 4 * h2 + (x & 3);
+        const bool ok = key < nkeys && k0 + key <= last;
+        const float v = ok ? sacc[kt][x] * p.scale_log2 : -INFINITY;
+        sacc[kt][x] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    float rs = 0.f;
+    bf16x8 pop[SH::US];
+#pragma unroll
+    for (int kt = 0; kt < SH::KT; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float pr = fast_exp2(sacc[kt][x] - m_use);
+        rs += pr;
+        pop[2 * kt + (x >> 3)][x & 7] = (__bf16)pr;
+      }
+    const float l_tot = rs + xor32(rs);
+    // ---- O^T = V^T P^T ----
+    f32x16 oacc[SH::DT];
+#pragma unroll
+    for (int dt = 0; dt < SH::DT; ++dt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) oacc[dt][x] = 0.f;
+    {
+      const int g16 = lane >> 4, jl = lane & 15;
+#pragma unroll
+      for (int u = 0; u < SH::US; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < SH::DT; ++dt) {
+          const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
+          const int c = d >> 3, off = d & 7;
+          const int r0 = 16 * u + 4 * h2 + (jl >> 2);
+          const int r1 = r0 + 8;
+          const bf16x4 lo = lds_read_tr16(Vs + r0 * D + k1_v_swz<SH::CPR>(r0, c) * 8 + off);
+          const bf16x4 hi = lds_read_tr16(Vs + r1 * D + k1_v_swz<SH::CPR>(r1, c) * 8 + off);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dt] = mfma32(a, pop[u], oacc[dt]);
+        }
+      }
+    }
+    // ---- write the normalised partial and its log-sum-exp to the edge's slot ----
+    if (row_ok) {
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const int64_t obase = (((int64_t)b * p.ks + ed.y) * p.N + qpos) * p.Hq + hq;
+      __bf16* orow = p.o_buf + obase * D;
+#pragma unroll
+      for (int dt = 0; dt < SH::DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 32 * dt + 8 * jj + 4 * h2;
+          bf16x4 v4 = {(__bf16)(oacc[dt][4 * jj + 0] * inv), (__bf16)(oacc[dt][4 * jj + 1] * inv),
+                       (__bf16)(oacc[dt][4 * jj + 2] * inv), (__bf16)(oacc[dt][4 * jj + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(orow + d) = v4;
+        }
+      if (h2 == 0) p.lse_buf[obase] = (l_tot > 0.f) ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, int BK>
+static hipError_t launch_k1(const KvOuterParams& p, int NB, const KvLayout& L, char* ws, hipStream_t s) {
+  kv_k1_kernel<D, BK><<<dim3(L.max_chunks), dim3(256), 0, s>>>(
+      p, NB, reinterpret_cast<const int32_t*>(ws + L.off_nchunk), reinterpret_cast<const int4*>(ws + L.off_chunks),
+      reinterpret_cast<const int2*>(ws + L.off_edges));
+  return hipGetLastError();
+}
+
+hipError_t launch_kvouter(const KvOuterParams& p, void* wsv, hipStream_t s) {
+  const KvLayout L = kv_layout(p);
+  char* ws = static_cast<char*>(wsv);
+  const int NB = (int)((p.N + p.BK - 1) / p.BK);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + L.off_count);
+  int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.off_cursor);
+  int32_t* rowptr = reinterpret_cast<int32_t*>(ws + L.off_rowptr);
+  int32_t* nchunk = reinterpret_cast<int32_t*>(ws + L.off_nchunk);
+  int4* chunks = reinterpret_cast<int4*>(ws + L.off_chunks);
+  int2* edges = reinterpret_cast<int2*>(ws + L.off_edges);
+  const int cap = p.chunk_cap > 0 ? p.chunk_cap : 2 * p.ks * p.BK;
+
+  kv_clear_kernel<<<dim3(min(1024, (L.rows + 255) / 256)), dim3(256), 0, s>>>(count, cursor, L.rows);
+  const int64_t threads = (int64_t)p.B * p.N * p.Hkv;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  kv_count_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, count);
+  kv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, L.rows, cap, rowptr, nchunk, chunks);
+  kv_scatter_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, rowptr, cursor, edges);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.D == 128) return p.BK == 128 ? launch_k1<128, 128>(p, NB, L, ws, s) : launch_k1<128, 64>(p, NB, L, ws, s);
+  return p.BK == 128 ? launch_k1<64, 128>(p, NB, L, ws, s) : launch_k1<64, 64>(p, NB, L, ws, s);
+}
+
+// ----------------------------------------------------------------------------
+// K2: one workgroup per (b, position); thread handles 8 channels of one head.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_combine_kernel(CombineParams p) {
+  const int64_t bi = blockIdx.x;
+  const int64_t i = bi % p.N;
+  const int b = (int)(bi / p.N);
+  const int G = p.Hq / p.Hkv;
+  const int cpr = p.D / 8;
+  for (int c = threadIdx.x; c < p.Hq * cpr; c += 256) {
+    const int hq = c / cpr, dc = c % cpr;
+    const int n = min(p.nslot[((int64_t)b * p.N + i) * p.Hkv + hq / G], p.ks);
+    float a = -INFINITY;
+    for (int s = 0; s < n; ++s) a = fmaxf(a, p.lse_buf[(((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = -INFINITY;
+    if (n > 0 && a != -INFINITY) {
+      float z = 0.f;
+      for (int s = 0; s < n; ++s)
+        z += __expf(p.lse_buf[(((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq] - a);
+      L = a + __logf(z);
+      for (int s = 0; s < n; ++s) {
+        const int64_t row = (((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq;
+        const float wgt = __expf(p.lse_buf[row] - L);
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[e];
+      }
+    }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)acc[e];
+    *reinterpret_cast<bf16x8*>(p.out + b * p.o_sB + i * p.o_sN + hq * p.o_sH + dc * 8) = out;
+    if (p.lse && dc == 0) p.lse[((int64_t)b * p.Hq + hq) * p.N + i] = L;
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+  kv_combine_kernel<<<dim3((unsigned)(p.B * p.N)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

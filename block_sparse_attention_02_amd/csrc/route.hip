@@ -6,6 +6,8 @@
 // (per-block means of Q and K per batch and head, divided by the true length),
 // section 2.2 (E = Q_bar K_bar^T / sqrt(D), per-row TopK on the logits) and
 // section 4 (kept block ids in increasing order, -1 fill, separate count).
+#include <type_traits>
+
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -50,10 +52,14 @@ hipError_t launch_tile_index(int T, int H, int W, int bT, int bH, int bW, int J,
 // ============================================================================
 // Pool: one workgroup per (block i, batch b, tensor).  Each token row of all
 // heads is read with 16-byte loads (VW elements) and accumulated in fp32; the
-// sum is divided by the block's true length.
+// sum is divided by the block's true length.  Loads are unconditional (lanes
+// past the row read a clamped address and discard it) so that the UT x CPT
+// loads of an iteration are all in flight together.
 // ============================================================================
 template <typename T, int VW, int CPT>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  constexpr int UT = (CPT <= 2) ? 8 : 4;  // tokens per iteration
+  using Vec = typename std::conditional<VW == 1, T, u32x4>::type;
   const T* __restrict__ x = reinterpret_cast<const T*>(blockIdx.z ? p.k : p.q);
   float* __restrict__ out = blockIdx.z ? p.kbar : p.qbar;
   const int i = blockIdx.x, b = blockIdx.y;
@@ -67,41 +73,33 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     int64_t off[CPT];
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = c0 + threadIdx.x + 256 * u;
-      const int hh = c / cpr, dc = c % cpr;
-      off[u] = (c < nch) ? (int64_t)hh * p.sH + (int64_t)dc * VW : -1;
+      const int c = min(c0 + (int)threadIdx.x + 256 * u, nch - 1);
+      off[u] = (int64_t)(c / cpr) * p.sH + (int64_t)(c % cpr) * VW;
 #pragma unroll
       for (int e = 0; e < VW; ++e) acc[u][e] = 0.f;
     }
-    int r = 0;
-    for (; r + 4 <= n; r += 4) {
-      T v[4][CPT][VW];
+    for (int r = 0; r < n; r += UT) {
+      Vec v[UT][CPT];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const T* row = xb + (int64_t)members[r + rr] * p.sN;
+      for (int rr = 0; rr < UT; ++rr) {
+        const T* row = xb + (int64_t)members[min(r + rr, n - 1)] * p.sN;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) v[rr][u] = *reinterpret_cast<const Vec*>(row + off[u]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < UT; ++rr) {
+        if (r + rr >= n) break;
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-          if (off[u] >= 0) {
+          if constexpr (VW == 1) {
+            acc[u][0] += (float)v[rr][u];
+          } else {
+            const T* e8 = reinterpret_cast<const T*>(&v[rr][u]);
 #pragma unroll
-            for (int e = 0; e < VW; ++e) v[rr][u][e] = row[off[u] + e];
+            for (int e = 0; e < VW; ++e) acc[u][e] += (float)e8[e];
           }
         }
       }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int u = 0; u < CPT; ++u)
-          if (off[u] >= 0)
-#pragma unroll
-            for (int e = 0; e < VW; ++e) acc[u][e] += (float)v[rr][u][e];
-    }
-    for (; r < n; ++r) {
-      const T* row = xb + (int64_t)members[r] * p.sN;
-#pragma unroll
-      for (int u = 0; u < CPT; ++u)
-        if (off[u] >= 0)
-#pragma unroll
-          for (int e = 0; e < VW; ++e) acc[u][e] += (float)row[off[u] + e];
     }
     const float fn = (float)n;
 #pragma unroll
@@ -177,7 +175,8 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-template <int NT, int RT>
+// KD: D when it is a multiple of 32 (compile-time fast path), else 0.
+template <int NT, int RT, int KD>
 __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   constexpr int BM = 16 * RT;              // query blocks per workgroup
   constexpr int CW = 16 * NT;              // columns per wave
@@ -214,26 +213,31 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   // ---- scores: E^T tiles for this wave's columns -----------------------------
   float sc[RT][NT][4];
   const int g = lane >> 4, l16 = lane & 15;
+  if constexpr (KD > 0) {
+    // D is a multiple of 32: unconditional loads (rows past J clamped), and the
+    // next column tile's operands are fetched before this tile's products.
+    constexpr int KS = KD / 32;
+    f32x4 kbuf[2][2 * KS];
+    auto fetch = [&](f32x4* dst, int t) {
+      const int jr = min(w * CW + 16 * t + l16, J - 1);
+      const float* src = kb + (int64_t)jr * KD + 8 * g;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int j0 = w * CW + 16 * t;
-    const int jr = j0 + l16;  // A-operand row (key block)
-    f32x4 acc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (j0 < J) {
       for (int s = 0; s < KS; ++s) {
-        const int d0 = 32 * s + 8 * g;
-        float kv[8];
-        if (jr < J && d0 + 8 <= D) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(kb + (int64_t)jr * D + d0);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(kb + (int64_t)jr * D + d0 + 4);
-          kv[0] = a[0]; kv[1] = a[1]; kv[2] = a[2]; kv[3] = a[3];
-          kv[4] = b[0]; kv[5] = b[1]; kv[6] = b[2]; kv[7] = b[3];
-        } else {
+        dst[2 * s] = *reinterpret_cast<const f32x4*>(src + 32 * s);
+        dst[2 * s + 1] = *reinterpret_cast<const f32x4*>(src + 32 * s + 4);
+      }
+    };
+    fetch(kbuf[0], 0);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kv[e] = (jr < J && d0 + e < D) ? kb[(int64_t)jr * D + d0 + e] : 0.f;
-        }
+    for (int t = 0; t < NT; ++t) {
+      if (t + 1 < NT) fetch(kbuf[(t + 1) & 1], t + 1);
+      f32x4 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const f32x4 a = kbuf[t & 1][2 * s], c = kbuf[t & 1][2 * s + 1];
+        const float kv[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
         bf16x8 khi, klo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -243,18 +247,55 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int row = 16 * rt + l16;
-          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi + row * DP + d0);
-          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo + row * DP + d0);
+          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi + row * DP + 32 * s + 8 * g);
+          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo + row * DP + 32 * s + 8 * g);
           acc[rt] = mfma16(klo, qh, acc[rt]);
           acc[rt] = mfma16(khi, ql, acc[rt]);
           acc[rt] = mfma16(khi, qh, acc[rt]);
         }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
     }
+  } else {
+    // any D <= 256: element-wise guarded loads (small problems)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int t = 0; t < NT; ++t) {
+      const int j0 = w * CW + 16 * t;
+      const int jr = j0 + l16;
+      f32x4 acc[RT];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j0 < J) {
+        for (int s = 0; s < KS; ++s) {
+          const int d0 = 32 * s + 8 * g;
+          float kv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[e] = (jr < J && d0 + e < D) ? kb[(int64_t)jr * D + d0 + e] : 0.f;
+          bf16x8 khi, klo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            khi[e] = (__bf16)kv[e];
+            klo[e] = (__bf16)(kv[e] - (float)khi[e]);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int row = 16 * rt + l16;
+            const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi + row * DP + d0);
+            const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo + row * DP + d0);
+            acc[rt] = mfma16(klo, qh, acc[rt]);
+            acc[rt] = mfma16(khi, ql, acc[rt]);
+            acc[rt] = mfma16(khi, qh, acc[rt]);
+          }
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
+    }
   }
 
   // optional debug copy of the scores
@@ -386,6 +427,14 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   }
 }
 
+template <int NT, int RT, int KD>
+static hipError_t launch_route_k(const RouteParams& p, size_t smem, hipStream_t s) {
+  constexpr int BM = 16 * RT;
+  dim3 grid((p.J + BM - 1) / BM, p.B * p.H);
+  route_topk_kernel<NT, RT, KD><<<grid, 512, smem, s>>>(p);
+  return hipGetLastError();
+}
+
 template <int NT, int RT>
 static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
   constexpr int BM = 16 * RT;
@@ -393,9 +442,12 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
   const int KS = (p.D + 31) / 32, DP = KS * 32 + 8;
   const size_t smem = (size_t)2 * BM * DP * sizeof(__bf16) + (size_t)2 * BM * MW * 4 +
                       (size_t)2 * kRouteWaves * BM * 4;
-  dim3 grid((p.J + BM - 1) / BM, p.B * p.H);
-  route_topk_kernel<NT, RT><<<grid, 512, smem, s>>>(p);
-  return hipGetLastError();
+  switch (p.D) {
+    case 64: return launch_route_k<NT, RT, 64>(p, smem, s);
+    case 128: return launch_route_k<NT, RT, 128>(p, smem, s);
+    case 256: return launch_route_k<NT, RT, 256>(p, smem, s);
+    default: return launch_route_k<NT, RT, 0>(p, smem, s);
+  }
 }
 
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s) {

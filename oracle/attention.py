@@ -146,27 +146,28 @@ def kvouter_partials(q, k, v, q2k, BK, causal=True, scale=None, q2k_cnt=None,
     an empty J_s gives L_s = -inf and O_s = 0.
 
     Returns O_buf [B, ks, N, Hq, D], LSE_buf [B, ks, N, Hq] (unused slots:
-    O = 0, L = -inf) and nslot [B, N, Hkv].  ``positions`` optionally
-    restricts the work to a list of (b, i); other entries stay NaN / -1.
+    O = 0, L = -inf) and nslot [B, N, Hkv].  With ``positions`` (a list of
+    (b, i)) only those rows are computed and the arrays are compact, indexed by
+    the list order: O_buf [P, ks, Hq, D], LSE_buf [P, ks, Hq], nslot [P, Hkv].
     """
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     ks = q2k.shape[-1]
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
-    O_buf = np.full((B, ks, N, Hq, D), np.nan)
-    LSE_buf = np.full((B, ks, N, Hq), np.nan)
-    nslot = np.full((B, N, Hkv), -1, dtype=np.int64)
+    compact = positions is not None
     if positions is None:
         positions = [(b, i) for b in range(B) for i in range(N)]
-    for (b, i) in positions:
-        O_buf[b, :, i] = 0.0
-        LSE_buf[b, :, i] = -np.inf
+    P = len(positions)
+    O_buf = np.zeros((P, ks, Hq, D))
+    LSE_buf = np.full((P, ks, Hq), -np.inf)
+    nslot = np.zeros((P, Hkv), dtype=np.int64)
+    for n, (b, i) in enumerate(positions):
         for r in range(Hkv):
             row = q2k[b, i, r]
             cnt = ks if q2k_cnt is None else int(q2k_cnt[b, i, r])
             blocks = sorted(int(x) for x in row[:cnt] if x >= 0)
-            nslot[b, i, r] = len(blocks)
+            nslot[n, r] = len(blocks)
             heads = slice(r * G, (r + 1) * G)
             qq = q[b, i, heads, :].astype(np.float64)
             for s, blk in enumerate(blocks):
@@ -176,9 +177,14 @@ def kvouter_partials(q, k, v, q2k, BK, causal=True, scale=None, q2k_cnt=None,
                 kk = k[b, keys, r, :].astype(np.float64)
                 vv = v[b, keys, r, :].astype(np.float64)
                 w, l_ = _softmax_rows((qq @ kk.T) * scale)
-                O_buf[b, s, i, heads, :] = w @ vv
-                LSE_buf[b, s, i, heads] = l_
-    return O_buf, LSE_buf, nslot
+                O_buf[n, s, heads, :] = w @ vv
+                LSE_buf[n, s, heads] = l_
+    if compact:
+        return O_buf, LSE_buf, nslot
+    # full layout: [B, ks, N, Hq, D], [B, ks, N, Hq], [B, N, Hkv]
+    O_full = O_buf.reshape(B, N, ks, Hq, D).transpose(0, 2, 1, 3, 4)
+    L_full = LSE_buf.reshape(B, N, ks, Hq).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(O_full), np.ascontiguousarray(L_full), nslot.reshape(B, N, Hkv)
 
 
 def lse_combine(O_buf, LSE_buf, nslot, G):

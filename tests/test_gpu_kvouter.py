@@ -1,0 +1,150 @@
+"""GPU parity of the KV-outer schedule (reverse index, scheduler, K1 partials)
+and the K2 combine against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_attn_close, to64
+from workloads import msa_inputs, nsa_inputs, scaled, workload
+
+pytestmark = pytest.mark.gpu
+
+bsa = pytest.importorskip("block_sparse_attention_02_amd")
+DEV = torch.device("cuda:0")
+
+
+def _slot_mask(nslot, ks, G):
+    """[B, ks, N, Hq] mask of the valid slots."""
+    n = np.repeat(nslot, G, axis=2)                          # [B, N, Hq]
+    return np.arange(ks)[None, :, None, None] < n[:, None, :, :]
+
+
+def _check_partials(q, k, v, q2k, BK, causal, cnt, o_buf, lse_buf, nslot, name):
+    Hq, Hkv = q.shape[2], k.shape[2]
+    G = Hq // Hkv
+    ks = q2k.shape[-1]
+    r_o, r_l, r_n = oracle.kvouter_partials(to64(q), to64(k), to64(v), q2k.cpu().numpy(), BK, causal=causal,
+                                            q2k_cnt=None if cnt is None else cnt.cpu().numpy())
+    got_n = nslot.cpu().numpy()
+    assert np.array_equal(got_n, r_n), "nslot differs"
+    valid = _slot_mask(r_n, ks, G)
+    got_l = to64(lse_buf)
+    fin = valid & np.isfinite(r_l)
+    assert np.array_equal(np.isneginf(got_l[valid]), np.isneginf(r_l[valid]))
+    assert np.abs(got_l[fin] - r_l[fin]).max() <= 1e-3
+    assert_attn_close(o_buf, np.nan_to_num(r_o), name + " partials", mask=np.broadcast_to(valid[..., None], r_o.shape))
+    return r_o, r_l, r_n
+
+
+CASES = {
+    "msa_g16_bk128": (scaled("msa", N=2048, Hq=32, Hkv=2), True),
+    "msa_g8_bk64_d64": (scaled("msa", N=1500, Hq=16, Hkv=2, BK=64, D=64, k=8), True),
+    "msa_noncausal": (scaled("msa", N=1024, Hq=16, Hkv=1, k=6), False),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_kvouter_partials_and_combine(name):
+    cfg, causal = CASES[name]
+    print("case", name, flush=True)
+    q, k, v, q2k = msa_inputs(cfg, device=DEV)
+    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k, cfg["BK"], causal=causal)
+    out, lse = bsa.combine(o_buf, lse_buf, nslot, cfg["Hkv"], need_lse=True)
+    torch.cuda.synchronize()
+    r_o, r_l, r_n = _check_partials(q, k, v, q2k, cfg["BK"], causal, None, o_buf, lse_buf, nslot, name)
+    ref, ref_lse = oracle.nsa_attention(to64(q), to64(k), to64(v), q2k.cpu().numpy(), None, cfg["BK"], causal=causal)
+    assert_attn_close(out, ref, name + " combined")
+    got_lse = to64(lse).transpose(0, 2, 1)
+    fin = np.isfinite(ref_lse)
+    assert np.abs(got_lse[fin] - ref_lse[fin]).max() <= 1e-3
+    # the oracle's own combine of the oracle partials agrees too (identity check)
+    c_o, _ = oracle.lse_combine(r_o, r_l, r_n, G=cfg["Hq"] // cfg["Hkv"])
+    assert np.abs(c_o - ref).max() < 1e-10
+
+
+def test_kvouter_chunking_is_bitwise_invariant():
+    cfg = scaled("msa", N=2048, Hq=32, Hkv=2)
+    q, k, v, q2k = msa_inputs(cfg, device=DEV)
+    outs = []
+    for cap in (0, 128, 1 << 30):
+        o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k, 128, chunk_cap=cap)
+        out = bsa.combine(o_buf, lse_buf, nslot, 2)
+        torch.cuda.synchronize()
+        valid = torch.from_numpy(_slot_mask(nslot.cpu().numpy(), 16, 16)).to(DEV)
+        outs.append((torch.where(valid[..., None], o_buf, torch.zeros_like(o_buf)).clone(),
+                     torch.where(valid, lse_buf, torch.zeros_like(lse_buf)).clone(), out.clone()))
+    for o, l, fin in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+        assert torch.equal(fin.view(torch.int16), outs[0][2].view(torch.int16))
+
+
+def test_kvouter_counts_padding_duplicates():
+    """Counts, -1 entries inside the count, duplicate blocks and future blocks."""
+    cfg = scaled("msa", N=1024, Hq=16, Hkv=1, k=8)
+    q, k, v, q2k = msa_inputs(cfg, device=DEV)
+    sel = q2k.cpu().numpy().copy()
+    rng = np.random.default_rng(9)
+    cnt = np.full(sel.shape[:-1], 8, dtype=np.int32)
+    NB = 1024 // 128
+    for i in rng.integers(0, 1024, 60):
+        row = sel[0, i, 0]
+        c = int(rng.integers(1, 9))
+        cnt[0, i, 0] = c
+        if c >= 3:
+            row[1] = -1
+            row[2] = row[0]                              # duplicate
+        if c >= 4:
+            row[3] = int(rng.integers(0, NB))            # maybe after the query
+    q2k_d = torch.from_numpy(sel).to(DEV)
+    cnt_d = torch.from_numpy(cnt).to(DEV)
+    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k_d, 128, q2k_cnt=cnt_d)
+    out = bsa.combine(o_buf, lse_buf, nslot, 1)
+    torch.cuda.synchronize()
+    _check_partials(q, k, v, q2k_d, 128, True, cnt_d, o_buf, lse_buf, nslot, "padded")
+    ref, _ = oracle.nsa_attention(to64(q), to64(k), to64(v), sel, cnt, 128, causal=True)
+    assert_attn_close(out, ref, "padded combined")
+
+
+def test_nsa_indices_through_kvouter():
+    """The NSA workload's selections run through the KV-outer schedule."""
+    cfg = scaled("nsa", T=1024, HQ=32, H=2)
+    q, k, v, idx, cnt = nsa_inputs(cfg, device=DEV)
+    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, idx, 64, q2k_cnt=cnt)
+    out = bsa.combine(o_buf, lse_buf, nslot, 2)
+    qo = bsa.attention_nsa(q, k, v, idx, cnt, 64)
+    torch.cuda.synchronize()
+    ref, _ = oracle.nsa_attention(to64(q), to64(k), to64(v), idx.cpu().numpy(), cnt.cpu().numpy(), 64)
+    assert_attn_close(out, ref, "nsa via kv-outer")
+    assert_attn_close(qo, ref, "nsa via q-outer")
+
+
+def test_msa_full_size_sampled():
+    """The full MSA workload (65536 positions, 64/4 heads, k=16, BK=128)."""
+    cfg = workload("msa")
+    print("case msa full size", flush=True)
+    q, k, v, q2k = msa_inputs(cfg, device=DEV)
+    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k, 128)
+    out = bsa.combine(o_buf, lse_buf, nslot, 4)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    pos = [(0, int(i)) for i in rng.integers(0, cfg["N"], 24)] + [(0, 0), (0, 127), (0, 128), (0, cfg["N"] - 1)]
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    sel = q2k.cpu().numpy()
+    ref, _ = oracle.nsa_attention(q64, k64, v64, sel, None, 128, causal=True, tokens=pos)
+    mask = np.zeros(ref.shape, dtype=bool)
+    for (b, i) in pos:
+        mask[b, i] = True
+    assert_attn_close(out, np.nan_to_num(ref), "msa full (sampled)", mask=mask)
+    r_o, r_l, r_n = oracle.kvouter_partials(q64, k64, v64, sel, 128, positions=pos)
+    got_n = nslot.cpu().numpy()
+    for n_, (b, i) in enumerate(pos):
+        assert np.array_equal(got_n[b, i], r_n[n_])
+        for r in range(4):
+            heads = slice(16 * r, 16 * r + 16)
+            for s in range(int(r_n[n_, r])):
+                gl = to64(lse_buf[b, s, i, heads])
+                assert np.abs(gl - r_l[n_, s, heads]).max() <= 1e-3
+                assert np.abs(to64(o_buf[b, s, i, heads]) - r_o[n_, s, heads]).max() <= 2e-2

@@ -257,15 +257,19 @@ def test_kvouter_slot_rule_and_partials():
     q2k = np.full((1, T, H, 4), -1)
     q2k[0, i] = row[0]
     O_buf, L_buf, nslot = oracle.kvouter_partials(q, k, v, q2k, BK, positions=[(0, i)])
-    assert nslot[0, i, 0] == 3
+    assert nslot[0, 0] == 3
     for s, blk in enumerate([0, 3, 6]):
         keys = np.arange(blk * BK, min((blk + 1) * BK, i + 1))
         logits = q[0, i] @ k[0, keys, 0].T / math.sqrt(D)      # [HQ, n]
         lse = logsumexp(logits, axis=-1)
         w = np.exp(logits - lse[:, None])
-        assert np.abs(L_buf[0, s, i] - lse).max() < 1e-12
-        assert np.abs(O_buf[0, s, i] - w @ v[0, keys, 0]).max() < 1e-12
-    assert np.isneginf(L_buf[0, 3, i]).all() and (O_buf[0, 3, i] == 0).all()
+        assert np.abs(L_buf[0, s] - lse).max() < 1e-12
+        assert np.abs(O_buf[0, s] - w @ v[0, keys, 0]).max() < 1e-12
+    assert np.isneginf(L_buf[0, 3]).all() and (O_buf[0, 3] == 0).all()
+    # the compact rows equal the full-layout rows
+    O_f, L_f, n_f = oracle.kvouter_partials(q, k, v, q2k, BK)
+    assert np.array_equal(O_f[0, :, i], O_buf[0]) and np.array_equal(L_f[0, :, i], L_buf[0])
+    assert np.array_equal(n_f[0, i], nslot[0])
 
 
 def test_combine_single_slot_and_weights():

@@ -12,7 +12,7 @@ batch of synthetic input already resident in HBM:
   nsa    NSA selected-branch attention (32768 tokens, 64 query / 4 KV heads,
          blocks of 64, up to 16 selected), query-outer.
   msa    KV-outer schedule + combine (65536 tokens, 64 query / 4 KV heads,
-         KV blocks of 128, 16 selected blocks), when built.
+         KV blocks of 128, 16 selected blocks).
 
 Prints one JSON line.  ``value`` is the effective attention throughput of the
 whole step, 4*h*N*D*k*M / step time (the pages' FLOP count), in TFLOP/s.
@@ -141,6 +141,106 @@ def bench_video(args):
     return res, ctx
 
 
+def _time(fn, steps, warmup, stream):
+    """Average ms of fn() over `steps` launches, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return sum(a.elapsed_time(b) for a, b in evs) / steps, wall
+
+
+def bench_nsa(args):
+    """NSA selected branch, query-outer (token mode), 32768 tokens."""
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import nsa_inputs, workload
+
+    cfg = workload("nsa")
+    dev = torch.device("cuda:0")
+    q, k, v, idx, cnt = nsa_inputs(cfg, device=dev)
+    G = cfg["HQ"] // cfg["H"]
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    ms, wall = _time(lambda: bsa.attention_nsa(q, k, v, idx, cnt, cfg["BS"], out=out), args.steps, args.warmup,
+                     stream)
+    flops = bsa.metrics.nsa_nominal_flops(cnt, cfg["BS"], G, cfg["D"])
+    # algorithmic bytes: q read, o written, k/v read once, index tables
+    nbytes = 2 * q.numel() * 2 + 2 * k.numel() * 2 + idx.numel() * 4 + cnt.numel() * 4
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), random causal selections)",
+        "config": {"workload": "nsa_selected_branch", "T": cfg["T"], "HQ": cfg["HQ"], "H": cfg["H"], "D": cfg["D"],
+                   "BS": cfg["BS"], "S": cfg["S"], "causal": True},
+        "ms": {"attn": round(ms, 4)},
+        "roofline": {"kernel": "nsa_attn_kernel (bsa_forward_qouter, token mode)", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "hbm_gbps_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
+    }
+
+
+def bench_msa(args):
+    """KV-outer schedule (reverse index, scheduler, K1) + combine, 65536 positions."""
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import msa_inputs, workload
+
+    cfg = workload("msa")
+    dev = torch.device("cuda:0")
+    q, k, v, q2k = msa_inputs(cfg, device=dev)
+    B, N, Hq, D = q.shape
+    Hkv, ks, BK = cfg["Hkv"], cfg["k"], cfg["BK"]
+    G = Hq // Hkv
+    bufs = (torch.empty((B, ks, N, Hq, D), dtype=torch.bfloat16, device=dev),
+            torch.empty((B, ks, N, Hq), dtype=torch.float32, device=dev),
+            torch.empty((B, N, Hkv), dtype=torch.int32, device=dev))
+    out = torch.empty_like(q)
+    ws = [None]
+    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k, BK, bufs=bufs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def k1():
+        bsa.kvouter(q, k, v, q2k, BK, bufs=bufs, workspace=ws[0])
+
+    ws[0] = torch.empty(256 << 20, dtype=torch.uint8, device=dev)   # >= bsa_kvouter_ws for this shape
+    ms_k1, _ = _time(k1, args.steps, args.warmup, stream)
+    ms_k2, _ = _time(lambda: bsa.combine(o_buf, lse_buf, nslot, Hkv, out=out), args.steps, args.warmup, stream)
+    edges = int((q2k >= 0).sum().item())
+    flops = bsa.metrics.kvouter_nominal_flops(q2k, BK, G, D)
+    # K1 algorithmic bytes (the page's I/O model): K/V once, Q per edge, O_buf + LSE per edge
+    k1_bytes = 2 * k.numel() * 2 + edges * G * D * 2 * 2 + edges * G * 4
+    k2_bytes = edges * G * (D * 2 + 4) + q.numel() * 2 + nslot.numel() * 4
+    ms = ms_k1 + ms_k2
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), sink + local + Zipf(1.1) selections)",
+        "config": {"workload": "msa_kv_outer", "N": N, "Hq": Hq, "Hkv": Hkv, "D": D, "BK": BK, "k": ks,
+                   "edges": edges},
+        "ms": {"kvouter_k1": round(ms_k1, 4), "combine_k2": round(ms_k2, 4)},
+        "k1_tflops": round(flops / (ms_k1 * 1e-3) / 1e12, 2),
+        "k1_gbps_algorithmic": round(k1_bytes / (ms_k1 * 1e-3) / 1e9, 1),
+        "k2_gbps_algorithmic": round(k2_bytes / (ms_k2 * 1e-3) / 1e9, 1),
+        "pct_hbm_k2": round(100 * k2_bytes / (ms_k2 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "roofline": {"kernel": "kv_k1_kernel (bsa_forward_kvouter)", "bound": "hbm",
+                     "achieved": round(k1_bytes / (ms_k1 * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(k1_bytes / (ms_k1 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+
+
 def cpu_baseline_video(ctx, budget_s):
     """Oracle on a bounded sample: pool + route + TopK of one head, and exact
     attention of as many of that head's query blocks as fit the budget."""
@@ -185,17 +285,34 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video"])
+    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for hardware byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention shards by heads with no exchange, "
               "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
         return 2
-    res, ctx = bench_video(args)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_video(ctx, args.cpu_seconds)
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel(), "copy_bytes_written": dst.numel(), "launches": 3}))
+        return 0
+    if args.workload == "nsa":
+        res = bench_nsa(args)
+    elif args.workload == "msa":
+        res = bench_msa(args)
+    else:
+        res, ctx = bench_video(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_video(ctx, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

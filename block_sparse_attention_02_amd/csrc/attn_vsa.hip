@@ -26,7 +26,10 @@
 
 namespace bsa {
 
-#define BSA_BARRIER() asm volatile("s_barrier" ::: "memory")
+// Workgroup barrier that first retires this wave's outstanding LDS reads, so a
+// buffer can be refilled right after it.  Asynchronous global->LDS copies are
+// ordered separately with wait_vmcnt<>().
+#define BSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 // Physical 16-byte chunk of logical chunk c in tile row r.
 template <int CPR>
@@ -36,8 +39,8 @@ __device__ __forceinline__ int k_swz(int r, int c) {
 template <int CPR>
 __device__ __forceinline__ int v_swz(int r, int c) {
   if constexpr (CPR >= 16) {
-    constexpr int f[4] = {0, 6, 10, 12};
-    return c ^ f[r & 3];
+    // XOR pattern {0, 6, 10, 12} for r % 4 = 0..3, packed in nibbles
+    return c ^ ((0xCA60 >> (4 * (r & 3))) & 15);
   } else {
     return c ^ (2 * (r & 3));
   }
@@ -55,7 +58,7 @@ struct TileMap {
 };
 
 // Copy one K or V tile (rows given by tok[]) into LDS with asynchronous
-// 16-byte global->LDS copies.
+// 16-byte global->LDS copies (LPT per lane, counted by wait_vmcnt).
 template <int D, int MT, bool IS_V>
 __device__ __forceinline__ void stage_tile(__bf16* lds, const __bf16* __restrict__ base, int64_t sN,
                                            const int* tok, int w, int lane) {
@@ -65,23 +68,36 @@ __device__ __forceinline__ void stage_tile(__bf16* lds, const __bf16* __restrict
     const int r = TM::row(k, w, lane);
     const int pc = TM::pchunk(k, w, lane);
     const int lc = IS_V ? v_swz<TM::CPR>(r, pc) : k_swz<TM::CPR>(r, pc);
-    global_to_lds16(base + (int64_t)tok[k] * sN + lc * 8, lds + (size_t)(k * TM::NW + w) * 64 * 8);
+    global_to_lds16_async(base + (int64_t)tok[k] * sN + lc * 8, lds_offset(lds + (size_t)(k * TM::NW + w) * 64 * 8));
   }
 }
 
+// Token ids of the tile rows this lane copies.  Copy k of wave w covers the
+// RPI = 64/CPR consecutive rows starting at (k*NW + w)*RPI; their ids are read
+// with uniform (scalar) loads and each lane picks its own row, so these reads
+// do not count against the vector-memory counter the copies are tracked with.
 template <int D, int MT>
 __device__ __forceinline__ void tile_tokens(int* tok, const int32_t* __restrict__ perm, int j, int M,
                                             int nj, int w, int lane) {
   using TM = TileMap<D, MT>;
+  constexpr int RPI = 64 / TM::CPR;
+  const int sub = lane / TM::CPR;
+  const auto row0 = as_const(perm) + (int64_t)j * M;
 #pragma unroll
   for (int k = 0; k < TM::LPT; ++k) {
-    const int r = TM::row(k, w, lane);
-    tok[k] = perm[(int64_t)j * M + min(r, nj - 1)];
+    const int r0 = (k * TM::NW + w) * RPI;
+    int t = row0[min(r0, nj - 1)];
+#pragma unroll
+    for (int q = 1; q < RPI; ++q) {
+      const int tq = row0[min(r0 + q, nj - 1)];
+      t = (sub == q) ? tq : t;
+    }
+    tok[k] = t;
   }
 }
 
 template <int D, int MT>
-__global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
+__global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_attn_kernel(VsaAttnParams p) {
   using Tin = __bf16;
   using TM = TileMap<D, MT>;
   constexpr int NW = TM::NW;
@@ -95,7 +111,8 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
   __shared__ __align__(1024) __bf16 Ks[MT * D];
   __shared__ __align__(1024) __bf16 Vs[MT * D];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5;  // which half of the wave
   const int64_t wid = blockIdx.x;
   const int i = (int)(wid % p.J);
@@ -106,9 +123,10 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
   const Tin* __restrict__ qg = reinterpret_cast<const Tin*>(p.q) + b * p.q_sB + hh * p.q_sH;
   const Tin* __restrict__ kg = reinterpret_cast<const Tin*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
   const Tin* __restrict__ vg = reinterpret_cast<const Tin*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
-  const int32_t* __restrict__ sel = p.q2k_idx + (bh * p.J + i) * p.kmax;
-  const int num = min(p.q2k_num[bh * p.J + i], p.kmax);
-  const int ni = p.block_len[i];
+  const auto sel = as_const(p.q2k_idx) + (bh * p.J + i) * p.kmax;
+  const auto blen = as_const(p.block_len);
+  const int num = min(as_const(p.q2k_num)[bh * p.J + i], p.kmax);
+  const int ni = blen[i];
 
   // ---- query rows: B operand of S^T, lane l holds row 32w + l%32 ----
   const int qrow = 32 * w + (lane & 31);
@@ -116,6 +134,10 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
   bf16x8 qop[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<Tin>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
+  // Consume the query registers here so the compiler waits for their loads
+  // before the loop; from here on only the tile copies count against vmcnt.
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qop[s]));
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
   bool has_next = false;
   if (pc < num) {
     j = sel[pc];
-    nj = p.block_len[j];
+    nj = blen[j];
     tile_tokens<D, MT>(tok, p.perm, j, M, nj, w, lane);
     stage_tile<D, MT, false>(Ks, kg, p.kv_sN, tok, w, lane);
     pn = pc + 1;
@@ -139,28 +161,27 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
     has_next = pn < num;
     if (has_next) {
       jn = sel[pn];
-      njn = p.block_len[jn];
+      njn = blen[jn];
       tile_tokens<D, MT>(tokn, p.perm, jn, M, njn, w, lane);
     }
     stage_tile<D, MT, true>(Vs, vg, p.kv_sN, tok, w, lane);
   }
 
   while (pc < num) {
-    // ---- K(j) resident (V(j) and the next block's row tokens may be in flight)
-    if (has_next)
-      wait_vmcnt<2 * LPT>();
-    else
-      wait_vmcnt<LPT>();
+    // ---- K(j) resident; only V(j) may still be in flight ----
+    wait_vmcnt<LPT>();
     BSA_BARRIER();
 
     f32x16 sacc[KT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-      const int krow = 32 * kt + (lane & 31);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int krow = 32 * kt + (lane & 31);
         const int pch = k_swz<TM::CPR>(krow, 2 * s + h2);
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + pch * 8);
         sacc[kt] = mfma32(a, qop[s], sacc[kt]);
@@ -238,7 +259,7 @@ __global__ __launch_bounds__(2 * MT) void vsa_attn_kernel(VsaAttnParams p) {
     has_next = pn < num;
     if (has_next) {
       jn = sel[pn];
-      njn = p.block_len[jn];
+      njn = blen[jn];
       tile_tokens<D, MT>(tokn, p.perm, jn, M, njn, w, lane);
     }
     stage_tile<D, MT, true>(Vs, vg, p.kv_sN, tok, w, lane);

@@ -199,8 +199,8 @@ __device__ __forceinline__ int k1_k_swz(int r, int c) { return c ^ (r & 7); }
 template <int CPR>
 __device__ __forceinline__ int k1_v_swz(int r, int c) {
   if constexpr (CPR >= 16) {
-    constexpr int f[4] = {0, 6, 10, 12};
-    return c ^ f[r & 3];
+    // XOR pattern {0, 6, 10, 12} for r % 4 = 0..3, packed in nibbles
+    return c ^ ((0xCA60 >> (4 * (r & 3))) & 15);
   } else {
     return c ^ (2 * (r & 3));
   }

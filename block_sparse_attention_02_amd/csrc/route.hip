@@ -88,15 +88,15 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
       }
 #pragma unroll
       for (int rr = 0; rr < UT; ++rr) {
-        if (r + rr >= n) break;
+        const float wgt = (r + rr < n) ? 1.f : 0.f;  // no branch: keeps the loads batched
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
           if constexpr (VW == 1) {
-            acc[u][0] += (float)v[rr][u];
+            acc[u][0] += wgt * (float)v[rr][u];
           } else {
             const T* e8 = reinterpret_cast<const T*>(&v[rr][u]);
 #pragma unroll
-            for (int e = 0; e < VW; ++e) acc[u][e] += (float)e8[e];
+            for (int e = 0; e < VW; ++e) acc[u][e] += wgt * (float)e8[e];
           }
         }
       }

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64) void nsa_attn_kernel(NsaAttnParams p) {
   f32x4 oacc[SH::DT];
 #pragma unroll
   for (int dt = 0; dt < SH::DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, lx_run = 0.f;  // sums of rounded / exact weights
   const int64_t last = p.causal ? t : p.N - 1;  // last visible key position
 
   for (int pp = 0; pp < cnt; ++pp) {
@@ -128,18 +128,23 @@ __global__ __launch_bounds__(64) void nsa_attn_kernel(NsaAttnParams p) {
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+      // weights rounded to bf16 once; the row sum uses the rounded values.
+      // k-step u = kt/2 holds keys 32u + 4g + i (e = i) and 32u + 16 + 4g + i (e = 4 + i)
+      float rs = 0.f, rsx = 0.f;
       bf16x8 pop[SH::US];
 #pragma unroll
-      for (int kt = 0; kt < SH::KT; ++kt)
+      for (int u = 0; u < SH::US; ++u) {
+        u32x4 pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(sacc[kt][i] - m_use);
-          rs += pr;
-          // k-step u = kt/2 holds keys 32u + 4g + i (e = i) and 32u + 16 + 4g + i (e = 4 + i)
-          pop[kt >> 1][4 * (kt & 1) + i] = (__bf16)pr;
+        for (int e = 0; e < 4; ++e) {
+          const int kt = 2 * u + (e >> 1), i = 2 * (e & 1);
+          pk[e] = pack2_bf16_sum<true>(fast_exp2(sacc[kt][i] - m_use), fast_exp2(sacc[kt][i + 1] - m_use), &rs,
+                                       &rsx);
         }
+        pop[u] = __builtin_bit_cast(bf16x8, pk);
+      }
       l_run = l_run * alpha + rs;
+      lx_run = lx_run * alpha + rsx;
       m_run = m_new;
 #pragma unroll
       for (int dt = 0; dt < SH::DT; ++dt)
@@ -179,8 +184,11 @@ __global__ __launch_bounds__(64) void nsa_attn_kernel(NsaAttnParams p) {
                    (__bf16)(oacc[dt][3] * inv)};
       *reinterpret_cast<bf16x4*>(og + d) = v4;
     }
-    if (p.lse && g == 0)
-      p.lse[((int64_t)b * p.Hq + hq) * p.N + t] = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (p.lse) {
+      float lx = lx_run + __shfl_xor(lx_run, 16, 64);
+      lx += __shfl_xor(lx, 32, 64);
+      if (g == 0) p.lse[((int64_t)b * p.Hq + hq) * p.N + t] = (lx > 0.f) ? (m_run + __log2f(lx)) * kLn2 : -INFINITY;
+    }
   }
 }
 

@@ -29,13 +29,19 @@ namespace bsa {
 // Workgroup barrier that first retires this wave's outstanding LDS reads, so a
 // buffer can be refilled right after it.  Asynchronous global->LDS copies are
 // ordered separately with wait_vmcnt<>().
+// Workgroup barrier that first retires this wave's outstanding LDS reads, so a
+// buffer can be refilled right after it.  Asynchronous global->LDS copies are
+// ordered separately with wait_vmcnt<>().
 #define BSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// Physical 16-byte chunk of logical chunk c in tile row r.
+// Physical 16-byte chunk of logical chunk c in K tile row r: 16 consecutive
+// rows read at the same logical chunk land on 16 distinct bank groups.
 template <int CPR>
 __device__ __forceinline__ int k_swz(int r, int c) {
-  return c ^ (r & (CPR >= 8 ? 7 : CPR - 1));
+  return c ^ (r & (CPR >= 16 ? 15 : CPR - 1));
 }
+// V tile: the transposing read takes 4 consecutive rows x 32 bytes per 16-lane
+// group (two groups per 64-byte span); rows r%4 = 0..3 get disjoint chunks.
 template <int CPR>
 __device__ __forceinline__ int v_swz(int r, int c) {
   if constexpr (CPR >= 16) {
@@ -46,61 +52,91 @@ __device__ __forceinline__ int v_swz(int r, int c) {
   }
 }
 
-// Per-thread rows of a tile copy: instruction k of wave w covers the 64 chunks
-// [(k*NW + w)*64, +64) of the row-major tile, lane L chunk (k*NW + w)*64 + L.
+// Copy k of wave w covers the 64 chunks [(w*LPT + k)*64, +64) of the row-major
+// tile: lane L takes chunk (w*LPT + k)*64 + L, i.e. row (w*LPT + k)*RPI + L/CPR.
+// Wave w therefore copies the 32 consecutive rows [32w, 32w + 32).
 template <int D, int MT>
 struct TileMap {
   static constexpr int NW = MT / 32;
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int LPT = MT * CPR / (64 * NW);  // copies per thread per tile
-  __device__ static int row(int k, int w, int lane) { return ((k * NW + w) * 64 + lane) / CPR; }
-  __device__ static int pchunk(int k, int w, int lane) { return ((k * NW + w) * 64 + lane) % CPR; }
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per copy instruction
+  static constexpr int LPT = MT * CPR / (64 * NW);  // copies per lane per tile
+  static_assert(LPT * RPI == 32, "each wave copies 32 rows");
+  __device__ static int row(int k, int w, int lane) { return (w * LPT + k) * RPI + lane / CPR; }
+  __device__ static int pchunk(int lane) { return lane % CPR; }
 };
 
-// Copy one K or V tile (rows given by tok[]) into LDS with asynchronous
-// 16-byte global->LDS copies (LPT per lane, counted by wait_vmcnt).
-template <int D, int MT, bool IS_V>
-__device__ __forceinline__ void stage_tile(__bf16* lds, const __bf16* __restrict__ base, int64_t sN,
-                                           const int* tok, int w, int lane) {
-  using TM = TileMap<D, MT>;
-#pragma unroll
-  for (int k = 0; k < TM::LPT; ++k) {
-    const int r = TM::row(k, w, lane);
-    const int pc = TM::pchunk(k, w, lane);
-    const int lc = IS_V ? v_swz<TM::CPR>(r, pc) : k_swz<TM::CPR>(r, pc);
-    global_to_lds16_async(base + (int64_t)tok[k] * sN + lc * 8, lds_offset(lds + (size_t)(k * TM::NW + w) * 64 * 8));
-  }
+// Buffer resource of one (batch, head) slice: 32-bit byte offsets from `base`;
+// offsets at or beyond `bytes` read as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);  // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;                // raw 32-bit buffer
+  return r;
 }
 
-// Token ids of the tile rows this lane copies.  Copy k of wave w covers the
-// RPI = 64/CPR consecutive rows starting at (k*NW + w)*RPI; their ids are read
-// with uniform (scalar) loads and each lane picks its own row, so these reads
-// do not count against the vector-memory counter the copies are tracked with.
+// Asynchronous 16-byte buffer -> LDS copy (lane L lands in slot L of the
+// wave's 1 KiB LDS window at `lds_byte_offset`); counted by wait_vmcnt<>().
+__device__ __forceinline__ void buffer_to_lds16(i32x4 rsrc, uint32_t voffset, uint32_t lds_byte_offset) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "{m0}"(lds_byte_offset)
+      : "memory");
+}
+
+// Byte offsets (within the slice) of the tile rows this lane copies.  The 32
+// row ids of the wave are read with uniform (scalar) loads from the constant
+// address space and each lane picks its own row; padding rows (perm = -1) and
+// rows beyond the block capacity repeat the block's first token (their keys
+// are masked later).
 template <int D, int MT>
-__device__ __forceinline__ void tile_tokens(int* tok, const int32_t* __restrict__ perm, int j, int M,
-                                            int nj, int w, int lane) {
+__device__ __forceinline__ void tile_rows(uint32_t* rowoff, const int32_t* __restrict__ perm, int j, int M,
+                                          int w, int lane, uint32_t row_bytes) {
   using TM = TileMap<D, MT>;
-  constexpr int RPI = 64 / TM::CPR;
-  const int sub = lane / TM::CPR;
   const auto row0 = as_const(perm) + (int64_t)j * M;
+  const int first = row0[0];
+  const int sub = lane / TM::CPR;
+  // Capacities are 16, 32 or 64 with MT = max(32, M): only M = 16 leaves rows
+  // 16..31 of the (single) wave outside the block's table.
+  int ids[32];
+  const auto rw = row0 + 32 * w;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) ids[q] = rw[q];
+  if (M >= 32) {
+#pragma unroll
+    for (int q = 16; q < 32; ++q) ids[q] = rw[q];
+  } else {
+#pragma unroll
+    for (int q = 16; q < 32; ++q) ids[q] = -1;
+  }
 #pragma unroll
   for (int k = 0; k < TM::LPT; ++k) {
-    const int r0 = (k * TM::NW + w) * RPI;
-    int t = row0[min(r0, nj - 1)];
+    int t = ids[k * TM::RPI];
 #pragma unroll
-    for (int q = 1; q < RPI; ++q) {
-      const int tq = row0[min(r0 + q, nj - 1)];
-      t = (sub == q) ? tq : t;
-    }
-    tok[k] = t;
+    for (int q = 1; q < TM::RPI; ++q) t = (sub == q) ? ids[k * TM::RPI + q] : t;
+    t = (t < 0) ? first : t;
+    rowoff[k] = (uint32_t)t * row_bytes;
   }
 }
 
 template <int D, int MT>
-__global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_attn_kernel(VsaAttnParams p) {
-  using Tin = __bf16;
+__device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t lds_base, const uint32_t* rowoff,
+                                           const uint32_t* chunkoff, int w) {
   using TM = TileMap<D, MT>;
-  constexpr int NW = TM::NW;
+#pragma unroll
+  for (int k = 0; k < TM::LPT; ++k)
+    buffer_to_lds16(rsrc, rowoff[k] + chunkoff[k], lds_base + (uint32_t)((w * TM::LPT + k) * 1024));
+}
+
+// LSE: also keep the exact (unrounded) row sum for the log-sum-exp output.
+template <int D, int MT, bool LSE>
+__global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_attn_kernel(VsaAttnParams p) {
+  using TM = TileMap<D, MT>;
   constexpr int LPT = TM::LPT;
   constexpr int KT = MT / 32;   // 32-key tiles per KV tile
   constexpr int KS = D / 16;    // k-steps of QK^T
@@ -120,20 +156,34 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int M = p.M;
 
-  const Tin* __restrict__ qg = reinterpret_cast<const Tin*>(p.q) + b * p.q_sB + hh * p.q_sH;
-  const Tin* __restrict__ kg = reinterpret_cast<const Tin*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
-  const Tin* __restrict__ vg = reinterpret_cast<const Tin*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
+  const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
+  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
+  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
+  const uint32_t row_bytes = (uint32_t)(p.kv_sN * 2);
+  const uint32_t slice_bytes = (uint32_t)((p.N - 1) * p.kv_sN * 2 + D * 2);
+  const i32x4 krs = make_rsrc(kg, slice_bytes), vrs = make_rsrc(vg, slice_bytes);
+  const uint32_t ks_lds = lds_offset(Ks), vs_lds = lds_offset(Vs);
+
   const auto sel = as_const(p.q2k_idx) + (bh * p.J + i) * p.kmax;
   const auto blen = as_const(p.block_len);
   const int num = min(as_const(p.q2k_num)[bh * p.J + i], p.kmax);
   const int ni = blen[i];
+
+  // per-lane swizzled chunk offsets of the copies (fixed for the whole kernel)
+  uint32_t koff[LPT], voff[LPT];
+#pragma unroll
+  for (int k = 0; k < LPT; ++k) {
+    const int r = TM::row(k, w, lane), pc = TM::pchunk(lane);
+    koff[k] = (uint32_t)k_swz<TM::CPR>(r, pc) * 16;
+    voff[k] = (uint32_t)v_swz<TM::CPR>(r, pc) * 16;
+  }
 
   // ---- query rows: B operand of S^T, lane l holds row 32w + l%32 ----
   const int qrow = 32 * w + (lane & 31);
   const int qtok = p.perm[(int64_t)i * M + min(qrow, ni - 1)];
   bf16x8 qop[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<Tin>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
+  for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
   // Consume the query registers here so the compiler waits for their loads
   // before the loop; from here on only the tile copies count against vmcnt.
 #pragma unroll
@@ -144,31 +194,29 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max in log2 units; lane-partial sums of the rounded (and exact) weights
+  float m_run = -INFINITY, l_run = 0.f, lx_run = 0.f;
 
-  int pc = 0;
-  while (pc < num && sel[pc] < 0) ++pc;
-  int tok[LPT], tokn[LPT];
-  int j = 0, nj = 0, pn = num, jn = 0, njn = 0;
-  bool has_next = false;
-  if (pc < num) {
-    j = sel[pc];
-    nj = blen[j];
-    tile_tokens<D, MT>(tok, p.perm, j, M, nj, w, lane);
-    stage_tile<D, MT, false>(Ks, kg, p.kv_sN, tok, w, lane);
-    pn = pc + 1;
-    while (pn < num && sel[pn] < 0) ++pn;
-    has_next = pn < num;
-    if (has_next) {
-      jn = sel[pn];
-      njn = blen[jn];
-      tile_tokens<D, MT>(tokn, p.perm, jn, M, njn, w, lane);
+  // Kept blocks are visited in table order; an entry < 0 is an empty tile
+  // (copies of block 0, every key masked), which leaves the result unchanged.
+  uint32_t rows[LPT], rowsn[LPT];
+  int nj = 0, njn = 0;
+  if (num > 0) {
+    const int j = sel[0];
+    nj = (j >= 0) ? blen[j] : 0;
+    tile_rows<D, MT>(rows, p.perm, max(j, 0), M, w, lane, row_bytes);
+    stage_tile<D, MT>(krs, ks_lds, rows, koff, w);
+    stage_tile<D, MT>(vrs, vs_lds, rows, voff, w);
+    if (num > 1) {
+      const int jn = sel[1];
+      njn = (jn >= 0) ? blen[jn] : 0;
+      tile_rows<D, MT>(rowsn, p.perm, max(jn, 0), M, w, lane, row_bytes);
     }
-    stage_tile<D, MT, true>(Vs, vg, p.kv_sN, tok, w, lane);
   }
 
-  while (pc < num) {
-    // ---- K(j) resident; only V(j) may still be in flight ----
+  for (int pc = 0; pc < num; ++pc) {
+    const bool has_next = pc + 1 < num;
+    // ---- K(j) resident; V(j) may still be in flight ----
     wait_vmcnt<LPT>();
     BSA_BARRIER();
 
@@ -188,39 +236,59 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
     }
     BSA_BARRIER();  // every wave is done reading Ks
-    if (has_next) stage_tile<D, MT, false>(Ks, kg, p.kv_sN, tokn, w, lane);
+    if (has_next) stage_tile<D, MT>(krs, ks_lds, rowsn, koff, w);
 
     // ---- online softmax (log2 domain); lane owns query 32w + l%32 ----
+    if (nj < MT) {  // edge / short block: mask keys at or beyond its true length
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          sacc[kt][r] = (key < nj) ? sacc[kt][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float x = (key < nj) ? sacc[kt][r] * p.scale_log2 : -INFINITY;
-        sacc[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+    // Lazy rescale: keep the old reference unless some row's maximum grew by
+    // more than 8 (probabilities then stay below 2^8); the final O = U / l uses
+    // the same reference, so the result is unchanged.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first kept block
+      l_run *= alpha;
+      if constexpr (LSE) lx_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // Weights are rounded to bf16 once; the row sum uses the rounded values the
+    // PV product uses, so O = U / l is an exact convex combination of V rows.
+    float rs = 0.f, rsx = 0.f;
     bf16x8 pop[US];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(sacc[kt][r] - m_use);
-        rs += pr;
-        pop[2 * kt + (r >> 3)][r & 7] = (__bf16)pr;
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * hlf + 2 * e;
+          const float a = fast_exp2(__builtin_fmaf(sacc[kt][r], p.scale_log2, -m_use));
+          const float c = fast_exp2(__builtin_fmaf(sacc[kt][r + 1], p.scale_log2, -m_use));
+          pk[e] = pack2_bf16_sum<LSE>(a, c, &rs, &rsx);
+        }
+        pop[2 * kt + hlf] = __builtin_bit_cast(bf16x8, pk);
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    l_run += rs;
+    if constexpr (LSE) lx_run += rsx;
 
     // ---- V(j) resident (K of the next block may be in flight) ----
     if (has_next)
@@ -248,21 +316,16 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     BSA_BARRIER();  // every wave is done reading Vs
 
     if (!has_next) break;
-    // ---- advance: tokens of the block after next, then V of the next block ----
-    pc = pn;
-    j = jn;
+    // ---- advance: V of the next block, then the rows of the block after ----
     nj = njn;
 #pragma unroll
-    for (int k = 0; k < LPT; ++k) tok[k] = tokn[k];
-    pn = pc + 1;
-    while (pn < num && sel[pn] < 0) ++pn;
-    has_next = pn < num;
-    if (has_next) {
-      jn = sel[pn];
-      njn = blen[jn];
-      tile_tokens<D, MT>(tokn, p.perm, jn, M, njn, w, lane);
+    for (int k = 0; k < LPT; ++k) rows[k] = rowsn[k];
+    stage_tile<D, MT>(vrs, vs_lds, rows, voff, w);
+    if (pc + 2 < num) {
+      const int jn = sel[pc + 2];
+      njn = (jn >= 0) ? blen[jn] : 0;
+      tile_rows<D, MT>(rowsn, p.perm, max(jn, 0), M, w, lane, row_bytes);
     }
-    stage_tile<D, MT, true>(Vs, vg, p.kv_sN, tok, w, lane);
   }
 
   // ---- epilogue: O = U / l, written at the tokens' original positions ----
@@ -279,8 +342,9 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                      (__bf16)(oacc[dt][4 * jj + 2] * inv), (__bf16)(oacc[dt][4 * jj + 3] * inv)};
         *reinterpret_cast<bf16x4*>(og + d) = v4;
       }
-    if (p.lse && h2 == 0) {
-      p.lse[bh * p.N + qtok] = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if constexpr (LSE) {
+      const float lx = lx_run + xor32(lx_run);
+      if (h2 == 0) p.lse[bh * p.N + qtok] = (lx > 0.f) ? (m_run + __log2f(lx)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -350,15 +414,20 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   }
 }
 
+template <int D, int MT>
+static hipError_t launch_vsa_mt(const VsaAttnParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.B * p.H * p.J;
+  if (p.lse)
+    vsa_attn_kernel<D, MT, true><<<dim3((unsigned)items), dim3(2 * MT), 0, s>>>(p);
+  else
+    vsa_attn_kernel<D, MT, false><<<dim3((unsigned)items), dim3(2 * MT), 0, s>>>(p);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_vsa_d(const VsaAttnParams& p, hipStream_t s) {
-  const int64_t items = (int64_t)p.B * p.H * p.J;
-  if (p.M <= 32) {
-    vsa_attn_kernel<D, 32><<<dim3((unsigned)items), dim3(64), 0, s>>>(p);
-  } else {
-    vsa_attn_kernel<D, 64><<<dim3((unsigned)items), dim3(128), 0, s>>>(p);
-  }
-  return hipGetLastError();
+  if (p.M <= 32) return launch_vsa_mt<D, 32>(p, s);
+  return launch_vsa_mt<D, 64>(p, s);
 }
 
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s) {

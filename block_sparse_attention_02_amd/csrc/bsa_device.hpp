@@ -13,6 +13,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define BSA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -92,6 +93,20 @@ __device__ __forceinline__ float xor32(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (one packed conversion, nearest even) and return
+// the packed pair; *sum gains the two rounded values and, when EXACT, *exact
+// gains the two unrounded ones.
+template <bool EXACT = false>
+__device__ __forceinline__ uint32_t pack2_bf16_sum(float a, float b, float* sum, float* exact = nullptr) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  *sum += __builtin_bit_cast(float, u << 16) + __builtin_bit_cast(float, u & 0xffff0000u);
+  if constexpr (EXACT) *exact += a + b;
+  return u;
+}
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 r;

@@ -281,17 +281,24 @@ __global__ __launch_bounds__(256) void kv_k1_kernel(KvOuterParams p, int NB, con
       }
     mx = fmaxf(mx, xor32(mx));
     const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    float rs = 0.f;
+    // weights rounded to bf16 once; the row sum uses the rounded values
+    float rs = 0.f, rsx = 0.f;
     bf16x8 pop[SH::US];
 #pragma unroll
     for (int kt = 0; kt < SH::KT; ++kt)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float pr = fast_exp2(sacc[kt][x] - m_use);
-        rs += pr;
-        pop[2 * kt + (x >> 3)][x & 7] = (__bf16)pr;
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 8 * hlf + 2 * e;
+          pk[e] = pack2_bf16_sum<true>(fast_exp2(sacc[kt][x] - m_use), fast_exp2(sacc[kt][x + 1] - m_use), &rs,
+                                       &rsx);
+        }
+        pop[2 * kt + hlf] = __builtin_bit_cast(bf16x8, pk);
       }
-    const float l_tot = rs + xor32(rs);
+    const float l_tot = rs + xor32(rs);     // normalises O_s (rounded weights)
+    const float l_exact = rsx + xor32(rsx);  // gives L_s
     // ---- O^T = V^T P^T ----
     f32x16 oacc[SH::DT];
 #pragma unroll
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(256) void kv_k1_kernel(KvOuterParams p, int NB, con
                        (__bf16)(oacc[dt][4 * jj + 2] * inv), (__bf16)(oacc[dt][4 * jj + 3] * inv)};
           *reinterpret_cast<bf16x4*>(orow + d) = v4;
         }
-      if (h2 == 0) p.lse_buf[obase] = (l_tot > 0.f) ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (h2 == 0) p.lse_buf[obase] = (l_exact > 0.f) ? (m_use + __log2f(l_exact)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -133,7 +133,7 @@ def bench_video(args):
         "pct_bf16_peak_attn": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "route_gbps": round(route_bytes / (ms["route"] * 1e-3) / 1e9, 1),
         "pct_hbm_route": round(100 * route_bytes / (ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-        "roofline": {"kernel": "vsa_attn_kernel (bsa_forward_qouter, block mode)", "bound": "mfma",
+        "roofline": {"kernel": "vsa4_kernel (bsa_forward_qouter, block mode)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }

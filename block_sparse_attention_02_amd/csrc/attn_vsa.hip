@@ -21,10 +21,17 @@
 // are XOR-swizzled per row so both reads are bank-conflict free.  The copy of
 // K for the next kept block overlaps the softmax and PV of the current one,
 // the copy of V overlaps the next QK^T.
+#include <algorithm>
+
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
 namespace bsa {
+
+constexpr int kMaxRounds = 4096;
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // Workgroup barrier that first retires this wave's outstanding LDS reads, so a
 // buffer can be refilled right after it.  Asynchronous global->LDS copies are
@@ -89,39 +96,41 @@ __device__ __forceinline__ void buffer_to_lds16(i32x4 rsrc, uint32_t voffset, ui
       : "memory");
 }
 
-// Byte offsets (within the slice) of the tile rows this lane copies.  The 32
-// row ids of the wave are read with uniform (scalar) loads from the constant
-// address space and each lane picks its own row; padding rows (perm = -1) and
-// rows beyond the block capacity repeat the block's first token (their keys
-// are masked later).
+// Asynchronous copy of one block's token ids into the wave's 256-byte LDS id
+// buffer: lane L copies the id of row L.  Rows at or beyond the block capacity
+// read the next block's ids, and reads past the table return zero; both only
+// name keys that are masked.  Counted by wait_vmcnt<>() like the tile copies.
+__device__ __forceinline__ void stage_ids(i32x4 prs, int j, int M, uint32_t ids_lds, int lane) {
+  const uint32_t voff = (uint32_t)(j * M + lane) * 4u;
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(prs), "{m0}"(ids_lds)
+      : "memory");
+}
+
+// Byte offsets (within the slice) of the LPT tile rows this lane copies.  Copy
+// k of wave w fills LDS row 32w + RPI*k + sub (sub = lane / CPR) with key
+// 32w + LPT*sub + k of the block, so a lane's keys are LPT consecutive entries
+// of the id buffer.  Padding ids (-1) read token 0; their keys are masked.
 template <int D, int MT>
-__device__ __forceinline__ void tile_rows(uint32_t* rowoff, const int32_t* __restrict__ perm, int j, int M,
-                                          int w, int lane, uint32_t row_bytes) {
+__device__ __forceinline__ void tile_rows(uint32_t* rowoff, const int* ids, int w, int lane, uint32_t row_bytes) {
   using TM = TileMap<D, MT>;
-  const auto row0 = as_const(perm) + (int64_t)j * M;
-  const int first = row0[0];
-  const int sub = lane / TM::CPR;
-  // Capacities are 16, 32 or 64 with MT = max(32, M): only M = 16 leaves rows
-  // 16..31 of the (single) wave outside the block's table.
-  int ids[32];
-  const auto rw = row0 + 32 * w;
+  const int* src = ids + 32 * w + TM::LPT * (lane / TM::CPR);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) ids[q] = rw[q];
-  if (M >= 32) {
+  for (int q = 0; q < TM::LPT / 4; ++q) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(src + 4 * q);
 #pragma unroll
-    for (int q = 16; q < 32; ++q) ids[q] = rw[q];
-  } else {
-#pragma unroll
-    for (int q = 16; q < 32; ++q) ids[q] = -1;
+    for (int e = 0; e < 4; ++e) rowoff[4 * q + e] = (uint32_t)max(v[e], 0) * row_bytes;
   }
-#pragma unroll
-  for (int k = 0; k < TM::LPT; ++k) {
-    int t = ids[k * TM::RPI];
-#pragma unroll
-    for (int q = 1; q < TM::RPI; ++q) t = (sub == q) ? ids[k * TM::RPI + q] : t;
-    t = (t < 0) ? first : t;
-    rowoff[k] = (uint32_t)t * row_bytes;
-  }
+}
+
+// Key (position in the block) held by LDS row 32*kt + rr of a tile.
+template <int D, int MT>
+__device__ __forceinline__ constexpr int tile_key(int kt, int rr) {
+  using TM = TileMap<D, MT>;
+  return 32 * kt + TM::LPT * (rr % TM::RPI) + rr / TM::RPI;
 }
 
 template <int D, int MT>
@@ -133,24 +142,23 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t lds_base, const 
     buffer_to_lds16(rsrc, rowoff[k] + chunkoff[k], lds_base + (uint32_t)((w * TM::LPT + k) * 1024));
 }
 
-// LSE: also keep the exact (unrounded) row sum for the log-sum-exp output.
+// One query block (work item `wid` = (b*H + h)*J + i).  LSE: also keep the
+// exact (unrounded) row sum for the log-sum-exp output.
 template <int D, int MT, bool LSE>
-__global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_attn_kernel(VsaAttnParams p) {
+__device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in, __bf16* Ks, __bf16* Vs, int* Ids) {
+  const int64_t wid = __builtin_amdgcn_readfirstlane(wid_in);  // uniform by construction
   using TM = TileMap<D, MT>;
   constexpr int LPT = TM::LPT;
   constexpr int KT = MT / 32;   // 32-key tiles per KV tile
   constexpr int KS = D / 16;    // k-steps of QK^T
   constexpr int DT = D / 32;    // 32-channel tiles of O
   constexpr int US = MT / 16;   // 16-key steps of PV
-  static_assert(LPT >= 1 && LPT <= 16, "tile copy shape");
-
-  __shared__ __align__(1024) __bf16 Ks[MT * D];
-  __shared__ __align__(1024) __bf16 Vs[MT * D];
+  static_assert(LPT >= 4 && LPT <= 16 && LPT % 4 == 0, "tile copy shape");
+  constexpr int PF = 2;         // operand prefetch distance (products)
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5;  // which half of the wave
-  const int64_t wid = blockIdx.x;
   const int i = (int)(wid % p.J);
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
@@ -199,25 +207,30 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   // Kept blocks are visited in table order; an entry < 0 is an empty tile
   // (copies of block 0, every key masked), which leaves the result unchanged.
-  uint32_t rows[LPT], rowsn[LPT];
-  int nj = 0, njn = 0;
+  // Copies in flight, oldest first, at the top of iteration pc:
+  //   K(pc) [LPT], ids(pc+1) [1], V(pc) [LPT]
+  // ids(pc+1) land before K(pc+1) is staged (after QK^T); V(pc) before PV.
+  const i32x4 prs = make_rsrc(p.perm, (uint32_t)p.J * (uint32_t)M * 4u);
+  int* ids = Ids + 64 * w;
+  const uint32_t ids_lds = lds_offset(ids);
+  uint32_t rows[LPT];
+  int nj = 0, njn = 0, jn1 = 0;
   if (num > 0) {
-    const int j = sel[0];
-    nj = (j >= 0) ? blen[j] : 0;
-    tile_rows<D, MT>(rows, p.perm, max(j, 0), M, w, lane, row_bytes);
+    const int j0 = sel[0];
+    nj = (j0 >= 0) ? blen[j0] : 0;
+    stage_ids(prs, max(j0, 0), M, ids_lds, lane);
+    wait_vmcnt<0>();
+    tile_rows<D, MT>(rows, ids, w, lane, row_bytes);
     stage_tile<D, MT>(krs, ks_lds, rows, koff, w);
+    jn1 = sel[min(1, num - 1)];
+    stage_ids(prs, max(jn1, 0), M, ids_lds, lane);
     stage_tile<D, MT>(vrs, vs_lds, rows, voff, w);
-    if (num > 1) {
-      const int jn = sel[1];
-      njn = (jn >= 0) ? blen[jn] : 0;
-      tile_rows<D, MT>(rowsn, p.perm, max(jn, 0), M, w, lane, row_bytes);
-    }
   }
 
   for (int pc = 0; pc < num; ++pc) {
     const bool has_next = pc + 1 < num;
-    // ---- K(j) resident; V(j) may still be in flight ----
-    wait_vmcnt<LPT>();
+    // ---- K(pc) resident; ids(pc+1) and V(pc) may still be in flight ----
+    wait_vmcnt<LPT + 1>();
     BSA_BARRIER();
 
     f32x16 sacc[KT];
@@ -225,18 +238,43 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+    {
+      // K operands are read PF k-steps ahead of the products that use them,
+      // so the LDS latency overlaps the matrix ops.
+      bf16x8 ka[KS][KT];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+      for (int s = 0; s < KS + PF; ++s) {
+        if (s < KS) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const int krow = 32 * kt + (lane & 31);
-        const int pch = k_swz<TM::CPR>(krow, 2 * s + h2);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * D + pch * 8);
-        sacc[kt] = mfma32(a, qop[s], sacc[kt]);
+          for (int kt = 0; kt < KT; ++kt) {
+            const int krow = 32 * kt + (lane & 31);
+            const int pch = k_swz<TM::CPR>(krow, 2 * s + h2);
+            ka[s][kt] = *reinterpret_cast<const bf16x8*>(Ks + krow * D + pch * 8);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KT, 0);
+        }
+        if (s >= PF) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) sacc[kt] = mfma32(ka[s - PF][kt], qop[s - PF], sacc[kt]);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, KT, 0);
+        }
       }
     }
     BSA_BARRIER();  // every wave is done reading Ks
-    if (has_next) stage_tile<D, MT>(krs, ks_lds, rowsn, koff, w);
+    if (has_next) {
+      wait_vmcnt<LPT>();  // ids(pc+1) resident
+      tile_rows<D, MT>(rows, ids, w, lane, row_bytes);
+      stage_tile<D, MT>(krs, ks_lds, rows, koff, w);
+    }
+
+    // Scalar table reads for the coming iterations are issued here, where no
+    // LDS result is awaited until the barrier after the softmax: the block
+    // after next (the last one again near the end, a harmless repeat) and the
+    // true length of the next block.
+    __builtin_amdgcn_sched_barrier(0);
+    const int jn2 = sel[min(pc + 2, num - 1)];
+    njn = (jn1 >= 0) ? blen[max(jn1, 0)] : 0;
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax (log2 domain); lane owns query 32w + l%32 ----
     if (nj < MT) {  // edge / short block: mask keys at or beyond its true length
@@ -244,7 +282,7 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const int key = tile_key<D, MT>(kt, 8 * (r >> 2) + 4 * h2 + (r & 3));
           sacc[kt][r] = (key < nj) ? sacc[kt][r] : -INFINITY;
         }
     }
@@ -297,35 +335,38 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       wait_vmcnt<0>();
     BSA_BARRIER();
     {
+      // V operands (two transposing reads each) run PF products ahead.
       const int g16 = lane >> 4, jl = lane & 15;
+      constexpr int NP = US * DT;
+      bf16x8 va[NP];
 #pragma unroll
-      for (int u = 0; u < US; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+      for (int x = 0; x < NP + PF; ++x) {
+        if (x < NP) {
+          const int u = x / DT, dt = x % DT;
           const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
           const int c = d >> 3, off = d & 7;
           const int r0 = 16 * u + 4 * h2 + (jl >> 2);
           const int r1 = r0 + 8;
           const bf16x4 lo = lds_read_tr16(Vs + r0 * D + v_swz<TM::CPR>(r0, c) * 8 + off);
           const bf16x4 hi = lds_read_tr16(Vs + r1 * D + v_swz<TM::CPR>(r1, c) * 8 + off);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = mfma32(a, pop[u], oacc[dt]);
+          va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        if (x >= PF) {
+          const int y = x - PF;
+          oacc[y % DT] = mfma32(va[y], pop[y / DT], oacc[y % DT]);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
       }
     }
     BSA_BARRIER();  // every wave is done reading Vs
 
     if (!has_next) break;
-    // ---- advance: V of the next block, then the rows of the block after ----
+    // ---- advance: ids of the block after next, then V of the next block ----
     nj = njn;
-#pragma unroll
-    for (int k = 0; k < LPT; ++k) rows[k] = rowsn[k];
+    stage_ids(prs, max(jn2, 0), M, ids_lds, lane);
     stage_tile<D, MT>(vrs, vs_lds, rows, voff, w);
-    if (pc + 2 < num) {
-      const int jn = sel[pc + 2];
-      njn = (jn >= 0) ? blen[jn] : 0;
-      tile_rows<D, MT>(rowsn, p.perm, max(jn, 0), M, w, lane, row_bytes);
-    }
+    jn1 = jn2;
   }
 
   // ---- epilogue: O = U / l, written at the tokens' original positions ----
@@ -346,6 +387,366 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const float lx = lx_run + xor32(lx_run);
       if (h2 == 0) p.lse[bh * p.N + qtok] = (lx > 0.f) ? (m_run + __log2f(lx)) * kLn2 : -INFINITY;
     }
+  }
+}
+
+// Persistent grid: workgroup g takes items g, g + G, g + 2G, ...  Every item
+// visits the same number of kept blocks, so the resident workgroups advance
+// through their sorted block lists roughly in step; at any moment they touch a
+// narrow window of each head's K/V, which stays in L2 (workgroups are spread
+// over the XCDs round-robin, so each XCD serves every 8th query block of the
+// same stretch and all eight share the same window in the last-level cache).
+// Round counters of the persistent grid (one per round of gridDim.x items,
+// cleared before each launch).
+static __device__ uint32_t g_round_ctr[kMaxRounds];
+
+__global__ void clear_rounds_kernel(int n) {
+  for (int r = threadIdx.x; r < n; r += blockDim.x) g_round_ctr[r] = 0u;
+}
+
+// Re-align the resident workgroups after each round: arrive, then wait
+// (bounded) until every workgroup of the grid has arrived.  The wait only
+// affects cache locality, never the result; it gives up after a fixed number
+// of polls.
+__device__ __forceinline__ void round_sync(int sync, int wid, int items, int round) {
+  if (sync && wid + (int)gridDim.x < items && round < kMaxRounds) {
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(&g_round_ctr[round], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int t = 0; t < 4096; ++t) {
+        if (__hip_atomic_load(&g_round_ctr[round], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gridDim.x) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int MT, bool LSE>
+__global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_attn_kernel(VsaAttnParams p,
+                                                                                                     int items,
+                                                                                                     int sync) {
+  __shared__ __align__(1024) __bf16 Ks[MT * D];
+  __shared__ __align__(1024) __bf16 Vs[MT * D];
+  __shared__ __align__(256) int Ids[(MT / 32) * 64];
+  int round = 0;
+  for (int wid = blockIdx.x; wid < items; wid += gridDim.x, ++round) {
+    vsa_attn_item<D, MT, LSE>(p, wid, Ks, Vs, Ids);
+    round_sync(sync, wid, items, round);
+  }
+}
+
+
+// ============================================================================
+// 64-row blocks: four waves per query block.  Wave w = 2*hq + g owns query
+// rows [32hq, 32hq + 32) and key half g (keys [32g, 32g + 32) of every kept
+// block) with its own online-softmax state; the two key halves are merged
+// through LDS once per query block.  K/V tiles are double-buffered: the copies
+// of block t+1 are issued right after the single barrier that opens block t,
+// so each tile has a whole block of compute to arrive.
+// ============================================================================
+template <int D>
+struct Tile4 {
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per copy instruction
+  static constexpr int LPT = 16 / RPI;  // copies per wave per tensor (16 rows)
+  static_assert(LPT >= 2 && LPT <= 4 && LPT * RPI == 16, "tile copy shape");
+  // LDS row that copy k of wave w fills for this lane
+  __device__ static int row(int k, int w, int lane) { return 16 * w + RPI * k + lane / CPR; }
+  // Block key held by LDS row rho: copy k of wave w, lane group sub holds key
+  // 16w + LPT*sub + k, so a lane's keys are consecutive entries of the ids.
+  __device__ static int key_of_row(int rho) {
+    const int r = rho & 15;
+    return (rho & ~15) + LPT * (r % RPI) + r / RPI;
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void tile_rows4(uint32_t* rowoff, const int* ids, int w, int lane, uint32_t row_bytes) {
+  using TM = Tile4<D>;
+  const int* src = ids + 16 * w + TM::LPT * (lane / TM::CPR);
+  if constexpr (TM::LPT == 4) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rowoff[e] = (uint32_t)max(v[e], 0) * row_bytes;
+  } else {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 v = *reinterpret_cast<const i32x2*>(src);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) rowoff[e] = (uint32_t)max(v[e], 0) * row_bytes;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage4(i32x4 rsrc, uint32_t lds_base, const uint32_t* rowoff, const uint32_t* chunkoff,
+                                       int w) {
+  using TM = Tile4<D>;
+#pragma unroll
+  for (int k = 0; k < TM::LPT; ++k)
+    buffer_to_lds16(rsrc, rowoff[k] + chunkoff[k], lds_base + (uint32_t)((w * TM::LPT + k) * 1024));
+}
+
+template <int D, bool LSE>
+__device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __bf16* KV, int* Ids, float* Mx) {
+  using TM = Tile4<D>;
+  constexpr int LPT = TM::LPT, CPR = TM::CPR;
+  constexpr int KS = D / 16;   // k-steps of QK^T
+  constexpr int DT = D / 32;   // 32-channel tiles of O
+  constexpr int TILE = 64 * D; // elements of one K or V tile
+  constexpr int PF = 2;        // operand prefetch distance (products)
+  const int64_t wid = __builtin_amdgcn_readfirstlane(wid_in);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hq = w >> 1, g = w & 1;  // query half, key half
+  const int h2 = lane >> 5;
+  const int i = (int)(wid % p.J);
+  const int64_t bh = wid / p.J;
+  const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
+  constexpr int M = 64;
+
+  const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
+  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
+  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
+  const uint32_t row_bytes = (uint32_t)(p.kv_sN * 2);
+  const uint32_t slice_bytes = (uint32_t)((p.N - 1) * p.kv_sN * 2 + D * 2);
+  const i32x4 krs = make_rsrc(kg, slice_bytes), vrs = make_rsrc(vg, slice_bytes);
+  const i32x4 prs = make_rsrc(p.perm, (uint32_t)p.J * (uint32_t)M * 4u);
+  const uint32_t kv_lds = lds_offset(KV);
+  // buffer x: K tile at kv_lds + x*4*TILE bytes, V tile TILE*2 bytes after it
+  auto kbuf = [&](int x) { return kv_lds + (uint32_t)(x * 4 * TILE); };
+  auto vbuf = [&](int x) { return kv_lds + (uint32_t)(x * 4 * TILE + 2 * TILE); };
+
+  const auto sel = as_const(p.q2k_idx) + (bh * p.J + i) * p.kmax;
+  const auto blen = as_const(p.block_len);
+  const int num = min(as_const(p.q2k_num)[bh * p.J + i], p.kmax);
+  const int ni = blen[i];
+
+  uint32_t koff[LPT], voff[LPT];
+#pragma unroll
+  for (int k = 0; k < LPT; ++k) {
+    const int r = TM::row(k, w, lane), pc = lane % CPR;
+    koff[k] = (uint32_t)k_swz<CPR>(r, pc) * 16;
+    voff[k] = (uint32_t)v_swz<CPR>(r, pc) * 16;
+  }
+
+  // ---- query rows: B operand of S^T, lane l holds row 32hq + l%32 ----
+  const int qrow = 32 * hq + (lane & 31);
+  const int qtok = p.perm[(int64_t)i * M + min(qrow, ni - 1)];
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qop[s]));
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, lx_run = 0.f;
+
+  // Copies in flight at the top of block t: K(t), V(t) [2*LPT] then ids(t+1) [1].
+  int* ids = Ids + 64 * w;
+  const uint32_t ids_lds = lds_offset(ids);
+  uint32_t rows[LPT];
+  int nj = 0, njn = 0, j1 = 0, j2 = 0;
+  if (num > 0) {
+    const int j0 = sel[0];
+    nj = (j0 >= 0) ? blen[j0] : 0;
+    stage_ids(prs, max(j0, 0), M, ids_lds, lane);
+    wait_vmcnt<0>();
+    tile_rows4<D>(rows, ids, w, lane, row_bytes);
+    stage4<D>(krs, kbuf(0), rows, koff, w);
+    stage4<D>(vrs, vbuf(0), rows, voff, w);
+    j1 = sel[min(1, num - 1)];
+    j2 = sel[min(2, num - 1)];
+    stage_ids(prs, max(j1, 0), M, ids_lds, lane);
+  }
+
+  constexpr int NCOPY = 2 * LPT + 1;  // K and V copies of the next block, then ids
+  static_assert(NCOPY <= KS + PF, "copies are spread over the QK^T steps");
+  for (int t = 0; t < num; ++t) {
+    const int cur = t & 1;
+    wait_vmcnt<0>();  // K(t), V(t) and ids(t+1) resident
+    BSA_BARRIER();    // every wave's copies visible; every wave done with t-1
+    // Rows of block t+1 (for the last block: the same block again, a
+    // harmless extra copy into the idle buffer).
+    tile_rows4<D>(rows, ids, w, lane, row_bytes);
+    const __bf16* Kc = KV + cur * 2 * TILE;
+    const __bf16* Vc = Kc + TILE;
+
+    // ---- S^T (32 keys x 32 queries) = K_g Q^T, with the copies of block t+1
+    // issued one per product so the memory pipeline sees a steady stream ----
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    {
+      const int krow = 32 * g + (lane & 31);
+      bf16x8 ka[KS];
+#pragma unroll
+      for (int s = 0; s < KS + PF; ++s) {
+        if (s < KS) {
+          ka[s] = *reinterpret_cast<const bf16x8*>(Kc + krow * D + k_swz<CPR>(krow, 2 * s + h2) * 8);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        if (s >= PF) {
+          sacc = mfma32(ka[s - PF], qop[s - PF], sacc);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        }
+        if (s < LPT) {
+          buffer_to_lds16(krs, rows[s] + koff[s], kbuf(cur ^ 1) + (uint32_t)((w * LPT + s) * 1024));
+        } else if (s < 2 * LPT) {
+          buffer_to_lds16(vrs, rows[s - LPT] + voff[s - LPT], vbuf(cur ^ 1) + (uint32_t)((w * LPT + s - LPT) * 1024));
+        } else if (s == 2 * LPT) {
+          stage_ids(prs, max(j2, 0), M, ids_lds, lane);  // near the end: a harmless repeat
+        }
+      }
+    }
+
+    // scalar table reads for the coming blocks (no LDS result is awaited
+    // until the barrier that opens the next block)
+    __builtin_amdgcn_sched_barrier(0);
+    const int j3 = sel[min(t + 3, num - 1)];
+    njn = (j1 >= 0) ? blen[max(j1, 0)] : 0;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- online softmax (log2 domain); lane owns query 32hq + l%32 ----
+    if (nj < M) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
+        sacc[r] = (key < nj) ? sacc[r] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      if constexpr (LSE) lx_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs = 0.f, rsx = 0.f;
+    bf16x8 pop[2];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * hlf + 2 * e;
+        const float a = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -m_use));
+        const float c = fast_exp2(__builtin_fmaf(sacc[r + 1], p.scale_log2, -m_use));
+        pk[e] = pack2_bf16_sum<LSE>(a, c, &rs, &rsx);
+      }
+      pop[hlf] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += rs;
+    if constexpr (LSE) lx_run += rsx;
+
+    // ---- O^T (D x 32 queries) += V_g^T P^T ----
+    {
+      const int g16 = lane >> 4, jl = lane & 15;
+      constexpr int NP = 2 * DT;
+      bf16x8 va[NP];
+#pragma unroll
+      for (int x = 0; x < NP + PF; ++x) {
+        if (x < NP) {
+          const int u = x / DT, dt = x % DT;
+          const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
+          const int c = d >> 3, off = d & 7;
+          const int r0 = 32 * g + 16 * u + 4 * h2 + (jl >> 2);
+          const int r1 = r0 + 8;
+          const bf16x4 lo = lds_read_tr16(Vc + r0 * D + v_swz<CPR>(r0, c) * 8 + off);
+          const bf16x4 hi = lds_read_tr16(Vc + r1 * D + v_swz<CPR>(r1, c) * 8 + off);
+          va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        if (x >= PF) {
+          const int y = x - PF;
+          oacc[y % DT] = mfma32(va[y], pop[y / DT], oacc[y % DT]);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        }
+      }
+    }
+    nj = njn;
+    j1 = j2;
+    j2 = j3;
+  }
+
+  // ---- merge the two key halves of each query row through LDS ----
+  // Once every wave is past its last tile and its copies have landed, buffer 1
+  // is free (the next query block's first copies go to buffer 0).
+  wait_vmcnt<0>();
+  BSA_BARRIER();
+  float* scr = reinterpret_cast<float*>(KV + 2 * TILE) + hq * (64 * DT * 16);
+  float* mx_sh = Mx + hq * 3 * 64;
+  if (g == 1) {
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 v = {oacc[d][4 * c4], oacc[d][4 * c4 + 1], oacc[d][4 * c4 + 2], oacc[d][4 * c4 + 3]};
+        *reinterpret_cast<f32x4*>(scr + ((d * 4 + c4) * 64 + lane) * 4) = v;
+      }
+    mx_sh[lane] = m_run;
+    mx_sh[64 + lane] = l_run;
+    mx_sh[128 + lane] = lx_run;
+  }
+  BSA_BARRIER();
+  if (g == 0) {
+    const float mb = mx_sh[lane], lb = mx_sh[64 + lane], lxb = mx_sh[128 + lane];
+    const float m = fmaxf(m_run, mb);
+    const float fa = (m == -INFINITY) ? 0.f : fast_exp2(m_run - m);
+    const float fb = (m == -INFINITY) ? 0.f : fast_exp2(mb - m);
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(scr + ((d * 4 + c4) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[d][4 * c4 + e] = fa * oacc[d][4 * c4 + e] + fb * v[e];
+      }
+    const float l_part = fa * l_run + fb * lb;
+    const float l_tot = l_part + xor32(l_part);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow < ni) {
+      __bf16* __restrict__ og =
+          reinterpret_cast<__bf16*>(p.o) + b * p.o_sB + (int64_t)qtok * p.o_sN + hh * p.o_sH;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int dd = 32 * d + 8 * jj + 4 * h2;
+          bf16x4 v4 = {(__bf16)(oacc[d][4 * jj + 0] * inv), (__bf16)(oacc[d][4 * jj + 1] * inv),
+                       (__bf16)(oacc[d][4 * jj + 2] * inv), (__bf16)(oacc[d][4 * jj + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(og + dd) = v4;
+        }
+      if constexpr (LSE) {
+        const float lx_part = fa * lx_run + fb * lxb;
+        const float lx = lx_part + xor32(lx_part);
+        if (h2 == 0) p.lse[bh * p.N + qtok] = (lx > 0.f) ? (m + __log2f(lx)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+}
+
+template <int D, bool LSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa4_kernel(VsaAttnParams p,
+                                                                                             int items, int sync) {
+  __shared__ __align__(1024) __bf16 KV[4 * 64 * D];  // 2 buffers x (K, V)
+  __shared__ __align__(256) int Ids[4 * 64];         // token ids, one buffer per wave
+  __shared__ float Mx[2 * 3 * 64];                   // merge: max, rounded sum, exact sum
+  int round = 0;
+  for (int wid = blockIdx.x; wid < items; wid += gridDim.x, ++round) {
+    vsa4_item<D, LSE>(p, wid, KV, Ids, Mx);
+    round_sync(sync, wid, items, round);
   }
 }
 
@@ -414,20 +815,55 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   }
 }
 
+// Resident workgroups of a kernel on the current device; `cache` is the
+// caller's per-device memo for that kernel.
+template <typename K>
+static int64_t resident_groups(K kernel, int threads, int64_t* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  cache[dev] = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  return cache[dev];
+}
+
+template <int D, int MT, bool LSE>
+static hipError_t launch_vsa_lse(const VsaAttnParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.B * p.H * p.J;
+  static int64_t cache[64] = {0};
+  const int64_t resident = resident_groups(vsa_attn_kernel<D, MT, LSE>, 2 * MT, cache);
+  const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
+  const int64_t rounds = (items + grid - 1) / grid;
+  const int sync = (rounds > 1) ? 1 : 0;
+  if (sync) clear_rounds_kernel<<<1, 256, 0, s>>>((int)std::min<int64_t>(rounds, kMaxRounds));
+  vsa_attn_kernel<D, MT, LSE><<<dim3((unsigned)grid), dim3(2 * MT), 0, s>>>(p, (int)items, sync);
+  return hipGetLastError();
+}
+
 template <int D, int MT>
 static hipError_t launch_vsa_mt(const VsaAttnParams& p, hipStream_t s) {
+  return p.lse ? launch_vsa_lse<D, MT, true>(p, s) : launch_vsa_lse<D, MT, false>(p, s);
+}
+
+template <int D, bool LSE>
+static hipError_t launch_vsa4(const VsaAttnParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.B * p.H * p.J;
-  if (p.lse)
-    vsa_attn_kernel<D, MT, true><<<dim3((unsigned)items), dim3(2 * MT), 0, s>>>(p);
-  else
-    vsa_attn_kernel<D, MT, false><<<dim3((unsigned)items), dim3(2 * MT), 0, s>>>(p);
+  static int64_t cache[64] = {0};
+  const int64_t resident = resident_groups(vsa4_kernel<D, LSE>, 256, cache);
+  const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
+  const int64_t rounds = (items + grid - 1) / grid;
+  const int sync = (rounds > 1) ? 1 : 0;
+  if (sync) clear_rounds_kernel<<<1, 256, 0, s>>>((int)std::min<int64_t>(rounds, kMaxRounds));
+  vsa4_kernel<D, LSE><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p, (int)items, sync);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_vsa_d(const VsaAttnParams& p, hipStream_t s) {
   if (p.M <= 32) return launch_vsa_mt<D, 32>(p, s);
-  return launch_vsa_mt<D, 64>(p, s);
+  return p.lse ? launch_vsa4<D, true>(p, s) : launch_vsa4<D, false>(p, s);
 }
 
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s) {

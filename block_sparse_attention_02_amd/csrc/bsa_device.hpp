@@ -102,10 +102,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <bool EXACT = false>
 __device__ __forceinline__ uint32_t pack2_bf16_sum(float a, float b, float* sum, float* exact = nullptr) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  *sum += __builtin_bit_cast(float, u << 16) + __builtin_bit_cast(float, u & 0xffff0000u);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  *sum = __builtin_amdgcn_fdot2_f32_bf16(v, ones, *sum, false);  // exact products, fp32 sum
   if constexpr (EXACT) *exact += a + b;
-  return u;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {

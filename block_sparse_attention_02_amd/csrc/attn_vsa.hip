@@ -400,8 +400,129 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
 // cleared before each launch).
 static __device__ uint32_t g_round_ctr[kMaxRounds];
 
+// Progress balancing between the two workgroups that share a CU.  The wave
+// arbiter favours the older workgroup (by ~18 % here), which would leave the
+// younger one behind at every round boundary; instead each workgroup publishes
+// how many tiles it has finished and raises its waves' priority while it
+// trails its partner.  Slots are found from the hardware CU id, registered
+// once per launch.
+constexpr int kCuKeys = 2048;  // 8 XCDs x 8 SEs x 2 SHs x 16 CUs
+static __device__ uint32_t g_cu_slots[kCuKeys];
+static __device__ uint32_t g_cu_progress[kCuKeys * 2];
+
+// Work distribution of the four-wave kernel's persistent grid: the first
+// gridDim.x query blocks go to the workgroups in order, every further one
+// comes from a global atomic queue, so an XCD that runs faster takes more of
+// them.  The workgroups of one XCD (found from the hardware XCC id) re-align
+// after every query block with a bounded wait, so they touch the same window
+// of each head's K/V, which then stays in that XCD's L2.  Correctness depends
+// only on the queue: each query block is taken exactly once, whatever the
+// waits do.
+constexpr int kXcds = 8;
+static __device__ uint32_t g_queue;
+static __device__ uint32_t g_registered;
+static __device__ uint32_t g_xcd_members[kXcds];
+static __device__ uint32_t g_xcd_exited[kXcds];
+static __device__ uint32_t g_xcd_rounds[kXcds * kMaxRounds];
+
+// Clears the scheduling state before a launch (grid-stride over all tables).
 __global__ void clear_rounds_kernel(int n) {
-  for (int r = threadIdx.x; r < n; r += blockDim.x) g_round_ctr[r] = 0u;
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x, nt = gridDim.x * blockDim.x;
+  for (int r = tid; r < n; r += nt) g_round_ctr[r] = 0u;
+  for (int r = tid; r < kCuKeys; r += nt) g_cu_slots[r] = 0u;
+  for (int r = tid; r < 2 * kCuKeys; r += nt) g_cu_progress[r] = 0u;
+  for (int r = tid; r < kXcds * kMaxRounds; r += nt) g_xcd_rounds[r] = 0u;
+  if (tid < kXcds) {
+    g_xcd_members[tid] = 0u;
+    g_xcd_exited[tid] = 0u;
+  }
+  if (tid == 0) {
+    g_queue = 0u;
+    g_registered = 0u;
+  }
+}
+
+__device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct Cohort {
+  uint32_t xcc = 0, members = 0;
+  int round = 0;
+};
+
+// Join this XCD's cohort; waits (bounded) until every workgroup of the grid
+// has joined so the member count is final.
+__device__ __forceinline__ Cohort cohort_register(uint32_t* sh) {
+  if (threadIdx.x == 0) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1);  // XCC_ID
+    __hip_atomic_fetch_add(&g_xcd_members[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&g_registered, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < 4096; ++t) {
+      if (load_relaxed(&g_registered) >= gridDim.x) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    sh[0] = xcc;
+    sh[1] = load_relaxed(&g_xcd_members[xcc]);
+  }
+  __syncthreads();
+  Cohort c;
+  c.xcc = __builtin_amdgcn_readfirstlane(sh[0]);
+  c.members = __builtin_amdgcn_readfirstlane(sh[1]);
+  __syncthreads();
+  return c;
+}
+
+// Arrive after a query block and wait (bounded) for the cohort's other
+// members, counting those that have already run out of work.
+__device__ __forceinline__ void cohort_sync(Cohort& c) {
+  if (threadIdx.x == 0 && c.round < kMaxRounds) {
+    uint32_t* ctr = &g_xcd_rounds[c.xcc * kMaxRounds + c.round];
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < 4096; ++t) {
+      if (load_relaxed(ctr) + load_relaxed(&g_xcd_exited[c.xcc]) >= c.members) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  ++c.round;
+  __syncthreads();
+}
+
+// The next query block from the queue (>= gridDim.x).
+__device__ __forceinline__ int next_item(uint32_t* sh) {
+  if (threadIdx.x == 0)
+    sh[0] = gridDim.x + __hip_atomic_fetch_add(&g_queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int wid = (int)__builtin_amdgcn_readfirstlane(sh[0]);
+  __syncthreads();
+  return wid;
+}
+
+struct Balance {
+  uint32_t* mine = nullptr;           // this workgroup's finished-tile count
+  const uint32_t* partner = nullptr;  // the other workgroup on the CU
+  uint32_t done = 0;
+};
+
+// Register this workgroup on its CU (call once, by every thread).
+__device__ __forceinline__ Balance balance_register(uint32_t* slot_sh) {
+  Balance bal;
+  if (threadIdx.x == 0) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg(4 | (31 << 11));   // HW_ID
+    const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 7u;  // XCC_ID
+    const uint32_t key = (((xcc * 8u + ((hw >> 13) & 7u)) * 2u + ((hw >> 12) & 1u)) * 16u + ((hw >> 8) & 15u));
+    const uint32_t slot = __hip_atomic_fetch_add(&g_cu_slots[key], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    slot_sh[0] = key;
+    slot_sh[1] = slot;
+  }
+  __syncthreads();
+  const uint32_t key = __builtin_amdgcn_readfirstlane(slot_sh[0]);
+  const uint32_t slot = __builtin_amdgcn_readfirstlane(slot_sh[1]);
+  if (slot < 2u && key < (uint32_t)kCuKeys) {
+    bal.mine = &g_cu_progress[key * 2 + slot];
+    bal.partner = &g_cu_progress[key * 2 + (slot ^ 1u)];
+  }
+  return bal;
 }
 
 // Re-align the resident workgroups after each round: arrive, then wait
@@ -486,7 +607,8 @@ __device__ __forceinline__ void stage4(i32x4 rsrc, uint32_t lds_base, const uint
 }
 
 template <int D, bool LSE>
-__device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __bf16* KV, int* Ids, float* Mx) {
+__device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __bf16* KV, int* Ids, float* Mx,
+                                          Balance& bal) {
   using TM = Tile4<D>;
   constexpr int LPT = TM::LPT, CPR = TM::CPR;
   constexpr int KS = D / 16;   // k-steps of QK^T
@@ -564,10 +686,26 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 
   constexpr int NCOPY = 2 * LPT + 1;  // K and V copies of the next block, then ids
   static_assert(NCOPY <= KS + PF, "copies are spread over the QK^T steps");
+  uint32_t partner_seen = 0;  // partner count, read one block before it is used
   for (int t = 0; t < num; ++t) {
     const int cur = t & 1;
     wait_vmcnt<0>();  // K(t), V(t) and ids(t+1) resident
     BSA_BARRIER();    // every wave's copies visible; every wave done with t-1
+    if (bal.mine != nullptr) {
+      // Every 4 blocks: act on the partner count read 1 block ago (that read
+      // has completed with the wait above), then publish and re-read.
+      if ((t & 3) == 1) {
+        if (bal.done + 1 < __builtin_amdgcn_readfirstlane(partner_seen))
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
+      }
+      if ((t & 3) == 0) {
+        if (w == 0 && lane == 0) __hip_atomic_store(bal.mine, bal.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        partner_seen = __hip_atomic_load(bal.partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      ++bal.done;
+    }
     // Rows of block t+1 (for the last block: the same block again, a
     // harmless extra copy into the idle buffer).
     tile_rows4<D>(rows, ids, w, lane, row_bytes);
@@ -743,11 +881,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(1024) __bf16 KV[4 * 64 * D];  // 2 buffers x (K, V)
   __shared__ __align__(256) int Ids[4 * 64];         // token ids, one buffer per wave
   __shared__ float Mx[2 * 3 * 64];                   // merge: max, rounded sum, exact sum
-  int round = 0;
-  for (int wid = blockIdx.x; wid < items; wid += gridDim.x, ++round) {
-    vsa4_item<D, LSE>(p, wid, KV, Ids, Mx);
-    round_sync(sync, wid, items, round);
+  __shared__ uint32_t slot_sh[2];
+  Balance bal;
+  Cohort coh;
+  if (sync) {
+    bal = balance_register(slot_sh);
+    coh = cohort_register(slot_sh);
   }
+  int wid = blockIdx.x;
+  while (wid < items) {
+    vsa4_item<D, LSE>(p, wid, KV, Ids, Mx, bal);
+    if (sync) {
+      cohort_sync(coh);
+      wid = next_item(slot_sh);
+    } else {
+      wid += gridDim.x;
+    }
+  }
+  if (sync && threadIdx.x == 0)
+    __hip_atomic_fetch_add(&g_xcd_exited[coh.xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ============================================================================
@@ -855,7 +1008,7 @@ static hipError_t launch_vsa4(const VsaAttnParams& p, hipStream_t s) {
   const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
   const int64_t rounds = (items + grid - 1) / grid;
   const int sync = (rounds > 1) ? 1 : 0;
-  if (sync) clear_rounds_kernel<<<1, 256, 0, s>>>((int)std::min<int64_t>(rounds, kMaxRounds));
+  if (sync) clear_rounds_kernel<<<32, 256, 0, s>>>(0);
   vsa4_kernel<D, LSE><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p, (int)items, sync);
   return hipGetLastError();
 }

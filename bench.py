@@ -36,6 +36,27 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 
 
+def _profiled_traffic(profile, sources):
+    """HBM bytes per launch recorded in a committed profile summary, or None
+    when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k_, v_ = line.split(":", 1)
+            fields[k_.strip()] = v_.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "block_sparse_attention_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def _events():
     import torch
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -135,7 +156,9 @@ def bench_video(args):
         "pct_hbm_route": round(100 * route_bytes / (ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {"kernel": "vsa4_kernel (bsa_forward_qouter, block mode)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profiled_traffic("vsa4_kernel_video.md",
+                                                  ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
     }
     ctx = dict(cfg=cfg, x=x, perm=perm, block_len=block_len, q2k_idx=q2k_idx, q2k_num=q2k_num, J=J, M=M)
     return res, ctx

@@ -80,6 +80,7 @@ def bench_video(args):
     inv = torch.empty(N, dtype=torch.int32, device=dev)
     q2k_idx = torch.empty((B, h, J, R), dtype=torch.int32, device=dev)
     q2k_num = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    order = torch.empty((B, h, J), dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     ws = torch.empty(bsa.route_workspace_bytes(q, J, M, R), dtype=torch.uint8, device=dev)
 
@@ -93,7 +94,8 @@ def bench_video(args):
         L.check(lib.vsa_tile_index(T, H, W, *cfg["block"], bsa.api._ptr(perm), bsa.api._ptr(block_len),
                                    bsa.api._ptr(inv), s_ptr))
 
-    ra = bsa.api._route_args(q, k, perm, block_len, J, M, R, R, 1.0 / D ** 0.5, q2k_idx, q2k_num, None, None, None)
+    ra = bsa.api._route_args(q, k, perm, block_len, J, M, R, R, 1.0 / D ** 0.5, q2k_idx, q2k_num, None, None, None,
+                             order)
     nws = ws.numel()
 
     def route():
@@ -102,6 +104,7 @@ def bench_video(args):
     qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
     qa.perm, qa.block_len, qa.J, qa.M = bsa.api._ptr(perm), bsa.api._ptr(block_len), J, M
     qa.q2k_idx, qa.q2k_num, qa.kmax = bsa.api._ptr(q2k_idx), bsa.api._ptr(q2k_num), R
+    qa.item_order = bsa.api._ptr(order)
 
     def attend():
         L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))

@@ -48,7 +48,7 @@ class RouteArgs(ctypes.Structure):
                 ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
                 ("R", _i32), ("kmax", _i32), ("scale", _f32),
                 ("q2k_idx", _p), ("q2k_num", _p),
-                ("qbar", _p), ("kbar", _p), ("E", _p)]
+                ("qbar", _p), ("kbar", _p), ("E", _p), ("item_order", _p)]
 
 
 class QOuterArgs(ctypes.Structure):
@@ -58,7 +58,7 @@ class QOuterArgs(ctypes.Structure):
                 ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
                 ("q2k_idx", _p), ("q2k_num", _p), ("kmax", _i32),
                 ("blk_idx", _p), ("blk_cnt", _p), ("S", _i32), ("BS", _i32), ("causal", _i32),
-                ("lse", _p)]
+                ("lse", _p), ("item_order", _p)]
 
 
 class KvOuterArgs(ctypes.Structure):

@@ -79,9 +79,9 @@ def keep_budget(drop_ratio, J):
     return r
 
 
-def _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E):
+def _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E, item_order=None):
     return L.RouteArgs(_ptr(q), _ptr(k), _desc(q), _dtype(q), _ptr(perm), _ptr(block_len), J, M, R, kmax,
-                       scale, _ptr(q2k_idx), _ptr(q2k_num), _ptr(qbar), _ptr(kbar), _ptr(E))
+                       scale, _ptr(q2k_idx), _ptr(q2k_num), _ptr(qbar), _ptr(kbar), _ptr(E), _ptr(item_order))
 
 
 def route_workspace_bytes(q, J, M, R, kmax=None, debug=False):
@@ -97,11 +97,13 @@ def route_workspace_bytes(q, J, M, R, kmax=None, debug=False):
 
 
 def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug=False,
-                    out=None, workspace=None):
+                    out=None, workspace=None, item_order=None):
     """Per-block means, routing scores and TopK index table.
 
     q, k: [B, N, H, D] (bf16 or float32).  Returns (q2k_idx [B,H,J,kmax],
     q2k_num [B,H,J]) and, with ``debug``, also (qbar, kbar, E) in float32.
+    ``item_order`` (optional int32 [B,H,J] tensor) is filled with a processing
+    order of the query blocks for attention_vsa.
     """
     _need_cuda(q, k, perm, block_len)
     B, N, H, D = q.shape
@@ -118,7 +120,11 @@ def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug
         qbar = torch.empty((B, H, J, D), dtype=torch.float32, device=dev)
         kbar = torch.empty_like(qbar)
         E = torch.empty((B, H, J, J), dtype=torch.float32, device=dev)
-    a = _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E)
+    if item_order is not None:
+        _need_cuda(item_order)
+        if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
+            raise ValueError("item_order must be a contiguous int32 tensor of B*H*J elements")
+    a = _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E, item_order)
     n = ctypes.c_size_t()
     L.check(_lib().vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None or workspace.numel() < n.value:
@@ -134,8 +140,10 @@ def _qouter_args(q, k, v, out, scale, mode, lse):
                         dout=_desc(out), dt=_dtype(q), scale=scale, mode=mode, lse=_ptr(lse))
 
 
-def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None):
-    """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D]."""
+def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
+                  item_order=None):
+    """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
+    ``item_order``: optional processing order (from pool_route_topk)."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -146,6 +154,11 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
     a = _qouter_args(q, k, v, out, scale, L.BSA_SEL_BLOCK, lse)
     a.perm, a.block_len, a.J, a.M = _ptr(perm), _ptr(block_len), J, M
     a.q2k_idx, a.q2k_num, a.kmax = _ptr(q2k_idx), _ptr(q2k_num), q2k_idx.shape[-1]
+    if item_order is not None:
+        _need_cuda(item_order)
+        if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
+            raise ValueError("item_order must be a contiguous int32 tensor of B*H*J elements")
+        a.item_order = _ptr(item_order)
     L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
     return (out, lse) if need_lse else out
 
@@ -226,10 +239,12 @@ def vsa_forward(q, k, v, geom, R, kmax=None, scale=None, need_lse=False, workspa
     """Routed block-sparse attention: pool -> route -> TopK -> exact attention.
 
     Returns (out, q2k_idx, q2k_num) (plus lse with ``need_lse``)."""
+    B, _, H, _ = q.shape
+    order = torch.empty((B, H, geom.J), dtype=torch.int32, device=q.device)
     q2k_idx, q2k_num = pool_route_topk(q, k, geom.perm, geom.block_len, geom.J, geom.M, R, kmax=kmax,
-                                       scale=scale, workspace=workspace, out=index_out)
+                                       scale=scale, workspace=workspace, out=index_out, item_order=order)
     res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
-                        need_lse=need_lse)
+                        need_lse=need_lse, item_order=order)
     if need_lse:
         return res[0], q2k_idx, q2k_num, res[1]
     return res, q2k_idx, q2k_num

@@ -150,7 +150,11 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
   if (e != hipSuccess) return hip_status(e, "pool launch");
   bsa::RouteParams rp{qbar, kbar, (int)a->d.B, (int)a->d.H, a->J, (int)a->d.D, a->R, a->kmax, a->scale,
                       a->q2k_idx, a->q2k_num, a->E};
-  return hip_status(bsa::launch_route_topk(rp, s), "route/topk launch");
+  e = bsa::launch_route_topk(rp, s);
+  if (e != hipSuccess || !a->item_order) return hip_status(e, "route/topk launch");
+  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, (int)(a->d.B * a->d.H), a->J, a->kmax,
+                                           a->item_order, s),
+                    "item order launch");
 }
 
 // ------------------------------------------------------------------- query-outer attention
@@ -194,7 +198,7 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
                          a->dout.sB, a->dout.sN, a->dout.sH,
                          a->perm, a->block_len, a->q2k_idx, a->q2k_num,
                          (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
-                         scale_log2, a->lse};
+                         scale_log2, a->lse, a->item_order};
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   if (a->mode == BSA_SEL_TOKEN) {

@@ -41,6 +41,15 @@ constexpr int kSchedDsRead = 0x100;
 // ordered separately with wait_vmcnt<>().
 #define BSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+// Query block of work item wid = (b*H + h)*J + slot: the slot itself, or the
+// slot's entry of the caller's processing order (-1 when that entry is not a
+// block index).
+__device__ __forceinline__ int item_block(const VsaAttnParams& p, int64_t wid) {
+  if (!p.order) return (int)(wid % p.J);
+  const int i = as_const(p.order)[wid];
+  return (i >= 0 && i < p.J) ? i : -1;
+}
+
 // Physical 16-byte chunk of logical chunk c in K tile row r: 16 consecutive
 // rows read at the same logical chunk land on 16 distinct bank groups.
 template <int CPR>
@@ -159,7 +168,8 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5;  // which half of the wave
-  const int i = (int)(wid % p.J);
+  const int i = item_block(p, wid);
+  if (i < 0) return;  // not a block index (whole workgroup)
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int M = p.M;
@@ -410,16 +420,19 @@ constexpr int kCuKeys = 2048;  // 8 XCDs x 8 SEs x 2 SHs x 16 CUs
 static __device__ uint32_t g_cu_slots[kCuKeys];
 static __device__ uint32_t g_cu_progress[kCuKeys * 2];
 
-// Work distribution of the four-wave kernel's persistent grid: the first
-// gridDim.x query blocks go to the workgroups in order, every further one
-// comes from a global atomic queue, so an XCD that runs faster takes more of
-// them.  The workgroups of one XCD (found from the hardware XCC id) re-align
-// after every query block with a bounded wait, so they touch the same window
-// of each head's K/V, which then stays in that XCD's L2.  Correctness depends
-// only on the queue: each query block is taken exactly once, whatever the
-// waits do.
+// Work distribution of the four-wave kernel's persistent grid.  Work items
+// (in processing order) are cut into chunks of kChunk; chunk c belongs to XCD
+// c % kXcds (found from the hardware XCC id), whose workgroups take its items
+// in order, so the workgroups of one XCD run consecutive items together; an
+// XCD that has used up its chunks takes items of the others', so a faster XCD
+// does more of the work.  The workgroups of one XCD also re-align after every
+// item with a bounded wait, so they touch the same window of each head's K/V,
+// which then stays in that XCD's L2.  Correctness depends only on the
+// per-XCD atomic counters: each item is taken exactly once, whatever the waits
+// do.
 constexpr int kXcds = 8;
-static __device__ uint32_t g_queue;
+constexpr int kChunk = 64;  // items per chunk; chunk c belongs to XCD c % kXcds
+static __device__ uint32_t g_xq[kXcds];  // items taken from each XCD's chunks
 static __device__ uint32_t g_registered;
 static __device__ uint32_t g_xcd_members[kXcds];
 static __device__ uint32_t g_xcd_exited[kXcds];
@@ -436,10 +449,8 @@ __global__ void clear_rounds_kernel(int n) {
     g_xcd_members[tid] = 0u;
     g_xcd_exited[tid] = 0u;
   }
-  if (tid == 0) {
-    g_queue = 0u;
-    g_registered = 0u;
-  }
+  if (tid < kXcds) g_xq[tid] = 0u;
+  if (tid == 0) g_registered = 0u;
 }
 
 __device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
@@ -488,10 +499,26 @@ __device__ __forceinline__ void cohort_sync(Cohort& c) {
   __syncthreads();
 }
 
-// The next query block from the queue (>= gridDim.x).
-__device__ __forceinline__ int next_item(uint32_t* sh) {
-  if (threadIdx.x == 0)
-    sh[0] = gridDim.x + __hip_atomic_fetch_add(&g_queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The k-th work item of XCD x's chunks (-1 past the end; the valid k form a
+// prefix, so a miss means that XCD's chunks are used up).
+__device__ __forceinline__ int xcd_item(uint32_t x, uint32_t k, int items) {
+  const uint64_t item = ((uint64_t)(k / kChunk) * kXcds + x) * kChunk + (k % kChunk);
+  return item < (uint64_t)items ? (int)item : -1;
+}
+
+// The next work item for a workgroup of XCD x: from its own chunks in order,
+// then from the other XCDs' chunks; -1 when everything is taken.  Every item
+// is handed out exactly once (one atomic counter per XCD).
+__device__ __forceinline__ int next_item(uint32_t x, int items, uint32_t* sh) {
+  if (threadIdx.x == 0) {
+    int it = -1;
+    for (uint32_t y = 0; y < (uint32_t)kXcds && it < 0; ++y) {
+      const uint32_t xx = (x + y) % kXcds;
+      if (xcd_item(xx, load_relaxed(&g_xq[xx]), items) < 0) continue;  // used up already
+      it = xcd_item(xx, __hip_atomic_fetch_add(&g_xq[xx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), items);
+    }
+    sh[0] = (uint32_t)it;
+  }
   __syncthreads();
   const int wid = (int)__builtin_amdgcn_readfirstlane(sh[0]);
   __syncthreads();
@@ -620,7 +647,8 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = w >> 1, g = w & 1;  // query half, key half
   const int h2 = lane >> 5;
-  const int i = (int)(wid % p.J);
+  const int i = item_block(p, wid);
+  if (i < 0) return;  // not a block index (whole workgroup)
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   constexpr int M = 64;
@@ -888,12 +916,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bal = balance_register(slot_sh);
     coh = cohort_register(slot_sh);
   }
-  int wid = blockIdx.x;
-  while (wid < items) {
+  int wid = sync ? next_item(coh.xcc, items, slot_sh) : (int)blockIdx.x;
+  while (wid >= 0 && wid < items) {
     vsa4_item<D, LSE>(p, wid, KV, Ids, Mx, bal);
     if (sync) {
       cohort_sync(coh);
-      wid = next_item(slot_sh);
+      wid = next_item(coh.xcc, items, slot_sh);
     } else {
       wid += gridDim.x;
     }
@@ -915,7 +943,8 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   __shared__ float Kt[64 * D];
   __shared__ float Vt[64 * D];
   const int64_t wid = blockIdx.x;
-  const int i = (int)(wid % p.J);
+  const int i = item_block(p, wid);
+  if (i < 0) return;  // not a block index (whole workgroup)
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;

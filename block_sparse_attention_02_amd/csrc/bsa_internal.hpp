@@ -38,6 +38,10 @@ struct RouteParams {
 // Largest J the fused route + TopK kernel handles.
 constexpr int kRouteMaxJ = 4096;
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
+// Processing order of the query blocks of every (b, h): Morton order of the
+// quartile entries of their kept lists ([B*H, J] int32 output).
+hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,
+                             int32_t* order, hipStream_t s);
 
 // ---- query-outer attention -----------------------------------------------------
 struct VsaAttnParams {
@@ -56,6 +60,7 @@ struct VsaAttnParams {
   int64_t N;
   float scale_log2;  // softmax scale * log2(e)
   float* lse;        // optional [B, H, N]
+  const int32_t* order;  // optional [B, H, J] processing order of query blocks
 };
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
 

@@ -450,6 +450,73 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Processing order for the attention kernel.  Query blocks whose kept lists
+// have similar quartile entries read overlapping windows of K/V; listing them
+// next to each other lets the workgroups that run at the same time share L2.
+// One workgroup per (b, h) sorts (Morton code of the three quartiles, 10 bits
+// each; block index) keys with a bitonic network in LDS.  The order changes no
+// attention result.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t spread3_10(uint32_t v) {
+  v &= 0x3ffu;
+  v = (v | (v << 16)) & 0x030000FFu;
+  v = (v | (v << 8)) & 0x0300F00Fu;
+  v = (v | (v << 4)) & 0x030C30C3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void item_order_kernel(const int32_t* __restrict__ q2k_idx,
+                                                          const int32_t* __restrict__ q2k_num, int J, int kmax,
+                                                          int np, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kRouteMaxJ];
+  const int64_t bh = blockIdx.x;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    uint64_t kk = ~0ull;
+    if (i < J) {
+      const int32_t* row = q2k_idx + (bh * J + i) * (int64_t)kmax;
+      const int n = min(q2k_num[bh * J + i], kmax);
+      uint32_t code = 0;
+      if (n > 0) {
+        const int pos[3] = {(n - 1) / 4, (n - 1) / 2, 3 * (n - 1) / 4};
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const int v = min(max(row[pos[c]], 0), J - 1);
+          code |= spread3_10((uint32_t)((int64_t)v * 1024 / J)) << c;
+        }
+      }
+      kk = ((uint64_t)code << 32) | (uint32_t)i;
+    }
+    key[i] = kk;
+  }
+  __syncthreads();
+  for (int k = 2; k <= np; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np; i += blockDim.x) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t a = key[i], b = key[l];
+          if ((a > b) == ((i & k) == 0)) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < J; i += blockDim.x) order[bh * J + i] = (int32_t)(uint32_t)key[i];
+}
+
+hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,
+                             int32_t* order, hipStream_t s) {
+  int np = 1;
+  while (np < J) np <<= 1;
+  if (np > kRouteMaxJ) return hipErrorInvalidValue;
+  item_order_kernel<<<dim3((unsigned)BH), dim3(1024), 0, s>>>(q2k_idx, q2k_num, J, kmax, np, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s) {
   const int cols_per_wave = (p.J + kRouteWaves - 1) / kRouteWaves;
   if (cols_per_wave <= 16) return launch_route_t<1, 2>(p, s);

@@ -122,6 +122,12 @@ int vsa_budget(double drop_ratio, int J);
  * q2k_num   int32 [B, H, J] contiguous
  * qbar, kbar  optional fp32 [B, H, J, D] outputs (NULL: kept in the workspace)
  * E         optional fp32 [B, H, J, J] output of the scores (debug; NULL: none)
+ * item_order  optional int32 [B, H, J] output (NULL: not computed): for each
+ *           (b, h) a permutation of 0..J-1 that places query blocks with
+ *           similar kept sets next to each other (ascending Morton code of the
+ *           quartile entries q2k_idx[.., (n-1)/4], [(n-1)/2], [3(n-1)/4],
+ *           each scaled to 10 bits, ties by block index).  It is a processing
+ *           order for bsa_forward_qouter and changes no result.
  * Supported: 1 <= R <= J <= 4096, D <= 256, any N.  The workspace holds the
  * pooled means: vsa_pool_route_topk_ws() bytes.
  * ------------------------------------------------------------------------- */
@@ -140,6 +146,7 @@ typedef struct {
   float* qbar;
   float* kbar;
   float* E;
+  int32_t* item_order;
 } vsa_route_args;
 
 bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes);
@@ -154,7 +161,11 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
  *   p < q2k_num[b,h,i] (entries < 0 skipped).  No causal mask.  Output rows are
  *   written at the tokens' original positions; padding rows are never written.
  *   Requires Hq == Hkv.  Fields: perm, block_len, J, M, q2k_idx [B,H,J,kmax],
- *   q2k_num [B,H,J], kmax.
+ *   q2k_num [B,H,J], kmax; optional item_order int32 [B,H,J] (NULL: blocks in
+ *   index order), the order in which the query blocks of each (b, h) are
+ *   processed -- a permutation of 0..J-1 (entries outside [0, J) are
+ *   skipped); vsa_pool_route_topk can produce one that raises cache reuse.
+ *   Results do not depend on it.
  *
  * mode BSA_SEL_TOKEN (NSA; [NSA] "Torch朴素实现"): query head hq of token t
  *   reads KV head hq / G (G = Hq / Hkv) and attends to the tokens
@@ -194,6 +205,7 @@ typedef struct {
   int S, BS, causal;
   /* optional */
   float* lse;
+  const int32_t* item_order;
 } bsa_qouter_args;
 
 bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);

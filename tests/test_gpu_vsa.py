@@ -164,6 +164,50 @@ def test_determinism():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_item_order_is_permutation_and_changes_nothing():
+    """The processing order from routing is a per-head permutation of the
+    query blocks, and attention results are bitwise the same with and without
+    it, and with a reversed order (including an entry that is skipped).
+    Twelve heads give more work items than resident workgroups, so the
+    per-XCD queues hand out items too."""
+    cfg = scaled("video", grid=(12, 16, 20), h=12, R=6)
+    x = vsa_inputs(cfg, device=DEV)
+    geom = bsa.VsaGeometry(cfg["grid"], cfg["block"], device=DEV)
+    B, N, H, D = x["q"].shape
+    J = geom.J
+    order = torch.full((B, H, J), -7, dtype=torch.int32, device=DEV)
+    idx, num = bsa.pool_route_topk(x["q"], x["k"], geom.perm, geom.block_len, J, geom.M, cfg["R"],
+                                   item_order=order)
+    torch.cuda.synchronize()
+    o_np = order.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            assert np.array_equal(np.sort(o_np[b, h]), np.arange(J))
+    plain = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num)
+    ordered = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num,
+                                item_order=order)
+    rev = torch.flip(order, dims=[-1]).contiguous()
+    rev_out = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num,
+                                item_order=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), ordered.view(torch.int16))
+    assert torch.equal(plain.view(torch.int16), rev_out.view(torch.int16))
+    # an out-of-range entry skips that slot: its block keeps the previous contents
+    bad = order.clone()
+    skipped = int(bad[0, 0, 0].item())
+    bad[0, 0, 0] = J + 5
+    marker = torch.full_like(plain, 3.0)
+    part = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num,
+                             item_order=bad, out=marker)
+    torch.cuda.synchronize()
+    toks = geom.perm.cpu().numpy().reshape(J, geom.M)[skipped]
+    toks = toks[toks >= 0]
+    assert torch.all(part[0, toks, 0] == 3.0)
+    keep = torch.ones(N, dtype=torch.bool)
+    keep[torch.as_tensor(toks, dtype=torch.long)] = False
+    assert torch.equal(part[0, keep.to(DEV), 0].view(torch.int16), plain[0, keep.to(DEV), 0].view(torch.int16))
+
+
 def test_edge_cases_index_table():
     """Empty rows, -1 entries inside the count, duplicates and kmax > count."""
     cfg = scaled("small", h=2)

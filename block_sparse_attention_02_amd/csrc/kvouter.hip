@@ -174,6 +174,87 @@ __global__ void kv_scatter_kernel(KvOuterParams p, int NB, const int32_t* __rest
 }
 
 // ----------------------------------------------------------------------------
+// Reverse index with per-workgroup histograms.  A workgroup of 1024 threads
+// takes 1024 consecutive (i, r) selection rows of one batch entry and counts
+// their edges per (r, block) bin in LDS; only one global atomic per non-empty
+// bin and workgroup follows (instead of one per edge: every row holds the sink
+// block and popular blocks collect thousands of edges).  The scatter pass
+// recounts, reserves each bin's range with one global atomic and writes its
+// edges at the reserved offset plus an LDS rank.  The order of edges inside a
+// row then depends on atomic order; K1 results do not (each edge writes its
+// own slot).  Used when Hkv * NB fits kIndexBins.
+// ----------------------------------------------------------------------------
+constexpr int kIndexBins = 8192;
+constexpr int kIndexRows = 1024;
+
+template <bool SCATTER>
+__global__ __launch_bounds__(1024) void kv_index_kernel(KvOuterParams p, int NB, int32_t* __restrict__ count,
+                                                        const int32_t* __restrict__ rowptr,
+                                                        int32_t* __restrict__ cursor, int2* __restrict__ edges) {
+  __shared__ int hist[kIndexBins];
+  __shared__ int rank[SCATTER ? kIndexBins : 1];
+  const int nbins = p.Hkv * NB;
+  const int64_t rows_b = (int64_t)p.N * p.Hkv;
+  const int64_t per_b = (rows_b + kIndexRows - 1) / kIndexRows;
+  const int b = (int)(blockIdx.x / per_b);
+  const int64_t rr = (blockIdx.x % per_b) * kIndexRows + threadIdx.x;  // row within batch entry b
+  for (int x = threadIdx.x; x < nbins; x += blockDim.x) {
+    hist[x] = 0;
+    if constexpr (SCATTER) rank[x] = 0;
+  }
+  __syncthreads();
+  const bool live = rr < rows_b;
+  const int64_t tid = (int64_t)b * rows_b + rr;  // global (b, i, r) row
+  const int r = (int)(rr % p.Hkv);
+  const int64_t i = rr / p.Hkv;
+  const int32_t* row = p.q2k + tid * p.ks;
+  const int cnt = live ? (p.q2k_cnt ? min(p.q2k_cnt[tid], p.ks) : p.ks) : 0;
+  const int G = p.Hq / p.Hkv;
+  int nvalid = 0;
+  for (int q = 0; q < cnt; ++q) {
+    const int blk = row[q];
+    if (blk < 0 || blk >= NB) continue;
+    ++nvalid;
+    if (p.causal && (int64_t)blk * p.BK > i) {
+      if constexpr (!SCATTER) {  // empty partial of a block entirely after the query
+        const int s = kv_slot(row, cnt, NB, q, blk);
+        const int64_t base = (((int64_t)b * p.ks + s) * p.N + i) * p.Hq + (int64_t)r * G;
+        for (int h = 0; h < G; ++h) {
+          p.lse_buf[base + h] = -INFINITY;
+          for (int d = 0; d < p.D; ++d) p.o_buf[(base + h) * p.D + d] = (__bf16)0.f;
+        }
+      }
+      continue;
+    }
+    atomicAdd(&hist[r * NB + blk], 1);
+  }
+  if constexpr (!SCATTER) {
+    if (live) p.nslot[tid] = nvalid;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < nbins; x += blockDim.x) {
+    const int c = hist[x];
+    if (c == 0) continue;
+    const int64_t rid = ((int64_t)b * p.Hkv + x / NB) * NB + x % NB;
+    if constexpr (SCATTER)
+      hist[x] = rowptr[rid] + atomicAdd(&cursor[rid], c);
+    else
+      atomicAdd(&count[rid], c);
+  }
+  if constexpr (SCATTER) {
+    __syncthreads();
+    for (int q = 0; q < cnt; ++q) {
+      const int blk = row[q];
+      if (blk < 0 || blk >= NB) continue;
+      if (p.causal && (int64_t)blk * p.BK > i) continue;
+      const int x = r * NB + blk;
+      const int at = hist[x] + atomicAdd(&rank[x], 1);
+      edges[at] = make_int2((int)i, kv_slot(row, cnt, NB, q, blk));
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // K1.  One workgroup (4 waves) per chunk of a reverse-index row (b, r, blk):
 // the block's K and V tiles (BK keys x D) are staged in LDS once; the chunk's
 // edges x G heads form a flat list of query rows processed 128 at a time, 32
@@ -341,9 +422,268 @@ __global__ __launch_bounds__(256) void kv_k1_kernel(KvOuterParams p, int NB, con
   }
 }
 
+// ----------------------------------------------------------------------------
+// K1 on 16x16x32 MFMAs.  One workgroup of 8 waves per chunk stages the
+// block's K and V tiles (BK x D) in LDS once; every wave then walks its own
+// 16-row tiles of the chunk's flat (edge, head) row list -- with G = 16 one
+// tile is one edge: one query position and its 16 heads -- with no further
+// barrier:
+//   S^T (BK keys x 16 rows) = K Q^T     v_mfma_f32_16x16x32_bf16
+//   single-pass softmax per row over the block's visible keys
+//   O^T (D x 16 rows)       = V^T P^T   v_mfma_f32_16x16x32_bf16
+// Lane l owns row l%16 and keys 16kt + 4(l/16) + i of S^T; the 8 weights of
+// a 32-key step are the B operand of the PV product as they lie (V rows are
+// read in the matching order).  The next tile's query rows are loaded into
+// the operand registers right after the QK^T product that frees them, the
+// edge list two tiles ahead, so the gathers overlap the softmax and PV.
+// ----------------------------------------------------------------------------
+template <int D, int BK>
+struct K1w {
+  static constexpr int NW = 8;                     // waves per workgroup
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int LPT = BK * CPR / (64 * NW); // staging copies per lane per tensor
+  static constexpr int KT = BK / 16;               // 16-key tiles of S^T
+  static constexpr int KS = D / 32;                // 32-channel k-steps of QK^T
+  static constexpr int DT = D / 16;                // 16-channel tiles of O^T
+  static constexpr int US = BK / 32;               // 32-key k-steps of PV
+  static_assert(LPT >= 1 && KT % 2 == 0 && DT % 2 == 0, "K1 shape");
+};
+
+// 16-byte chunk c of row r sits at physical chunk c ^ (r % 16).
+template <int CPR>
+__device__ __forceinline__ int k1w_swz(int r, int c) {
+  return c ^ (r & (CPR >= 16 ? 15 : CPR - 1));
+}
+
+// Edge and head of flat row f of a chunk (G heads per edge).
+struct K1Row {
+  int qpos, slot, hq;
+};
+
+template <int D, int BK>
+__global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, const int32_t* __restrict__ nchunk,
+                                                     const int4* __restrict__ chunks, const int2* __restrict__ edges) {
+  using SH = K1w<D, BK>;
+  constexpr int CPR = SH::CPR;
+  __shared__ __align__(1024) __bf16 Ks[BK * D];
+  __shared__ __align__(1024) __bf16 Vs[BK * D];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, jl = lane & 15;
+  if ((int)blockIdx.x >= *nchunk) return;
+  const int4 ck = chunks[blockIdx.x];
+  const int rid = ck.x, e0 = ck.y, e1 = ck.z;
+  const int blk = rid % NB;
+  const int r = (rid / NB) % p.Hkv;
+  const int b = rid / (NB * p.Hkv);
+  const int G = p.Hq / p.Hkv;
+  const int64_t k0 = (int64_t)blk * BK;
+  const int nkeys = (int)min((int64_t)BK, p.N - k0);
+
+  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + r * p.kv_sH;
+  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + r * p.kv_sH;
+#pragma unroll
+  for (int kk = 0; kk < SH::LPT; ++kk) {
+    const int cidx = (kk * SH::NW + w) * 64 + lane;
+    const int row = cidx / CPR, pc = cidx % CPR;
+    const int64_t pos = k0 + min(row, nkeys - 1);
+    global_to_lds16(kg + pos * p.kv_sN + k1w_swz<CPR>(row, pc) * 8, Ks + (size_t)(kk * SH::NW + w) * 64 * 8);
+    global_to_lds16(vg + pos * p.kv_sN + k1w_swz<CPR>(row, pc) * 8, Vs + (size_t)(kk * SH::NW + w) * 64 * 8);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const int64_t nrows = (int64_t)(e1 - e0) * G;
+  const int ntile = (int)((nrows + 15) / 16);
+  const __bf16* __restrict__ qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB;
+  auto row_of = [&](int t, int2 ed) {
+    const int64_t f = min((int64_t)t * 16 + jl, nrows - 1);
+    return K1Row{ed.x, ed.y, r * G + (int)(f % G)};
+  };
+  auto edge_of = [&](int t) {
+    const int64_t f = min((int64_t)t * 16 + jl, nrows - 1);
+    return edges[e0 + f / G];
+  };
+  auto load_q = [&](bf16x8* qop, const K1Row& rw) {
+    const __bf16* qrow = qbase + (int64_t)rw.qpos * p.q_sN + (int64_t)rw.hq * p.q_sH;
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
+  };
+
+  // The query rows of a wave's tiles t, t+NW, ... are gathered two tiles
+  // ahead into two register sets used in turn; edge records three ahead.
+  int2 ea = edge_of(min(w, ntile - 1));
+  int2 eb = edge_of(min(w + SH::NW, ntile - 1));
+  int2 ec = edge_of(min(w + 2 * SH::NW, ntile - 1));
+  bf16x8 qa[SH::KS], qb[SH::KS];
+  load_q(qa, row_of(min(w, ntile - 1), ea));
+  __builtin_amdgcn_sched_barrier(0);
+  // Output of a tile is written one tile later, right after the next QK^T and
+  // before the next query gather, so at every QK^T the gathered rows are the
+  // youngest memory operations in flight and the wait for them never waits
+  // for stores.  Every load and store is unconditional (a tail row beyond the
+  // chunk recomputes the chunk's last row and writes the same values), and the
+  // first "pending" output is zeros written to the wave's own first tile,
+  // which the real values overwrite later in program order.
+  u32x4 pend[SH::DT / 2];
+#pragma unroll
+  for (int m = 0; m < SH::DT / 2; ++m) pend[m] = u32x4{0u, 0u, 0u, 0u};
+  float pend_lse = -INFINITY;
+  int64_t pend_obase;
+  {
+    const K1Row r0w = row_of(min(w, ntile - 1), ea);
+    pend_obase = (((int64_t)b * p.ks + r0w.slot) * p.N + r0w.qpos) * p.Hq + r0w.hq;
+  }
+  auto store_pending = [&]() {
+    __bf16* orow = p.o_buf + pend_obase * D;
+    const bool odd = (g & 1) != 0;
+#pragma unroll
+    for (int m = 0; m < SH::DT / 2; ++m) {
+      const int ch = odd ? 32 * m + 16 + 4 * (g - 1) : 32 * m + 4 * g;
+      *reinterpret_cast<u32x4*>(orow + ch) = pend[m];
+    }
+    p.lse_buf[pend_obase] = pend_lse;  // the four lanes of a row write the same value
+  };
+  // Same memory-operation history on entry as around the loop: gather,
+  // (zero) output of the pending tile, gather of the other register set.
+  store_pending();
+  load_q(qb, row_of(min(w + SH::NW, ntile - 1), eb));
+  __builtin_amdgcn_sched_barrier(0);
+  // One tile: t with edge ed_cur and query rows qop; afterwards qop holds the
+  // rows of tile t + 2NW (edge ed_two); returns the edge of tile t + 3NW.
+  auto tile = [&](const int t, const int2 ed_cur, bf16x8* qop, const int2 ed_two) -> int2 {
+    const K1Row rw = row_of(t, ed_cur);
+
+    // ---- S^T over all BK keys (operands read PF products ahead) ----
+    constexpr int PF = 2;
+    constexpr int NQ = SH::KT * SH::KS;
+    f32x4 sacc[SH::KT];
+#pragma unroll
+    for (int kt = 0; kt < SH::KT; ++kt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sacc[kt][x] = 0.f;
+    {
+      bf16x8 ka[NQ];
+#pragma unroll
+      for (int x = 0; x < NQ + PF; ++x) {
+        if (x < NQ) {
+          const int kt = x / SH::KS, s = x % SH::KS;
+          const int krow = 16 * kt + jl;
+          ka[x] = *reinterpret_cast<const bf16x8*>(Ks + krow * D + k1w_swz<CPR>(krow, 4 * s + g) * 8);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (x >= PF) {
+          const int y = x - PF;
+          sacc[y / SH::KS] = mfma16(ka[y], qop[y % SH::KS], sacc[y / SH::KS]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    }
+    // ---- next tile's operands: edges two tiles ahead, query rows one ahead ----
+    const int2 ed_far = edge_of(min(t + 3 * SH::NW, ntile - 1));
+    store_pending();
+    load_q(qop, row_of(min(t + 2 * SH::NW, ntile - 1), ed_two));
+    __builtin_amdgcn_sched_barrier(0);  // keep the gathers here, ahead of the softmax
+
+    // ---- single-pass softmax (log2 domain) with the causal / tail mask ----
+    const int64_t last = p.causal ? min((int64_t)rw.qpos, p.N - 1) : p.N - 1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < SH::KT; ++kt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int key = 16 * kt + 4 * g + x;
+        const bool ok = key < nkeys && k0 + key <= last;
+        const float v = ok ? sacc[kt][x] : -INFINITY;
+        sacc[kt][x] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, xor32(mx));
+    const float m_use = (mx == -INFINITY) ? 0.f : mx * p.scale_log2;
+    float rs = 0.f, rsx = 0.f;
+    bf16x8 pop[SH::US];
+#pragma unroll
+    for (int u = 0; u < SH::US; ++u) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kt = 2 * u + (e >> 1), x = 2 * (e & 1);
+        pk[e] = pack2_bf16_sum<true>(fast_exp2(__builtin_fmaf(sacc[kt][x], p.scale_log2, -m_use)),
+                                     fast_exp2(__builtin_fmaf(sacc[kt][x + 1], p.scale_log2, -m_use)), &rs, &rsx);
+      }
+      pop[u] = __builtin_bit_cast(bf16x8, pk);
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += xor32(rs);
+    rsx += __shfl_xor(rsx, 16, 64);
+    rsx += xor32(rsx);
+
+    // ---- O^T = V^T P^T ----
+    f32x4 oacc[SH::DT];
+#pragma unroll
+    for (int dt = 0; dt < SH::DT; ++dt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) oacc[dt][x] = 0.f;
+    {
+      constexpr int NV = SH::US * SH::DT;
+      bf16x8 va[NV];
+#pragma unroll
+      for (int x = 0; x < NV + PF; ++x) {
+        if (x < NV) {
+          const int u = x / SH::DT, dt = x % SH::DT;
+          const int c = 2 * dt + ((jl & 3) >> 1), off = 4 * (jl & 1);
+          const int r0 = 32 * u + 4 * g + (jl >> 2);
+          const int r1 = r0 + 16;
+          const bf16x4 lo = lds_read_tr16(Vs + r0 * D + k1w_swz<CPR>(r0, c) * 8 + off);
+          const bf16x4 hi = lds_read_tr16(Vs + r1 * D + k1w_swz<CPR>(r1, c) * 8 + off);
+          va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        if (x >= PF) {
+          const int y = x - PF;
+          oacc[y % SH::DT] = mfma16(va[y], pop[y / SH::DT], oacc[y % SH::DT]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    }
+
+    // ---- normalised partial and its log-sum-exp into the edge's slot ----
+    // Lanes g and g^1 trade halves so that every lane writes 16 bytes: even g
+    // writes channels 32m + 4g .. +7 of tile pair m, odd g channels
+    // 32m + 16 + 4(g-1) .. +7.
+    const float inv = (rs > 0.f) ? 1.f / rs : 0.f;
+    pend_obase = (((int64_t)b * p.ks + rw.slot) * p.N + rw.qpos) * p.Hq + rw.hq;
+#pragma unroll
+    for (int m = 0; m < SH::DT / 2; ++m) {
+      const bf16x4 v0 = {(__bf16)(oacc[2 * m][0] * inv), (__bf16)(oacc[2 * m][1] * inv),
+                         (__bf16)(oacc[2 * m][2] * inv), (__bf16)(oacc[2 * m][3] * inv)};
+      const bf16x4 v1 = {(__bf16)(oacc[2 * m + 1][0] * inv), (__bf16)(oacc[2 * m + 1][1] * inv),
+                         (__bf16)(oacc[2 * m + 1][2] * inv), (__bf16)(oacc[2 * m + 1][3] * inv)};
+      const bool odd = (g & 1) != 0;
+      const uint2 send = __builtin_bit_cast(uint2, odd ? v0 : v1);
+      uint2 recv;
+      recv.x = (uint32_t)__shfl_xor((int)send.x, 16, 64);
+      recv.y = (uint32_t)__shfl_xor((int)send.y, 16, 64);
+      const uint2 mine = __builtin_bit_cast(uint2, odd ? v1 : v0);
+      pend[m] = odd ? u32x4{recv.x, recv.y, mine.x, mine.y} : u32x4{mine.x, mine.y, recv.x, recv.y};
+    }
+    pend_lse = (rsx > 0.f) ? (m_use + __log2f(rsx)) * kLn2 : -INFINITY;
+    return ed_far;
+  };
+  for (int t = w; t < ntile; t += 2 * SH::NW) {
+    const int2 ed3 = tile(t, ea, qa, ec);
+    if (t + SH::NW >= ntile) break;
+    const int2 ed4 = tile(t + SH::NW, eb, qb, ed3);
+    ea = ec;
+    eb = ed3;
+    ec = ed4;
+  }
+  if (w < ntile) store_pending();  // the wave's last tile
+}
+
 template <int D, int BK>
 static hipError_t launch_k1(const KvOuterParams& p, int NB, const KvLayout& L, char* ws, hipStream_t s) {
-  kv_k1_kernel<D, BK><<<dim3(L.max_chunks), dim3(256), 0, s>>>(
+  kv_k1w_kernel<D, BK><<<dim3(L.max_chunks), dim3(512), 0, s>>>(
       p, NB, reinterpret_cast<const int32_t*>(ws + L.off_nchunk), reinterpret_cast<const int4*>(ws + L.off_chunks),
       reinterpret_cast<const int2*>(ws + L.off_edges));
   return hipGetLastError();
@@ -364,9 +704,17 @@ hipError_t launch_kvouter(const KvOuterParams& p, void* wsv, hipStream_t s) {
   kv_clear_kernel<<<dim3(min(1024, (L.rows + 255) / 256)), dim3(256), 0, s>>>(count, cursor, L.rows);
   const int64_t threads = (int64_t)p.B * p.N * p.Hkv;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  kv_count_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, count);
+  const bool lds_index = (int64_t)p.Hkv * NB <= kIndexBins;
+  const unsigned igrid = (unsigned)(p.B * (((int64_t)p.N * p.Hkv + kIndexRows - 1) / kIndexRows));
+  if (lds_index)
+    kv_index_kernel<false><<<dim3(igrid), dim3(kIndexRows), 0, s>>>(p, NB, count, nullptr, nullptr, nullptr);
+  else
+    kv_count_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, count);
   kv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(count, L.rows, cap, rowptr, nchunk, chunks);
-  kv_scatter_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, rowptr, cursor, edges);
+  if (lds_index)
+    kv_index_kernel<true><<<dim3(igrid), dim3(kIndexRows), 0, s>>>(p, NB, nullptr, rowptr, cursor, edges);
+  else
+    kv_scatter_kernel<<<dim3(grid), dim3(256), 0, s>>>(p, NB, rowptr, cursor, edges);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128) return p.BK == 128 ? launch_k1<128, 128>(p, NB, L, ws, s) : launch_k1<128, 64>(p, NB, L, ws, s);

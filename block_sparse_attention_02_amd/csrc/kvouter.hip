@@ -725,29 +725,54 @@ hipError_t launch_kvouter(const KvOuterParams& p, void* wsv, hipStream_t s) {
 // K2: one workgroup per (b, position); thread handles 8 channels of one head.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_combine_kernel(CombineParams p) {
+  constexpr int SB = 8;  // slots per batch: their loads are all in flight together
   const int64_t bi = blockIdx.x;
   const int64_t i = bi % p.N;
   const int b = (int)(bi / p.N);
   const int G = p.Hq / p.Hkv;
   const int cpr = p.D / 8;
+  const int64_t sstride = p.N * p.Hq;  // rows between consecutive slots
   for (int c = threadIdx.x; c < p.Hq * cpr; c += 256) {
     const int hq = c / cpr, dc = c % cpr;
     const int n = min(p.nslot[((int64_t)b * p.N + i) * p.Hkv + hq / G], p.ks);
+    const int64_t row0 = ((int64_t)b * p.ks * p.N + i) * p.Hq + hq;
+    // a = max_s L_s, z = sum_s exp(L_s - a)
     float a = -INFINITY;
-    for (int s = 0; s < n; ++s) a = fmaxf(a, p.lse_buf[(((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq]);
+    for (int s0 = 0; s0 < n; s0 += SB) {
+      float l[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) l[u] = (s0 + u < n) ? p.lse_buf[row0 + (s0 + u) * sstride] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) a = fmaxf(a, l[u]);
+    }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (n > 0 && a != -INFINITY) {
       float z = 0.f;
-      for (int s = 0; s < n; ++s)
-        z += __expf(p.lse_buf[(((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq] - a);
-      L = a + __logf(z);
-      for (int s = 0; s < n; ++s) {
-        const int64_t row = (((int64_t)b * p.ks + s) * p.N + i) * p.Hq + hq;
-        const float wgt = __expf(p.lse_buf[row] - L);
-        const bf16x8 o = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
+      for (int s0 = 0; s0 < n; s0 += SB) {
+        float l[SB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[e];
+        for (int u = 0; u < SB; ++u) l[u] = (s0 + u < n) ? p.lse_buf[row0 + (s0 + u) * sstride] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) z += __expf(l[u] - a);
+      }
+      L = a + __logf(z);
+      for (int s0 = 0; s0 < n; s0 += SB) {
+        bf16x8 o[SB];
+        float l[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const bool ok = s0 + u < n;
+          const int64_t row = row0 + (int64_t)min(s0 + u, n - 1) * sstride;
+          o[u] = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
+          l[u] = ok ? p.lse_buf[row] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const float wgt = __expf(l[u] - L);  // 0 for the batch's padding slots
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[u][e];
+        }
       }
     }
     bf16x8 out;

@@ -141,4 +141,9 @@ __device__ __forceinline__ uint32_t float_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// inverse of float_key (a negative zero comes back as +0)
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 }  // namespace bsa

@@ -157,6 +157,7 @@ hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_
 // kept ids are emitted in increasing order from per-row bit masks.
 // ============================================================================
 constexpr int kRouteWaves = 8;
+constexpr int kBucket = 64;  // bucket keys gathered per row (more: plain rounds)
 
 __device__ __forceinline__ int wave_excl_scan(int x) {
   const int lane = threadIdx.x & 63;
@@ -211,7 +212,9 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   __syncthreads();
 
   // ---- scores: E^T tiles for this wave's columns -----------------------------
-  float sc[RT][NT][4];
+  // order-preserving keys of this lane's scores (padding columns: key 0,
+  // below every float)
+  uint32_t key[RT][NT][4];
   const int g = lane >> 4, l16 = lane & 15;
   if constexpr (KD > 0) {
     // D is a multiple of 32: unconditional loads (rows past J clamped), and the
@@ -257,7 +260,11 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
+        for (int v = 0; v < 4; ++v) {
+          const float e = acc[rt][v] * p.scale;
+          const int j = w * CW + 16 * t + 4 * g + v;
+          key[rt][t][v] = (j < J) ? float_key(e) : 0u;
+        }
     }
   } else {
     // any D <= 256: element-wise guarded loads (small problems)
@@ -294,44 +301,37 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sc[rt][t][v] = acc[rt][v] * p.scale;
-    }
-  }
-
-  // optional debug copy of the scores
-  if (p.E) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int i = i0 + 16 * rt + l16;
-      if (i >= J) continue;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
         for (int v = 0; v < 4; ++v) {
+          const float e = acc[rt][v] * p.scale;
           const int j = w * CW + 16 * t + 4 * g + v;
-          if (j < J) p.E[((int64_t)bh * J + i) * J + j] = sc[rt][t][v];
+          key[rt][t][v] = (j < J) ? float_key(e) : 0u;
         }
     }
   }
 
-  // ---- order-preserving keys; padding columns get key 0 (below every float) ----
-  uint32_t key[RT][NT][4];
+  if (p.E) {  // optional debug copy of the scores (the key map is a bijection)
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = w * CW + 16 * t + 4 * g + v;
-        key[rt][t][v] = (j < J) ? float_key(sc[rt][t][v]) : 0u;
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int i = i0 + 16 * rt + l16, j = w * CW + 16 * t + 4 * g + v;
+          if (i < J && j < J) p.E[((int64_t)bh * J + i) * J + j] = key_float(key[rt][t][v]);
+        }
+  }
 
   // ---- exact threshold: the R-th largest key of every row ------------------------
+  // Rounds over bits 31..16 fix the threshold's top half.  The keys that share
+  // it (the row's "bucket", a handful for continuous scores) are then gathered
+  // in LDS and one wave finds the exact rank among them with ballots.  When
+  // some row's bucket holds more than kBucket keys the workgroup finishes with
+  // the plain rounds over bits 15..0 instead; both give the same threshold.
   uint32_t thr[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) thr[rt] = 0u;
   int par = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  auto round_bit = [&](int bit) {
     int cnt[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -358,6 +358,72 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
       if (tot >= p.R) thr[rt] |= (1u << bit);
     }
     par ^= 1;
+  };
+  for (int bit = 31; bit >= 16; --bit) round_bit(bit);
+
+  // bucket of each row: keys whose top 16 bits equal the threshold's
+  {
+    int* bcnt = red + 2 * kRouteWaves * BM;                   // [BM] bucket sizes
+    int* res = bcnt + BM;                                     // [BM] final thresholds
+    int* flag = res + BM;                                     // [1] some bucket overflowed
+    uint32_t* bkey = reinterpret_cast<uint32_t*>(flag + 4);   // [BM][kBucket]
+    for (int e = threadIdx.x; e < BM; e += 512) bcnt[e] = 0;
+    if (threadIdx.x == 0) *flag = 0;
+    __syncthreads();
+    int above[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * rt + l16;
+      const uint32_t hi = thr[rt] >> 16;
+      int c = 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t k = key[rt][t][v];  // padding columns hold 0, never in a bucket above 0
+          c += ((k >> 16) > hi) ? 1 : 0;
+          if ((k >> 16) == hi && (w * CW + 16 * t + 4 * g + v) < J) {
+            const int slot = atomicAdd(&bcnt[row], 1);
+            if (slot < kBucket) bkey[row * kBucket + slot] = k;
+          }
+        }
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      above[rt] = c;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) red[(par * kRouteWaves + w) * BM + 16 * rt + lane] = above[rt];
+    }
+    __syncthreads();
+    for (int row = threadIdx.x; row < BM; row += 512)
+      if (bcnt[row] > kBucket) *flag = 1;
+    __syncthreads();
+    if (*flag) {
+      for (int bit = 15; bit >= 0; --bit) round_bit(bit);
+    } else {
+      // the need-th largest bucket key, need = R - #keys above the bucket;
+      // one wave per row, one bucket key per lane, ballots over the low 16 bits
+      for (int row = w; row < BM; row += kRouteWaves) {
+        int ab = 0;
+        for (int ww = 0; ww < kRouteWaves; ++ww) ab += red[(par * kRouteWaves + ww) * BM + row];
+        const int need = p.R - ab;
+        const int nb = bcnt[row];
+        const uint32_t mine = lane < nb ? bkey[row * kBucket + lane] : 0u;
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(
+                                (int)(lane < nb ? mine : 0u)) & 0xffff0000u;
+        uint32_t t32 = hi;
+        for (int bit = 15; bit >= 0; --bit) {
+          const uint32_t cand = t32 | (1u << bit);
+          const int c = __popcll(__builtin_amdgcn_ballot_w64(lane < nb && mine >= cand));
+          if (c >= need) t32 = cand;
+        }
+        if (lane == 0) res[row] = (int)t32;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) thr[rt] = (uint32_t)res[16 * rt + l16];
+    }
   }
 
   // ---- bit masks of keys above / equal to the threshold ------------------------
@@ -441,7 +507,7 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
   constexpr int MW = kRouteWaves * 16 * NT / 32;
   const int KS = (p.D + 31) / 32, DP = KS * 32 + 8;
   const size_t smem = (size_t)2 * BM * DP * sizeof(__bf16) + (size_t)2 * BM * MW * 4 +
-                      (size_t)2 * kRouteWaves * BM * 4;
+                      (size_t)2 * kRouteWaves * BM * 4 + (size_t)(2 * BM + 4) * 4 + (size_t)BM * kBucket * 4;
   switch (p.D) {
     case 64: return launch_route_k<NT, RT, 64>(p, smem, s);
     case 128: return launch_route_k<NT, RT, 128>(p, smem, s);

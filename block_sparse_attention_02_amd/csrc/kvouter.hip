@@ -255,174 +255,6 @@ __global__ __launch_bounds__(1024) void kv_index_kernel(KvOuterParams p, int NB,
 }
 
 // ----------------------------------------------------------------------------
-// K1.  One workgroup (4 waves) per chunk of a reverse-index row (b, r, blk):
-// the block's K and V tiles (BK keys x D) are staged in LDS once; the chunk's
-// edges x G heads form a flat list of query rows processed 128 at a time, 32
-// rows per wave:
-//   S^T (keys x rows) = K Q^T     32x32x16 bf16 MFMA, all BK keys at once
-//   single-pass local softmax per row (causal mask per query position)
-//   O^T (chans x rows) = V^T P^T  32x32x16 bf16 MFMA
-// and every row writes its normalised partial O_s (bf16) and L_s (fp32) to the
-// edge's preassigned slot.
-// ----------------------------------------------------------------------------
-template <int D, int BK>
-struct K1Shape {
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int LPT = BK * CPR / 256;      // tile copies per thread
-  static constexpr int KT = BK / 32;              // 32-key tiles of S^T
-  static constexpr int KS = D / 16;               // k-steps of QK^T
-  static constexpr int DT = D / 32;               // 32-channel tiles of O^T
-  static constexpr int US = BK / 16;              // 16-key steps of PV
-};
-
-template <int CPR>
-__device__ __forceinline__ int k1_k_swz(int r, int c) { return c ^ (r & 7); }
-template <int CPR>
-__device__ __forceinline__ int k1_v_swz(int r, int c) {
-  if constexpr (CPR >= 16) {
-    // XOR pattern {0, 6, 10, 12} for r % 4 = 0..3, packed in nibbles
-    return c ^ ((0xCA60 >> (4 * (r & 3))) & 15);
-  } else {
-    return c ^ (2 * (r & 3));
-  }
-}
-
-template <int D, int BK>
-__global__ __launch_bounds__(256) void kv_k1_kernel(KvOuterParams p, int NB, const int32_t* __restrict__ nchunk,
-                                                    const int4* __restrict__ chunks, const int2* __restrict__ edges) {
-  using SH = K1Shape<D, BK>;
-  __shared__ __align__(1024) __bf16 Ks[BK * D];
-  __shared__ __align__(1024) __bf16 Vs[BK * D];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h2 = lane >> 5;
-  if ((int)blockIdx.x >= *nchunk) return;
-  const int4 ck = chunks[blockIdx.x];
-  const int rid = ck.x, e0 = ck.y, e1 = ck.z;
-  const int blk = rid % NB;
-  const int r = (rid / NB) % p.Hkv;
-  const int b = rid / (NB * p.Hkv);
-  const int G = p.Hq / p.Hkv;
-  const int64_t k0 = (int64_t)blk * BK;
-  const int nkeys = (int)min((int64_t)BK, p.N - k0);
-
-  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + r * p.kv_sH;
-  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + r * p.kv_sH;
-  // ---- stage the K and V tiles once (rows past N clamped to valid memory) ----
-#pragma unroll
-  for (int kk = 0; kk < SH::LPT; ++kk) {
-    const int chunk = (kk * 4 + w) * 64 + lane;
-    const int row = chunk / SH::CPR, pc = chunk % SH::CPR;
-    const int64_t pos = k0 + min(row, nkeys - 1);
-    global_to_lds16(kg + pos * p.kv_sN + k1_k_swz<SH::CPR>(row, pc) * 8, Ks + (size_t)(kk * 4 + w) * 64 * 8);
-    global_to_lds16(vg + pos * p.kv_sN + k1_v_swz<SH::CPR>(row, pc) * 8, Vs + (size_t)(kk * 4 + w) * 64 * 8);
-  }
-  wait_vmcnt<0>();
-  BSA_BARRIER();
-
-  const int64_t nrows = (int64_t)(e1 - e0) * G;
-  const __bf16* __restrict__ qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB;
-  for (int64_t t0 = 0; t0 < nrows; t0 += 128) {
-    // ---- this lane's query row: flat index t0 + 32w + l%32 -> (edge, head) ----
-    const int64_t fr = t0 + 32 * w + (lane & 31);
-    const bool row_ok = fr < nrows;
-    const int64_t frc = row_ok ? fr : nrows - 1;
-    const int2 ed = edges[e0 + frc / G];
-    const int hq = r * G + (int)(frc % G);
-    const int64_t qpos = ed.x;
-    const __bf16* qrow = qbase + qpos * p.q_sN + (int64_t)hq * p.q_sH;
-    bf16x8 qop[SH::KS];
-#pragma unroll
-    for (int s = 0; s < SH::KS; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * h2);
-
-    // ---- S^T over all BK keys ----
-    f32x16 sacc[SH::KT];
-#pragma unroll
-    for (int kt = 0; kt < SH::KT; ++kt) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sacc[kt][x] = 0.f;
-      const int krow = 32 * kt + (lane & 31);
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Ks + krow * D + k1_k_swz<SH::CPR>(krow, 2 * s + h2) * 8);
-        sacc[kt] = mfma32(a, qop[s], sacc[kt]);
-      }
-    }
-    // ---- local softmax (log2 domain) with the causal / tail mask ----
-    const int64_t last = p.causal ? min(qpos, p.N - 1) : p.N - 1;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < SH::KT; ++kt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int key = 32 * kt + 8 * (x >> 2) + 4 * h2 + (x & 3);
-        const bool ok = key < nkeys && k0 + key <= last;
-        const float v = ok ? sacc[kt][x] * p.scale_log2 : -INFINITY;
-        sacc[kt][x] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    // weights rounded to bf16 once; the row sum uses the rounded values
-    float rs = 0.f, rsx = 0.f;
-    bf16x8 pop[SH::US];
-#pragma unroll
-    for (int kt = 0; kt < SH::KT; ++kt)
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 8 * hlf + 2 * e;
-          pk[e] = pack2_bf16_sum<true>(fast_exp2(sacc[kt][x] - m_use), fast_exp2(sacc[kt][x + 1] - m_use), &rs,
-                                       &rsx);
-        }
-        pop[2 * kt + hlf] = __builtin_bit_cast(bf16x8, pk);
-      }
-    const float l_tot = rs + xor32(rs);     // normalises O_s (rounded weights)
-    const float l_exact = rsx + xor32(rsx);  // gives L_s
-    // ---- O^T = V^T P^T ----
-    f32x16 oacc[SH::DT];
-#pragma unroll
-    for (int dt = 0; dt < SH::DT; ++dt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) oacc[dt][x] = 0.f;
-    {
-      const int g16 = lane >> 4, jl = lane & 15;
-#pragma unroll
-      for (int u = 0; u < SH::US; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < SH::DT; ++dt) {
-          const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
-          const int c = d >> 3, off = d & 7;
-          const int r0 = 16 * u + 4 * h2 + (jl >> 2);
-          const int r1 = r0 + 8;
-          const bf16x4 lo = lds_read_tr16(Vs + r0 * D + k1_v_swz<SH::CPR>(r0, c) * 8 + off);
-          const bf16x4 hi = lds_read_tr16(Vs + r1 * D + k1_v_swz<SH::CPR>(r1, c) * 8 + off);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = mfma32(a, pop[u], oacc[dt]);
-        }
-      }
-    }
-    // ---- write the normalised partial and its log-sum-exp to the edge's slot ----
-    if (row_ok) {
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      const int64_t obase = (((int64_t)b * p.ks + ed.y) * p.N + qpos) * p.Hq + hq;
-      __bf16* orow = p.o_buf + obase * D;
-#pragma unroll
-      for (int dt = 0; dt < SH::DT; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = 32 * dt + 8 * jj + 4 * h2;
-          bf16x4 v4 = {(__bf16)(oacc[dt][4 * jj + 0] * inv), (__bf16)(oacc[dt][4 * jj + 1] * inv),
-                       (__bf16)(oacc[dt][4 * jj + 2] * inv), (__bf16)(oacc[dt][4 * jj + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(orow + d) = v4;
-        }
-      if (h2 == 0) p.lse_buf[obase] = (l_exact > 0.f) ? (m_use + __log2f(l_exact)) * kLn2 : -INFINITY;
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
 // K1 on 16x16x32 MFMAs.  One workgroup of 8 waves per chunk stages the
 // block's K and V tiles (BK x D) in LDS once; every wave then walks its own
 // 16-row tiles of the chunk's flat (edge, head) row list -- with G = 16 one

@@ -327,13 +327,16 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
   const int64_t nrows = (int64_t)(e1 - e0) * G;
   const int ntile = (int)((nrows + 15) / 16);
   const __bf16* __restrict__ qbase = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB;
+  // flat row f = edge * G + head; shifts when G is a power of two (uniform)
+  const int lg_g = ((G & (G - 1)) == 0) ? __builtin_ctz(G) : -1;
   auto row_of = [&](int t, int2 ed) {
     const int64_t f = min((int64_t)t * 16 + jl, nrows - 1);
-    return K1Row{ed.x, ed.y, r * G + (int)(f % G)};
+    const int head = (lg_g >= 0) ? (int)(f & (G - 1)) : (int)(f % G);
+    return K1Row{ed.x, ed.y, r * G + head};
   };
   auto edge_of = [&](int t) {
     const int64_t f = min((int64_t)t * 16 + jl, nrows - 1);
-    return edges[e0 + f / G];
+    return edges[e0 + ((lg_g >= 0) ? (f >> lg_g) : f / G)];
   };
   auto load_q = [&](bf16x8* qop, const K1Row& rw) {
     const __bf16* qrow = qbase + (int64_t)rw.qpos * p.q_sN + (int64_t)rw.hq * p.q_sH;
@@ -417,18 +420,23 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
     __builtin_amdgcn_sched_barrier(0);  // keep the gathers here, ahead of the softmax
 
     // ---- single-pass softmax (log2 domain) with the causal / tail mask ----
-    const int64_t last = p.causal ? min((int64_t)rw.qpos, p.N - 1) : p.N - 1;
+    // keys [0, lim) of the block are visible to this row; the masking pass
+    // runs only when some row of the tile does not see the whole block
+    const int lim = p.causal ? (int)max((int64_t)0, min((int64_t)nkeys, (int64_t)rw.qpos - k0 + 1)) : nkeys;
+    if (__builtin_amdgcn_ballot_w64(lim < BK) != 0) {
+#pragma unroll
+      for (int kt = 0; kt < SH::KT; ++kt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int key = 16 * kt + 4 * g + x;
+          sacc[kt][x] = (key < lim) ? sacc[kt][x] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < SH::KT; ++kt)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int key = 16 * kt + 4 * g + x;
-        const bool ok = key < nkeys && k0 + key <= last;
-        const float v = ok ? sacc[kt][x] : -INFINITY;
-        sacc[kt][x] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int x = 0; x < 4; ++x) mx = fmaxf(mx, sacc[kt][x]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, xor32(mx));
     const float m_use = (mx == -INFINITY) ? 0.f : mx * p.scale_log2;
@@ -482,7 +490,10 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
     // ---- normalised partial and its log-sum-exp into the edge's slot ----
     // Lanes g and g^1 trade halves so that every lane writes 16 bytes: even g
     // writes channels 32m + 4g .. +7 of tile pair m, odd g channels
-    // 32m + 16 + 4(g-1) .. +7.
+    // 32m + 16 + 4(g-1) .. +7.  One row swap (v_permlane16_swap: the odd
+    // 16-lane rows of the first operand trade with the even rows of the
+    // second) does the exchange: afterwards an even row holds (its v0, the
+    // odd row's v0) and an odd row (the even row's v1, its v1).
     const float inv = (rs > 0.f) ? 1.f / rs : 0.f;
     pend_obase = (((int64_t)b * p.ks + rw.slot) * p.N + rw.qpos) * p.Hq + rw.hq;
 #pragma unroll
@@ -491,13 +502,10 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
                          (__bf16)(oacc[2 * m][2] * inv), (__bf16)(oacc[2 * m][3] * inv)};
       const bf16x4 v1 = {(__bf16)(oacc[2 * m + 1][0] * inv), (__bf16)(oacc[2 * m + 1][1] * inv),
                          (__bf16)(oacc[2 * m + 1][2] * inv), (__bf16)(oacc[2 * m + 1][3] * inv)};
-      const bool odd = (g & 1) != 0;
-      const uint2 send = __builtin_bit_cast(uint2, odd ? v0 : v1);
-      uint2 recv;
-      recv.x = (uint32_t)__shfl_xor((int)send.x, 16, 64);
-      recv.y = (uint32_t)__shfl_xor((int)send.y, 16, 64);
-      const uint2 mine = __builtin_bit_cast(uint2, odd ? v1 : v0);
-      pend[m] = odd ? u32x4{recv.x, recv.y, mine.x, mine.y} : u32x4{mine.x, mine.y, recv.x, recv.y};
+      const uint2 a = __builtin_bit_cast(uint2, v0), c = __builtin_bit_cast(uint2, v1);
+      const auto sx = __builtin_amdgcn_permlane16_swap(a.x, c.x, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(a.y, c.y, false, false);
+      pend[m] = u32x4{sx[0], sy[0], sx[1], sy[1]};
     }
     pend_lse = (rsx > 0.f) ? (m_use + __log2f(rsx)) * kLn2 : -INFINITY;
     return ed_far;

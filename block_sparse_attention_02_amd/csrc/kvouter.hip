@@ -265,7 +265,9 @@ __global__ __launch_bounds__(1024) void kv_index_kernel(KvOuterParams p, int NB,
 //   O^T (D x 16 rows)       = V^T P^T   v_mfma_f32_16x16x32_bf16
 // Lane l owns row l%16 and keys 16kt + 4(l/16) + i of S^T; the 8 weights of
 // a 32-key step are the B operand of the PV product as they lie (V rows are
-// read in the matching order).  The next tile's query rows are loaded into
+// read in the matching order).  K and V rows are padded in LDS (K by 16
+// bytes, V by 32) rather than swizzled: both reads are then bank-conflict
+// free and every operand address is a per-lane base plus a constant.  The next tile's query rows are loaded into
 // the operand registers right after the QK^T product that frees them, the
 // edge list two tiles ahead, so the gathers overlap the softmax and PV.
 // ----------------------------------------------------------------------------
@@ -273,18 +275,31 @@ template <int D, int BK>
 struct K1w {
   static constexpr int NW = 8;                     // waves per workgroup
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int LPT = BK * CPR / (64 * NW); // staging copies per lane per tensor
   static constexpr int KT = BK / 16;               // 16-key tiles of S^T
   static constexpr int KS = D / 32;                // 32-channel k-steps of QK^T
   static constexpr int DT = D / 16;                // 16-channel tiles of O^T
   static constexpr int US = BK / 32;               // 32-key k-steps of PV
-  static_assert(LPT >= 1 && KT % 2 == 0 && DT % 2 == 0, "K1 shape");
+  static constexpr int KSE = D + 8;                // K row stride in LDS (elements)
+  static constexpr int VSE = D + 16;               // V row stride in LDS (elements)
+  static constexpr int SK = CPR + 1, SV = CPR + 2; // 16-byte slots per padded row
+  static constexpr int NIK = BK * SK / 64;         // staging copies (64 slots each)
+  static constexpr int NIV = BK * SV / 64;
+  static_assert(KT % 2 == 0 && DT % 2 == 0 && (BK * SK) % 64 == 0 && (BK * SV) % 64 == 0, "K1 shape");
 };
 
-// 16-byte chunk c of row r sits at physical chunk c ^ (r % 16).
+// Stage a block's rows into an LDS tile of `slots` 16-byte slots per row:
+// copy ii (of ni, spread over the waves) fills the 64 consecutive slots
+// [64 ii, 64 ii + 64); a slot maps back to (row, chunk), and slots in a row's
+// padding copy chunk 0 (never read).
 template <int CPR>
-__device__ __forceinline__ int k1w_swz(int r, int c) {
-  return c ^ (r & (CPR >= 16 ? 15 : CPR - 1));
+__device__ __forceinline__ void k1_stage(const __bf16* src, int64_t row_stride, int64_t k0, int nkeys, __bf16* lds,
+                                         int slots, int ni, int w, int nw, int lane) {
+  for (int ii = w; ii < ni; ii += nw) {
+    const int sl = ii * 64 + lane;
+    const int row = sl / slots, c = sl % slots;
+    const int64_t pos = k0 + min(row, nkeys - 1);
+    global_to_lds16(src + pos * row_stride + (c < CPR ? c : 0) * 8, lds + (size_t)ii * 64 * 8);
+  }
 }
 
 // Edge and head of flat row f of a chunk (G heads per edge).
@@ -297,8 +312,8 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
                                                      const int4* __restrict__ chunks, const int2* __restrict__ edges) {
   using SH = K1w<D, BK>;
   constexpr int CPR = SH::CPR;
-  __shared__ __align__(1024) __bf16 Ks[BK * D];
-  __shared__ __align__(1024) __bf16 Vs[BK * D];
+  __shared__ __align__(1024) __bf16 Ks[BK * SH::KSE];
+  __shared__ __align__(1024) __bf16 Vs[BK * SH::VSE];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, jl = lane & 15;
   if ((int)blockIdx.x >= *nchunk) return;
@@ -313,14 +328,8 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
 
   const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + r * p.kv_sH;
   const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + r * p.kv_sH;
-#pragma unroll
-  for (int kk = 0; kk < SH::LPT; ++kk) {
-    const int cidx = (kk * SH::NW + w) * 64 + lane;
-    const int row = cidx / CPR, pc = cidx % CPR;
-    const int64_t pos = k0 + min(row, nkeys - 1);
-    global_to_lds16(kg + pos * p.kv_sN + k1w_swz<CPR>(row, pc) * 8, Ks + (size_t)(kk * SH::NW + w) * 64 * 8);
-    global_to_lds16(vg + pos * p.kv_sN + k1w_swz<CPR>(row, pc) * 8, Vs + (size_t)(kk * SH::NW + w) * 64 * 8);
-  }
+  k1_stage<CPR>(kg, p.kv_sN, k0, nkeys, Ks, SH::SK, SH::NIK, w, SH::NW, lane);
+  k1_stage<CPR>(vg, p.kv_sN, k0, nkeys, Vs, SH::SV, SH::NIV, w, SH::NW, lane);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
         if (x < NQ) {
           const int kt = x / SH::KS, s = x % SH::KS;
           const int krow = 16 * kt + jl;
-          ka[x] = *reinterpret_cast<const bf16x8*>(Ks + krow * D + k1w_swz<CPR>(krow, 4 * s + g) * 8);
+          ka[x] = *reinterpret_cast<const bf16x8*>(Ks + krow * SH::KSE + (4 * s + g) * 8);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         if (x >= PF) {
@@ -471,11 +480,11 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
       for (int x = 0; x < NV + PF; ++x) {
         if (x < NV) {
           const int u = x / SH::DT, dt = x % SH::DT;
-          const int c = 2 * dt + ((jl & 3) >> 1), off = 4 * (jl & 1);
+          const int col = 16 * dt + 4 * (jl & 3);
           const int r0 = 32 * u + 4 * g + (jl >> 2);
           const int r1 = r0 + 16;
-          const bf16x4 lo = lds_read_tr16(Vs + r0 * D + k1w_swz<CPR>(r0, c) * 8 + off);
-          const bf16x4 hi = lds_read_tr16(Vs + r1 * D + k1w_swz<CPR>(r1, c) * 8 + off);
+          const bf16x4 lo = lds_read_tr16(Vs + r0 * SH::VSE + col);
+          const bf16x4 hi = lds_read_tr16(Vs + r1 * SH::VSE + col);
           va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
@@ -523,7 +532,7 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
 
 template <int D, int BK>
 static hipError_t launch_k1(const KvOuterParams& p, int NB, const KvLayout& L, char* ws, hipStream_t s) {
-  kv_k1w_kernel<D, BK><<<dim3(L.max_chunks), dim3(512), 0, s>>>(
+  kv_k1w_kernel<D, BK><<<dim3(L.max_chunks), dim3(64 * K1w<D, BK>::NW), 0, s>>>(
       p, NB, reinterpret_cast<const int32_t*>(ws + L.off_nchunk), reinterpret_cast<const int4*>(ws + L.off_chunks),
       reinterpret_cast<const int2*>(ws + L.off_edges));
   return hipGetLastError();

@@ -571,9 +571,9 @@ hipError_t launch_kvouter(const KvOuterParams& p, void* wsv, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// K2: one workgroup per (b, position); thread handles 8 channels of one head.
+// K2: one workgroup per (b, position); a thread handles 8 channels of one head.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kv_combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(1024) void kv_combine_kernel(CombineParams p) {
   constexpr int SB = 8;  // slots per batch: their loads are all in flight together
   const int64_t bi = blockIdx.x;
   const int64_t i = bi % p.N;
@@ -581,49 +581,50 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(CombineParams p) {
   const int G = p.Hq / p.Hkv;
   const int cpr = p.D / 8;
   const int64_t sstride = p.N * p.Hq;  // rows between consecutive slots
-  for (int c = threadIdx.x; c < p.Hq * cpr; c += 256) {
+  for (int c = threadIdx.x; c < p.Hq * cpr; c += blockDim.x) {
     const int hq = c / cpr, dc = c % cpr;
     const int n = min(p.nslot[((int64_t)b * p.N + i) * p.Hkv + hq / G], p.ks);
     const int64_t row0 = ((int64_t)b * p.ks * p.N + i) * p.Hq + hq;
-    // a = max_s L_s, z = sum_s exp(L_s - a)
-    float a = -INFINITY;
+    // One pass over the slots, SB at a time with all their loads in flight:
+    // running maximum m, z = sum_s exp(L_s - m), acc = sum_s exp(L_s - m) O_s,
+    // rescaled when m grows; then L = m + log z and O = acc / z, which is the
+    // section's merge with weights exp(L_s - L).
+    float m = -INFINITY, z = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n; s0 += SB) {
+      bf16x8 o[SB];
       float l[SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) l[u] = (s0 + u < n) ? p.lse_buf[row0 + (s0 + u) * sstride] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < SB; ++u) a = fmaxf(a, l[u]);
-    }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = -INFINITY;
-    if (n > 0 && a != -INFINITY) {
-      float z = 0.f;
-      for (int s0 = 0; s0 < n; s0 += SB) {
-        float l[SB];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) l[u] = (s0 + u < n) ? p.lse_buf[row0 + (s0 + u) * sstride] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < SB; ++u) z += __expf(l[u] - a);
+      for (int u = 0; u < SB; ++u) {
+        const int64_t row = row0 + (int64_t)min(s0 + u, n - 1) * sstride;
+        o[u] = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
+        l[u] = p.lse_buf[row];
       }
-      L = a + __logf(z);
-      for (int s0 = 0; s0 < n; s0 += SB) {
-        bf16x8 o[SB];
-        float l[SB];
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const bool ok = s0 + u < n;
-          const int64_t row = row0 + (int64_t)min(s0 + u, n - 1) * sstride;
-          o[u] = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
-          l[u] = ok ? p.lse_buf[row] : -INFINITY;
-        }
+      for (int u = 0; u < SB; ++u)
+        if (s0 + u >= n) l[u] = -INFINITY;  // the batch's padding slots
+      float bm = l[0];
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const float wgt = __expf(l[u] - L);  // 0 for the batch's padding slots
+      for (int u = 1; u < SB; ++u) bm = fmaxf(bm, l[u]);
+      const float m_new = fmaxf(m, bm);
+      if (m_new == -INFINITY) continue;  // nothing visible yet
+      const float scale = __expf(m - m_new);  // 0 while m is -inf
+      z *= scale;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[u][e];
-        }
+      for (int e = 0; e < 8; ++e) acc[e] *= scale;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const float wgt = __expf(l[u] - m_new);
+        z += wgt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[u][e];
       }
+      m = m_new;
     }
+    const float inv = (z > 0.f) ? 1.f / z : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    const float L = (z > 0.f) ? m + __logf(z) : -INFINITY;
     bf16x8 out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (__bf16)acc[e];
@@ -633,7 +634,10 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  kv_combine_kernel<<<dim3((unsigned)(p.B * p.N)), dim3(256), 0, s>>>(p);
+  // one (head, 8-channel chunk) item per thread when it fits
+  const int items = p.Hq * (p.D / 8);
+  const int threads = std::min(1024, (items + 63) / 64 * 64);
+  kv_combine_kernel<<<dim3((unsigned)(p.B * p.N)), dim3(threads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@ it is written directly from the source pages:
   branch with externally supplied block indices/counts and GQA.
 * "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top) -- the
   K1 local partials and the exact LSE combine of the KV-outer schedule.
+* "深度解读|Spark-H3：从注意力几何到稀疏内核代码" (jefxiong.cn) -- the
+  Spark-Reweight block summaries and the joint softmax of exact tokens and
+  virtual tokens.
 
 Every function computes the plain definition in float64 with NumPy: no online
 softmax, no blocking, no reverse index.  Each one is pinned by the ``not gpu``
@@ -28,6 +31,7 @@ from .attention import (
     kvouter_partials,
     lse_combine,
 )
+from .reweight import anchor_queries, block_summaries, virtual_logit, reweight_attention
 
 __all__ = [
     "tile_dims",
@@ -37,6 +41,10 @@ __all__ = [
     "routing_matrix",
     "select_topk",
     "vsa_attention",
+    "anchor_queries",
+    "block_summaries",
+    "virtual_logit",
+    "reweight_attention",
     "nsa_attention",
     "kvouter_partials",
     "lse_combine",

@@ -14,6 +14,7 @@ from .api import (
     pool_route_topk,
     route_workspace_bytes,
     attention_vsa,
+    spark_summaries,
     attention_nsa,
     kvouter,
     combine,
@@ -31,6 +32,7 @@ __all__ = [
     "pool_route_topk",
     "route_workspace_bytes",
     "attention_vsa",
+    "spark_summaries",
     "attention_nsa",
     "kvouter",
     "combine",

@@ -58,7 +58,14 @@ class QOuterArgs(ctypes.Structure):
                 ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
                 ("q2k_idx", _p), ("q2k_num", _p), ("kmax", _i32),
                 ("blk_idx", _p), ("blk_cnt", _p), ("S", _i32), ("BS", _i32), ("causal", _i32),
-                ("lse", _p), ("item_order", _p)]
+                ("lse", _p), ("item_order", _p),
+                ("k_sum", _p), ("v_sum", _p), ("b_sum", _p)]
+
+
+class SummaryArgs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k", _p), ("v", _p), ("d", TDesc), ("dt", _i32),
+                ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32), ("scale", _f32),
+                ("anchor", _p), ("anchor_out", _p), ("k_sum", _p), ("v_sum", _p), ("b_sum", _p)]
 
 
 class KvOuterArgs(ctypes.Structure):
@@ -84,6 +91,8 @@ PROTOTYPES = {
     "vsa_pool_route_topk_ws": (_i32, [ctypes.POINTER(RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_pool_route_topk": (_i32, [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]),
     "bsa_forward_qouter": (_i32, [ctypes.POINTER(QOuterArgs), _p]),
+    "spark_summaries_ws": (_i32, [ctypes.POINTER(SummaryArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "spark_summaries": (_i32, [ctypes.POINTER(SummaryArgs), _p, ctypes.c_size_t, _p]),
     "bsa_kvouter_ws": (_i32, [ctypes.POINTER(KvOuterArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "bsa_forward_kvouter": (_i32, [ctypes.POINTER(KvOuterArgs), _p, ctypes.c_size_t, _p]),
     "bsa_combine": (_i32, [ctypes.POINTER(CombineArgs), _p]),

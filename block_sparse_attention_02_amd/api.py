@@ -140,10 +140,43 @@ def _qouter_args(q, k, v, out, scale, mode, lse):
                         dout=_desc(out), dt=_dtype(q), scale=scale, mode=mode, lse=_ptr(lse))
 
 
+def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, need_anchor=False):
+    """Spark-Reweight block summaries: bf16 k_sum, v_sum [B, H, J, D] and fp32
+    b_sum [B, H, J] (plus the fp32 anchor [B, H, D] with ``need_anchor``).
+    ``anchor``: optional fp32 [B, H, D] representative queries (default: the
+    mean of q over all tokens of each head)."""
+    _need_cuda(k, v, perm, block_len)
+    if k.stride() != v.stride() or k.shape != v.shape or (q is not None and (q.stride() != k.stride()
+                                                                               or q.shape != k.shape)):
+        raise ValueError("q, k and v must share shape and strides")
+    B, N, H, D = k.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = k.device
+    k_sum = torch.empty((B, H, J, D), dtype=torch.bfloat16, device=dev)
+    v_sum = torch.empty((B, H, J, D), dtype=torch.bfloat16, device=dev)
+    b_sum = torch.empty((B, H, J), dtype=torch.float32, device=dev)
+    anchor_out = torch.empty((B, H, D), dtype=torch.float32, device=dev) if need_anchor else None
+    if anchor is not None:
+        _need_cuda(anchor)
+        if anchor.dtype != torch.float32 or anchor.numel() != B * H * D or not anchor.is_contiguous():
+            raise ValueError("anchor must be a contiguous float32 tensor of B*H*D elements")
+    a = L.SummaryArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), d=_desc(k), dt=_dtype(k), perm=_ptr(perm),
+                      block_len=_ptr(block_len), J=J, M=M, scale=scale, anchor=_ptr(anchor),
+                      anchor_out=_ptr(anchor_out), k_sum=_ptr(k_sum), v_sum=_ptr(v_sum), b_sum=_ptr(b_sum))
+    lib = _lib()
+    nbytes = ctypes.c_size_t(0)
+    L.check(lib.spark_summaries_ws(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev) if nbytes.value else None
+    L.check(lib.spark_summaries(ctypes.byref(a), _ptr(ws), nbytes.value, _stream(dev)))
+    return (k_sum, v_sum, b_sum, anchor_out) if need_anchor else (k_sum, v_sum, b_sum)
+
+
 def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
-                  item_order=None):
+                  item_order=None, summaries=None):
     """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
-    ``item_order``: optional processing order (from pool_route_topk)."""
+    ``item_order``: optional processing order (from pool_route_topk).
+    ``summaries``: optional (k_sum, v_sum, b_sum) from spark_summaries; every
+    block a query block does not keep then enters through its virtual token."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -159,6 +192,14 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
         if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
             raise ValueError("item_order must be a contiguous int32 tensor of B*H*J elements")
         a.item_order = _ptr(item_order)
+    if summaries is not None:
+        k_sum, v_sum, b_sum = summaries
+        _need_cuda(k_sum, v_sum, b_sum)
+        if (k_sum.dtype != torch.bfloat16 or v_sum.dtype != torch.bfloat16 or b_sum.dtype != torch.float32
+                or k_sum.numel() != B * H * J * D or v_sum.numel() != B * H * J * D or b_sum.numel() != B * H * J
+                or not (k_sum.is_contiguous() and v_sum.is_contiguous() and b_sum.is_contiguous())):
+            raise ValueError("summaries must be contiguous bf16 [B,H,J,D] k_sum/v_sum and float32 [B,H,J] b_sum")
+        a.k_sum, a.v_sum, a.b_sum = _ptr(k_sum), _ptr(v_sum), _ptr(b_sum)
     L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
     return (out, lse) if need_lse else out
 

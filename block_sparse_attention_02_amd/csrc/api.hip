@@ -193,12 +193,21 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block capacity M must be 16, 32 or 64");
     if ((int64_t)a->dq.B * a->dq.H * a->J >= (int64_t)1 << 31)
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks");
+    if (a->k_sum || a->v_sum || a->b_sum) {
+      if (!a->k_sum || !a->v_sum || !a->b_sum)
+        return fail(BSA_ERR_ARG, "bsa_forward_qouter: k_sum, v_sum and b_sum go together");
+      if (a->dt != BSA_BF16 || a->M != 64)
+        return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: summaries need bf16 and block capacity 64");
+      if (a->J > 4096) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: summaries need J <= 4096");
+      if (!aligned16(a->k_sum) || !aligned16(a->v_sum) || (reinterpret_cast<uintptr_t>(a->b_sum) & 3))
+        return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: k_sum/v_sum must be 16-byte and b_sum 4-byte aligned");
+    }
     bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
                          a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
                          a->dout.sB, a->dout.sN, a->dout.sH,
                          a->perm, a->block_len, a->q2k_idx, a->q2k_num,
                          (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
-                         scale_log2, a->lse, a->item_order};
+                         scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum};
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   if (a->mode == BSA_SEL_TOKEN) {
@@ -219,6 +228,67 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
     return hip_status(bsa::launch_nsa_attention(p, false, s), "nsa attention launch");
   }
   return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
+}
+
+// ------------------------------------------------------------ Spark-Reweight summaries
+static bsa_status check_summaries(const spark_summary_args* a) {
+  if (!a) return fail(BSA_ERR_ARG, "spark_summaries: null args");
+  if (!a->k || !a->v || !a->perm || !a->block_len || !a->k_sum || !a->v_sum || !a->b_sum)
+    return fail(BSA_ERR_ARG, "spark_summaries: k, v, perm, block_len, k_sum, v_sum and b_sum are required");
+  if (!a->anchor && !a->q) return fail(BSA_ERR_ARG, "spark_summaries: q is required when anchor is NULL");
+  if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "spark_summaries: bf16 only");
+  bsa_status st = check_desc(a->d, "q/k/v", 8, true);
+  if (st != BSA_OK) return st;
+  if (a->d.D != 64 && a->d.D != 128) return fail(BSA_ERR_UNSUPPORTED, "spark_summaries: D must be 64 or 128");
+  if (a->J < 1 || a->M < 1 || a->M > 64)
+    return fail(BSA_ERR_SHAPE, "spark_summaries: J must be positive and M in [1, 64]");
+  if ((int64_t)a->d.B * a->d.H * a->J >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "spark_summaries: too many blocks");
+  if (a->d.N >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "spark_summaries: N must be below 2^31");
+  if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "spark_summaries: scale must be finite");
+  if (!aligned16(a->k) || !aligned16(a->v) || (a->q && !aligned16(a->q)) || !aligned16(a->k_sum) ||
+      !aligned16(a->v_sum))
+    return fail(BSA_ERR_SHAPE, "spark_summaries: q, k, v, k_sum, v_sum must be 16-byte aligned");
+  return BSA_OK;
+}
+
+bsa_status spark_summaries_ws(const spark_summary_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "spark_summaries_ws: null output");
+  bsa_status st = check_summaries(a);
+  if (st != BSA_OK) return st;
+  *bytes = 0;
+  if (!a->anchor) {
+    *bytes += round_up(bsa::anchor_workspace_bytes((int)a->d.B, (int)a->d.N, (int)a->d.H, (int)a->d.D));
+    if (!a->anchor_out) *bytes += round_up((size_t)a->d.B * a->d.H * a->d.D * sizeof(float));
+  }
+  return ok();
+}
+
+bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  bsa_status st = spark_summaries_ws(a, &need);
+  if (st != BSA_OK) return st;
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "spark_summaries: workspace of %zu bytes required", need);
+  hipStream_t s = (hipStream_t)stream;
+  const int B = (int)a->d.B, N = (int)a->d.N, H = (int)a->d.H, D = (int)a->d.D;
+  const float* anchor = a->anchor;
+  if (!anchor) {
+    char* w = static_cast<char*>(ws);
+    float* part = reinterpret_cast<float*>(w);
+    w += round_up(bsa::anchor_workspace_bytes(B, N, H, D));
+    float* anc = a->anchor_out ? a->anchor_out : reinterpret_cast<float*>(w);
+    hipError_t e = bsa::launch_anchor(a->q, a->d.sB, a->d.sN, a->d.sH, B, N, H, D, part, anc, s);
+    if (e != hipSuccess) return hip_status(e, "anchor launch");
+    anchor = anc;
+  } else if (a->anchor_out) {
+    hipError_t e = hipMemcpyAsync(a->anchor_out, a->anchor, (size_t)B * H * D * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_status(e, "anchor copy");
+  }
+  bsa::SummaryParams sp{a->k, a->v, a->d.sB, a->d.sN, a->d.sH, B, H, D, a->J, a->M,
+                        a->perm, a->block_len, anchor, a->scale, a->k_sum, a->v_sum, a->b_sum};
+  return hip_status(bsa::launch_summaries(sp, s), "summary launch");
 }
 
 // ------------------------------------------------------------------------ KV-outer

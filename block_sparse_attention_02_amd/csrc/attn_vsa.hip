@@ -29,6 +29,8 @@
 namespace bsa {
 
 constexpr int kMaxRounds = 4096;
+// Kept-block bitmask words of the summary mode (J <= 32 * kSumMaskWords).
+constexpr int kSumMaskWords = 128;
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -633,9 +635,9 @@ __device__ __forceinline__ void stage4(i32x4 rsrc, uint32_t lds_base, const uint
     buffer_to_lds16(rsrc, rowoff[k] + chunkoff[k], lds_base + (uint32_t)((w * TM::LPT + k) * 1024));
 }
 
-template <int D, bool LSE>
+template <int D, bool LSE, bool SUM>
 __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __bf16* KV, int* Ids, float* Mx,
-                                          Balance& bal) {
+                                          Balance& bal, uint32_t* Kept, float* Bsum) {
   using TM = Tile4<D>;
   constexpr int LPT = TM::LPT, CPR = TM::CPR;
   constexpr int KS = D / 16;   // k-steps of QK^T
@@ -669,6 +671,36 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const auto blen = as_const(p.block_len);
   const int num = min(as_const(p.q2k_num)[bh * p.J + i], p.kmax);
   const int ni = blen[i];
+
+  // Spark-Reweight summaries: after the kept blocks come ceil(J/64) tiles of
+  // 64 virtual tokens (summary key, value and bias of blocks 64*tau ..);
+  // those of kept blocks and those past J are masked.  Kept holds the kept
+  // list as a bitmask, Bsum the biases of the next tile (one 64-entry buffer
+  // per wave and parity).
+  const int ns = SUM ? (p.J + 63) / 64 : 0;
+  const int T = num + ns;
+  i32x4 ksrs = krs, vsrs = vrs, bsrs = prs;
+  const float bias_mul = 1.4426950408889634f / p.scale_log2;  // 1 / scale
+  auto bs_lds = [&](int x) { return lds_offset(Bsum + (x * 4 + w) * 64); };
+  if constexpr (SUM) {
+    const uint32_t sbytes = (uint32_t)p.J * (uint32_t)(D * 2);
+    ksrs = make_rsrc(reinterpret_cast<const __bf16*>(p.k_sum) + bh * p.J * D, sbytes);
+    vsrs = make_rsrc(reinterpret_cast<const __bf16*>(p.v_sum) + bh * p.J * D, sbytes);
+    bsrs = make_rsrc(p.b_sum + bh * p.J, (uint32_t)p.J * 4u);
+    for (int x = threadIdx.x; x < kSumMaskWords; x += blockDim.x) Kept[x] = 0u;
+    __syncthreads();
+    for (int pp = threadIdx.x; pp < num; pp += blockDim.x) {
+      const int j = p.q2k_idx[(bh * p.J + i) * p.kmax + pp];
+      if (j >= 0 && j < p.J) atomicOr(&Kept[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+  }
+  // byte offsets of the summary rows this lane copies for summary tile tau
+  auto sum_rows = [&](uint32_t* r, int tau) {
+#pragma unroll
+    for (int k = 0; k < TM::LPT; ++k)
+      r[k] = (uint32_t)min(64 * tau + 16 * w + TM::LPT * (lane / TM::CPR) + k, p.J - 1) * (uint32_t)(D * 2);
+  };
 
   uint32_t koff[LPT], voff[LPT];
 #pragma unroll
@@ -710,12 +742,21 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
     j1 = sel[min(1, num - 1)];
     j2 = sel[min(2, num - 1)];
     stage_ids(prs, max(j1, 0), M, ids_lds, lane);
+  } else if constexpr (SUM) {
+    if (T > 0) {  // no kept block: the first tile is summary tile 0
+      sum_rows(rows, 0);
+      stage4<D>(ksrs, kbuf(0), rows, koff, w);
+      stage4<D>(vsrs, vbuf(0), rows, voff, w);
+    }
+  }
+  if constexpr (SUM) {
+    if (T > 0) stage_ids(bsrs, max(-num, 0), 64, bs_lds(0), lane);  // biases of tile 0 if it is a summary tile
   }
 
-  constexpr int NCOPY = 2 * LPT + 1;  // K and V copies of the next block, then ids
+  constexpr int NCOPY = 2 * LPT + 1 + (SUM ? 1 : 0);  // K and V of the next tile, ids, biases
   static_assert(NCOPY <= KS + PF, "copies are spread over the QK^T steps");
   uint32_t partner_seen = 0;  // partner count, read one block before it is used
-  for (int t = 0; t < num; ++t) {
+  for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
     wait_vmcnt<0>();  // K(t), V(t) and ids(t+1) resident
     BSA_BARRIER();    // every wave's copies visible; every wave done with t-1
@@ -736,7 +777,12 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
     }
     // Rows of block t+1 (for the last block: the same block again, a
     // harmless extra copy into the idle buffer).
-    tile_rows4<D>(rows, ids, w, lane, row_bytes);
+    const bool next_sum = SUM && t + 1 >= num;
+    if (next_sum)
+      sum_rows(rows, t + 1 - num);
+    else
+      tile_rows4<D>(rows, ids, w, lane, row_bytes);
+    const i32x4 ckr = next_sum ? ksrs : krs, cvr = next_sum ? vsrs : vrs;
     const __bf16* Kc = KV + cur * 2 * TILE;
     const __bf16* Vc = Kc + TILE;
 
@@ -759,11 +805,13 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
         if (s < LPT) {
-          buffer_to_lds16(krs, rows[s] + koff[s], kbuf(cur ^ 1) + (uint32_t)((w * LPT + s) * 1024));
+          buffer_to_lds16(ckr, rows[s] + koff[s], kbuf(cur ^ 1) + (uint32_t)((w * LPT + s) * 1024));
         } else if (s < 2 * LPT) {
-          buffer_to_lds16(vrs, rows[s - LPT] + voff[s - LPT], vbuf(cur ^ 1) + (uint32_t)((w * LPT + s - LPT) * 1024));
+          buffer_to_lds16(cvr, rows[s - LPT] + voff[s - LPT], vbuf(cur ^ 1) + (uint32_t)((w * LPT + s - LPT) * 1024));
         } else if (s == 2 * LPT) {
           stage_ids(prs, max(j2, 0), M, ids_lds, lane);  // near the end: a harmless repeat
+        } else if (SUM && s == 2 * LPT + 1) {
+          stage_ids(bsrs, max(t + 1 - num, 0), 64, bs_lds(cur ^ 1), lane);
         }
       }
     }
@@ -771,11 +819,25 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
     // scalar table reads for the coming blocks (no LDS result is awaited
     // until the barrier that opens the next block)
     __builtin_amdgcn_sched_barrier(0);
-    const int j3 = sel[min(t + 3, num - 1)];
+    const int j3 = sel[max(0, min(t + 3, num - 1))];
     njn = (j1 >= 0) ? blen[max(j1, 0)] : 0;
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax (log2 domain); lane owns query 32hq + l%32 ----
+    if constexpr (SUM) {
+      if (t >= num) {  // virtual tokens: add the bias, mask kept blocks and rows past J
+        const int tau = t - num;
+        const float* bsm = Bsum + (cur * 4 + w) * 64;
+        const uint32_t m0 = Kept[2 * tau], m1 = Kept[2 * tau + 1];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
+          const uint32_t bit = ((key < 32 ? m0 : m1) >> (key & 31)) & 1u;
+          sacc[r] = (64 * tau + key < p.J && bit == 0u) ? sacc[r] + bsm[key] * bias_mul : -INFINITY;
+        }
+        nj = M;
+      }
+    }
     if (nj < M) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -903,13 +965,15 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   }
 }
 
-template <int D, bool LSE>
+template <int D, bool LSE, bool SUM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa4_kernel(VsaAttnParams p,
                                                                                              int items, int sync) {
   __shared__ __align__(1024) __bf16 KV[4 * 64 * D];  // 2 buffers x (K, V)
   __shared__ __align__(256) int Ids[4 * 64];         // token ids, one buffer per wave
   __shared__ float Mx[2 * 3 * 64];                   // merge: max, rounded sum, exact sum
   __shared__ uint32_t slot_sh[2];
+  __shared__ uint32_t Kept[SUM ? kSumMaskWords : 1];      // kept blocks of the query block (summaries)
+  __shared__ __align__(256) float Bsum[SUM ? 2 * 4 * 64 : 1];  // biases of a summary tile, per parity and wave
   Balance bal;
   Cohort coh;
   if (sync) {
@@ -918,7 +982,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   int wid = sync ? next_item(coh.xcc, items, slot_sh) : (int)blockIdx.x;
   while (wid >= 0 && wid < items) {
-    vsa4_item<D, LSE>(p, wid, KV, Ids, Mx, bal);
+    vsa4_item<D, LSE, SUM>(p, wid, KV, Ids, Mx, bal, Kept, Bsum);
     if (sync) {
       cohort_sync(coh);
       wid = next_item(coh.xcc, items, slot_sh);
@@ -1029,23 +1093,24 @@ static hipError_t launch_vsa_mt(const VsaAttnParams& p, hipStream_t s) {
   return p.lse ? launch_vsa_lse<D, MT, true>(p, s) : launch_vsa_lse<D, MT, false>(p, s);
 }
 
-template <int D, bool LSE>
+template <int D, bool LSE, bool SUM>
 static hipError_t launch_vsa4(const VsaAttnParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.B * p.H * p.J;
   static int64_t cache[64] = {0};
-  const int64_t resident = resident_groups(vsa4_kernel<D, LSE>, 256, cache);
+  const int64_t resident = resident_groups(vsa4_kernel<D, LSE, SUM>, 256, cache);
   const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
   const int64_t rounds = (items + grid - 1) / grid;
   const int sync = (rounds > 1) ? 1 : 0;
   if (sync) clear_rounds_kernel<<<32, 256, 0, s>>>(0);
-  vsa4_kernel<D, LSE><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p, (int)items, sync);
+  vsa4_kernel<D, LSE, SUM><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p, (int)items, sync);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_vsa_d(const VsaAttnParams& p, hipStream_t s) {
   if (p.M <= 32) return launch_vsa_mt<D, 32>(p, s);
-  return p.lse ? launch_vsa4<D, true>(p, s) : launch_vsa4<D, false>(p, s);
+  if (p.k_sum) return p.lse ? launch_vsa4<D, true, true>(p, s) : launch_vsa4<D, false, true>(p, s);
+  return p.lse ? launch_vsa4<D, true, false>(p, s) : launch_vsa4<D, false, false>(p, s);
 }
 
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s) {

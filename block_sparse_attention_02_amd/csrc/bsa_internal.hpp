@@ -43,6 +43,27 @@ hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
 hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,
                              int32_t* order, hipStream_t s);
 
+// ---- Spark-Reweight summaries -------------------------------------------------
+struct SummaryParams {
+  const void* k;
+  const void* v;
+  int64_t sB, sN, sH;
+  int B, H, D, J, M;
+  const int32_t* perm;
+  const int32_t* block_len;
+  const float* anchor;  // [B, H, D]
+  float scale;
+  void* k_sum;   // bf16 [B, H, J, D]
+  void* v_sum;   // bf16 [B, H, J, D]
+  float* b_sum;  // [B, H, J]
+};
+// Partial-sum buffer of the anchor reduction (bytes).
+size_t anchor_workspace_bytes(int B, int N, int H, int D);
+// anchor[b, h, :] = mean over the N tokens of q[b, :, h, :] (bf16 input).
+hipError_t launch_anchor(const void* q, int64_t sB, int64_t sN, int64_t sH, int B, int N, int H, int D, float* part,
+                         float* anchor, hipStream_t s);
+hipError_t launch_summaries(const SummaryParams& p, hipStream_t s);
+
 // ---- query-outer attention -----------------------------------------------------
 struct VsaAttnParams {
   const void* q;
@@ -61,6 +82,10 @@ struct VsaAttnParams {
   float scale_log2;  // softmax scale * log2(e)
   float* lse;        // optional [B, H, N]
   const int32_t* order;  // optional [B, H, J] processing order of query blocks
+  // optional Spark-Reweight summaries (M = 64, bf16): [B, H, J, D] bf16 and [B, H, J]
+  const void* k_sum;
+  const void* v_sum;
+  const float* b_sum;
 };
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
 

@@ -15,6 +15,7 @@
  *   [VSA]  "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" (maple.link)
  *   [NSA]  "NSA 算子解析（Torch/Tilelang）" (devpress.csdn.net)
  *   [MSA]  "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top)
+ *   [Spark] "深度解读|Spark-H3：从注意力几何到稀疏内核代码" (jefxiong.cn)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -206,9 +207,60 @@ typedef struct {
   /* optional */
   float* lse;
   const int32_t* item_order;
+  /* optional, BSA_SEL_BLOCK: Spark-Reweight summaries from spark_summaries
+   * ([Spark] sections 03 and 08).  When set, every block j of (b, h) that no
+   * kept entry of query block i names adds one virtual token to the same
+   * softmax: logit scale * q . k_sum[b,h,j,:] + b_sum[b,h,j], value
+   * v_sum[b,h,j,:].  k_sum, v_sum bf16 [B, H, J, D] and b_sum fp32 [B, H, J],
+   * contiguous; all three or none.  Needs bf16, M = 64 and J <= 4096. */
+  const void* k_sum;
+  const void* v_sum;
+  const float* b_sum;
 } bsa_qouter_args;
 
 bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Spark-Reweight block summaries ([Spark] sections 07 and 08).
+ *
+ * For every batch b and head h, with the representative query
+ * a = anchor[b,h,:] (NULL: the mean of q[b,n,h,:] over all N tokens, computed
+ * here), and every block j of the tiling (its n_j tokens t = perm[j*M + r]):
+ *   s_r = scale * a . k_t,  p_r = exp(s_r) / sum_r exp(s_r),  l_j = log sum_r exp(s_r)
+ *   k_sum[b,h,j,:] = bf16(sum_r p_r k_t)      v_sum[b,h,j,:] = bf16(sum_r p_r v_t)
+ *   b_sum[b,h,j]   = l_j - scale * a . k_sum[b,h,j,:]   (with the stored bf16 key)
+ * so that a query q sees block j through one virtual token with logit
+ * scale * q . k_sum + b_sum and value v_sum; at q = a it carries the block's
+ * exact exponential mass and content.
+ *   q, k, v     bf16 [B, N, H, D] strided views sharing the descriptor d
+ *               (q is read only when anchor is NULL)
+ *   anchor      optional fp32 [B, H, D] contiguous input
+ *   anchor_out  optional fp32 [B, H, D] contiguous output: the anchor used
+ *   k_sum, v_sum bf16 [B, H, J, D] contiguous; b_sum fp32 [B, H, J] contiguous
+ * Supported: D in {64, 128}, 1 <= M <= 64, 16-byte aligned tensors.  The
+ * workspace (only when anchor is NULL) holds the partial sums of the anchor:
+ * spark_summaries_ws() bytes.  The anchor is reduced in a fixed order, so
+ * results are deterministic.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  bsa_tdesc d;
+  bsa_dtype dt;
+  const int32_t* perm;
+  const int32_t* block_len;
+  int J, M;
+  float scale;
+  const float* anchor;
+  float* anchor_out;
+  void* k_sum;
+  void* v_sum;
+  float* b_sum;
+} spark_summary_args;
+
+bsa_status spark_summaries_ws(const spark_summary_args* a, size_t* bytes);
+bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
  * KV-outer schedule ([MSA] sections 5-8).

@@ -82,8 +82,10 @@ def reweight_attention(Q, K, V, perm, block_len, M, q2k_idx, q2k_num, k_sum, v_s
     Q, K, V: [B, N, h, D] in the original token order; k_sum/v_sum [B, h, J, D]
     and bias [B, h, J] are the block summaries (any float dtype, upcast
     exactly).  Entry p of row (b, h, i) is kept iff p < q2k_num and
-    q2k_idx >= 0; a block listed twice counts once.  ``items`` optionally
-    restricts the work to (b, h, i) query blocks; other outputs are NaN.
+    q2k_idx >= 0; as in the exact path, the tokens of a kept entry count once
+    per listing.  Every block that no kept entry names adds its virtual token.
+    ``items`` optionally restricts the work to (b, h, i) query blocks; other
+    outputs are NaN.
 
     Returns O float64 [B, N, h, D] and LSE [B, h, N] (natural log).
     """
@@ -96,18 +98,18 @@ def reweight_attention(Q, K, V, perm, block_len, M, q2k_idx, q2k_num, k_sum, v_s
         items = [(b, hh, i) for b in range(B) for hh in range(h) for i in range(J)]
     for (b, hh, i) in items:
         queries = np.asarray(perm[i * M: i * M + int(block_len[i])])
-        kept = set()
+        kept = []
         for p in range(int(q2k_num[b, hh, i])):
             j = int(q2k_idx[b, hh, i, p])
             if j < 0:
                 continue
             if j >= J:
                 raise IndexError("block index out of range")
-            kept.add(j)
+            kept.append(j)
         q = Q[b, queries, hh, :].astype(np.float64)
         parts_s, parts_v = [], []
         if kept:
-            toks = np.concatenate([np.asarray(perm[j * M: j * M + int(block_len[j])]) for j in sorted(kept)])
+            toks = np.concatenate([np.asarray(perm[j * M: j * M + int(block_len[j])]) for j in kept])
             parts_s.append((q @ K[b, toks, hh, :].astype(np.float64).T) * scale)
             parts_v.append(V[b, toks, hh, :].astype(np.float64))
         rest = [j for j in range(J) if j not in kept]

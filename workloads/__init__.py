@@ -14,9 +14,10 @@ exactly the tensors the device computed on.
 """
 
 from .configs import WORKLOADS, workload, scaled
-from .gen import vsa_inputs, nsa_inputs, msa_inputs
+from .gen import vsa_inputs, nsa_inputs, msa_inputs, kept_lists
 
 __all__ = [
+    "kept_lists",
     "WORKLOADS",
     "workload",
     "scaled",

@@ -23,6 +23,7 @@ msa   q [B,N,Hq,D], k, v [B,N,Hkv,D] ~ N(0,1) -> bf16; per KV head a random
 
 import math
 
+import numpy as np
 import torch
 
 _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -59,6 +60,27 @@ def vsa_inputs(cfg, device="cpu"):
             del c, field
     dt = _DT[cfg["dtype"]]
     return {k_: v_.to(dt) for k_, v_ in out.items()}
+
+
+def kept_lists(B, h, J, kmax, seed, device="cpu"):
+    """Seeded kept lists for block-selected attention: q2k_idx int32
+    [B, h, J, kmax] (ascending, -1 fill) and q2k_num int32 [B, h, J].  Row
+    counts are uniform in [0, kmax]; row 0 of every (b, h) keeps nothing and
+    row 1 keeps min(kmax, J) blocks, so both extremes always occur."""
+    g = np.random.default_rng(seed)
+    idx = np.full((B, h, J, kmax), -1, dtype=np.int32)
+    num = np.zeros((B, h, J), dtype=np.int32)
+    for b in range(B):
+        for hh in range(h):
+            for i in range(J):
+                n = int(g.integers(0, min(kmax, J) + 1))
+                if i == 0:
+                    n = 0
+                elif i == 1:
+                    n = min(kmax, J)
+                idx[b, hh, i, :n] = np.sort(g.choice(J, size=n, replace=False))
+                num[b, hh, i] = n
+    return torch.from_numpy(idx).to(device), torch.from_numpy(num).to(device)
 
 
 def _sorted_padded(sel, limit):

@@ -810,8 +810,8 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
           buffer_to_lds16(cvr, rows[s - LPT] + voff[s - LPT], vbuf(cur ^ 1) + (uint32_t)((w * LPT + s - LPT) * 1024));
         } else if (s == 2 * LPT) {
           stage_ids(prs, max(j2, 0), M, ids_lds, lane);  // near the end: a harmless repeat
-        } else if (SUM && s == 2 * LPT + 1) {
-          stage_ids(bsrs, max(t + 1 - num, 0), 64, bs_lds(cur ^ 1), lane);
+        } else if (SUM && s == 2 * LPT + 1 && next_sum) {
+          stage_ids(bsrs, t + 1 - num, 64, bs_lds(cur ^ 1), lane);
         }
       }
     }
@@ -825,15 +825,16 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 
     // ---- online softmax (log2 domain); lane owns query 32hq + l%32 ----
     if constexpr (SUM) {
-      if (t >= num) {  // virtual tokens: add the bias, mask kept blocks and rows past J
+      if (t >= num) {  // virtual tokens: add the bias; kept blocks and rows past J get -inf
         const int tau = t - num;
-        const float* bsm = Bsum + (cur * 4 + w) * 64;
-        const uint32_t m0 = Kept[2 * tau], m1 = Kept[2 * tau + 1];
+        float* bsm = Bsum + (cur * 4 + w) * 64;
+        // this wave's own copy of the tile's biases: lane k marks entry k
+        const uint32_t word = Kept[2 * tau + (lane >> 5)];
+        if (((word >> (lane & 31)) & 1u) != 0u || 64 * tau + lane >= p.J) bsm[lane] = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
-          const uint32_t bit = ((key < 32 ? m0 : m1) >> (key & 31)) & 1u;
-          sacc[r] = (64 * tau + key < p.J && bit == 0u) ? sacc[r] + bsm[key] * bias_mul : -INFINITY;
+          sacc[r] = __builtin_fmaf(bsm[key], bias_mul, sacc[r]);
         }
         nj = M;
       }

@@ -16,6 +16,8 @@
 // front (K and V straight into registers), the logits are reduced across the
 // lanes of a row, and the weighted sums across the rows.  Memory bound: every
 // K and V row is read once.
+#include <algorithm>
+
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -23,7 +25,7 @@ namespace bsa {
 
 constexpr int kAnchorTok = 256;  // tokens per partial sum
 
-__global__ __launch_bounds__(256) void anchor_partial_kernel(const __bf16* __restrict__ q, int64_t sB, int64_t sN,
+__global__ __launch_bounds__(1024) void anchor_partial_kernel(const __bf16* __restrict__ q, int64_t sB, int64_t sN,
                                                              int64_t sH, int N, int H, int D,
                                                              float* __restrict__ part) {
   const int c = blockIdx.x, b = blockIdx.y, nc = gridDim.x;
@@ -45,14 +47,25 @@ __global__ __launch_bounds__(256) void anchor_partial_kernel(const __bf16* __res
   }
 }
 
-__global__ __launch_bounds__(256) void anchor_final_kernel(const float* __restrict__ part, int nc, int B, int H,
-                                                           int D, int N, float* __restrict__ anchor) {
-  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b*H + h)*D + d
-  if (x >= (int64_t)B * H * D) return;
-  const int64_t b = x / ((int64_t)H * D), hd = x % ((int64_t)H * D);
+// Anchor, stage 2: one workgroup per (b, h); group gi of 128 threads sums the
+// partials c = gi, gi + 8, ... of one channel each, then the 8 group sums are
+// added in order (fixed order: deterministic).
+__global__ __launch_bounds__(1024) void anchor_final_kernel(const float* __restrict__ part, int nc, int H, int D,
+                                                            int N, float* __restrict__ anchor) {
+  __shared__ float red[8][128];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int gi = threadIdx.x / 128, d = threadIdx.x % 128;
   float s = 0.f;
-  for (int c = 0; c < nc; ++c) s += part[((int64_t)b * nc + c) * H * D + hd];
-  anchor[x] = s / (float)N;
+  if (d < D)
+    for (int c = gi; c < nc; c += 8) s += part[(((int64_t)b * nc + c) * H + h) * D + d];
+  red[gi][d] = s;
+  __syncthreads();
+  if (gi == 0 && d < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += red[k][d];
+    anchor[(int64_t)bh * D + d] = t / (float)N;
+  }
 }
 
 template <int D>
@@ -153,10 +166,12 @@ size_t anchor_workspace_bytes(int B, int N, int H, int D) {
 hipError_t launch_anchor(const void* q, int64_t sB, int64_t sN, int64_t sH, int B, int N, int H, int D, float* part,
                          float* anchor, hipStream_t s) {
   const int nc = (N + kAnchorTok - 1) / kAnchorTok;
-  anchor_partial_kernel<<<dim3((unsigned)nc, (unsigned)B), dim3(256), 0, s>>>(
+  // the fewest whole waves that give every 8-channel chunk of a token row a thread
+  const int nch = H * (D / 8);
+  const int threads = std::min(1024, (nch + 63) / 64 * 64);
+  anchor_partial_kernel<<<dim3((unsigned)nc, (unsigned)B), dim3(threads), 0, s>>>(
       reinterpret_cast<const __bf16*>(q), sB, sN, sH, N, H, D, part);
-  const int64_t total = (int64_t)B * H * D;
-  anchor_final_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(part, nc, B, H, D, N, anchor);
+  anchor_final_kernel<<<dim3((unsigned)(B * H)), dim3(1024), 0, s>>>(part, nc, H, D, N, anchor);
   return hipGetLastError();
 }
 

@@ -277,7 +277,9 @@ def bench_reweight(args):
         "pct_hbm_summaries": round(100 * sum_bytes / (ms["summaries"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "roofline": {"kernel": "vsa4_kernel with summaries (bsa_forward_qouter, block mode)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profiled_traffic("vsa4_kernel_reweight.md",
+                                                  ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
     }
     ctx = dict(cfg=cfg, x=x)
     return res, ctx

@@ -8,7 +8,8 @@ it is written directly from the source pages:
 
 * "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" (maple.link) -- 3D tiling,
   per-block mean pooling, the routing matrix, TopK with a keep budget, the
-  index-table format and exact sparse attention over the selected blocks.
+  index-table format, exact sparse attention over the selected blocks and the
+  coarse pooled-V branch.
 * "NSA 算子解析（Torch/Tilelang）" (devpress.csdn.net) -- the selected-attention
   branch with externally supplied block indices/counts and GQA.
 * "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top) -- the
@@ -32,6 +33,7 @@ from .attention import (
     lse_combine,
 )
 from .reweight import anchor_queries, block_summaries, virtual_logit, reweight_attention
+from .coarse import coarse_attention, add_coarse
 
 __all__ = [
     "tile_dims",
@@ -45,6 +47,8 @@ __all__ = [
     "block_summaries",
     "virtual_logit",
     "reweight_attention",
+    "coarse_attention",
+    "add_coarse",
     "nsa_attention",
     "kvouter_partials",
     "lse_combine",

@@ -96,11 +96,19 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
+// The compiler does not see the memory instruction inside these asm
+// statements, so it does not pad the hazards that instruction has with what
+// precedes it: an SGPR of the buffer resource written by a VALU instruction
+// (v_readlane_b32 when the compiler parks SGPRs in VGPR lanes, or
+// v_readfirstlane_b32) needs 5 wait states before a VMEM instruction reads
+// it, and M0 written by SALU needs 1 before an LDS DMA.  "s_nop 4" provides 5.
+#define BSA_VMEM_SGPR_GUARD "s_nop 4\n\t"
+
 // Asynchronous 16-byte buffer -> LDS copy (lane L lands in slot L of the
 // wave's 1 KiB LDS window at `lds_byte_offset`); counted by wait_vmcnt<>().
 __device__ __forceinline__ void buffer_to_lds16(i32x4 rsrc, uint32_t voffset, uint32_t lds_byte_offset) {
   asm volatile(
-      "s_nop 0\n\t"
+      BSA_VMEM_SGPR_GUARD
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voffset), "s"(rsrc), "{m0}"(lds_byte_offset)
@@ -114,7 +122,7 @@ __device__ __forceinline__ void buffer_to_lds16(i32x4 rsrc, uint32_t voffset, ui
 __device__ __forceinline__ void stage_ids(i32x4 prs, int j, int M, uint32_t ids_lds, int lane) {
   const uint32_t voff = (uint32_t)(j * M + lane) * 4u;
   asm volatile(
-      "s_nop 0\n\t"
+      BSA_VMEM_SGPR_GUARD
       "buffer_load_dword %0, %1, 0 offen lds"
       :
       : "v"(voff), "s"(prs), "{m0}"(ids_lds)

@@ -50,21 +50,6 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, BSA_LDS(void, lds), 16, 0, 0);
 }
 
-// The same copy issued as explicit machine code.  The compiler does not track
-// it, so it inserts no waits of its own for the LDS it writes: the caller
-// orders it with wait_vmcnt<>() (these copies count as vector-memory loads)
-// and a workgroup barrier before any wave reads the destination.
-__device__ __forceinline__ void global_to_lds16_async(const void* g, uint32_t lds_byte_offset) {
-  // M0 carries the LDS destination; one wait state separates its write from
-  // the copy.
-  asm volatile(
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "{m0}"(lds_byte_offset)
-      : "memory");
-}
-
 // Read-only view of an index table in the constant address space: the
 // compiler treats it as invariant, so reads at wave-uniform addresses become
 // scalar loads (they never count against vmcnt).

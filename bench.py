@@ -1,6 +1,6 @@
 """Throughput of routed block-sparse attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight|coarse] [--no-cpu-baseline]
 
 A step is one pass of the routed block-sparse attention hot path over one
 batch of synthetic input already resident in HBM:
@@ -16,6 +16,9 @@ batch of synthetic input already resident in HBM:
   reweight  the video step with Spark-Reweight: block summaries from the mean
          query of each head, and attention over the kept blocks plus one
          virtual token for each of the other 1728 blocks.
+  coarse the video step with the coarse pooled-V branch: the routing scores
+         are kept, V is pooled, C = softmax(E) V_bar over all 1920 blocks,
+         and the attention epilogue adds gate * C to every token.
 
 Prints one JSON line.  ``value`` is the effective attention throughput of the
 whole step, 4*h*N*D*k*M / step time (the pages' FLOP count), in TFLOP/s.
@@ -324,6 +327,162 @@ def cpu_baseline_reweight(ctx, budget_s):
             "ms_per_head": round(per_head_s * 1e3, 1)}
 
 
+def bench_coarse(args):
+    """Video workload with the coarse pooled-V branch: tiling + pool/route/TopK
+    (scores kept), V pooling and C = softmax(E) V_bar, and attention with the
+    gated C added in its epilogue."""
+    import ctypes
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import coarse_gate, vsa_inputs, workload
+
+    cfg = workload("video")
+    dev = torch.device("cuda:0")
+    T, H, W = cfg["grid"]
+    B, h, D, R = cfg["B"], cfg["h"], cfg["D"], cfg["R"]
+    N = T * H * W
+    x = vsa_inputs(cfg, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    gate = coarse_gate(h, D, seed=cfg["seed"], device=dev)
+    J, M = bsa.tile_dims(T, H, W, *cfg["block"])
+    perm = torch.empty(J * M, dtype=torch.int32, device=dev)
+    block_len = torch.empty(J, dtype=torch.int32, device=dev)
+    q2k_idx = torch.empty((B, h, J, R), dtype=torch.int32, device=dev)
+    q2k_num = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    order = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    E = torch.empty((B, h, J, J), dtype=torch.float32, device=dev)
+    vbar = torch.empty((B, h, J, D), dtype=torch.float32, device=dev)
+    C = torch.empty((B, h, J, D), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(bsa.route_workspace_bytes(q, J, M, R), dtype=torch.uint8, device=dev)
+    L = bsa._lib
+    lib = L.load()
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = bsa.api._stream(dev)
+    P = bsa.api._ptr
+
+    def tile():
+        L.check(lib.vsa_tile_index(T, H, W, *cfg["block"], P(perm), P(block_len), None, s_ptr))
+
+    ra = bsa.api._route_args(q, k, perm, block_len, J, M, R, R, 1.0 / D ** 0.5, q2k_idx, q2k_num, None, None, E,
+                             order)
+
+    def route():
+        L.check(lib.vsa_pool_route_topk(ctypes.byref(ra), P(ws), ws.numel(), s_ptr))
+
+    ca = L.CoarseArgs(v=P(v), d=bsa.api._desc(v), dt=L.BSA_BF16, perm=P(perm), block_len=P(block_len), J=J, M=M,
+                      E=P(E), vbar=P(vbar), C=P(C))
+
+    def coarse():
+        L.check(lib.vsa_coarse(ctypes.byref(ca), None, 0, s_ptr))
+
+    qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
+    qa.perm, qa.block_len, qa.J, qa.M = P(perm), P(block_len), J, M
+    qa.q2k_idx, qa.q2k_num, qa.kmax = P(q2k_idx), P(q2k_num), R
+    qa.item_order = P(order)
+    qa.coarse, qa.gate = P(C), P(gate)
+
+    def attend():
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+
+    stages = (("tile", tile), ("route", route), ("coarse", coarse), ("attn", attend))
+    ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
+
+    def step(i=None):
+        for name, fn in stages:
+            if i is not None:
+                ev[name][i][0].record(stream)
+            fn()
+            if i is not None:
+                ev[name][i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in ev}
+    # nominal work: the sparse attention (the pages' count) plus the coarse
+    # product softmax(E) V_bar of every head (2*J*J*D multiply-adds)
+    sparse_flops = 4.0 * B * h * N * D * R * M
+    coarse_flops = 2.0 * B * h * J * J * D
+    attn_tflops = sparse_flops / (ms["attn"] * 1e-3) / 1e12
+    # coarse stage: V read and V_bar written by the pooling, then E and V_bar
+    # read and C written by the branch
+    coarse_bytes = (v.numel() * v.element_size() + B * h * J * D * 4) + (E.numel() * 4 + 2 * B * h * J * D * 4)
+    res = {
+        "metric": METRIC,
+        "value": round((sparse_flops + coarse_flops) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + per-cell offsets, seeded N(0, 0.25) gate; no dataset or weights)",
+        "config": {"workload": "video_dit_vsa_coarse", "B": B, "heads": h, "grid": list(cfg["grid"]),
+                   "block": list(cfg["block"]), "D": D, "J": J, "M": M, "R": R, "tokens": N},
+        "ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "coarse_gbps": round(coarse_bytes / (ms["coarse"] * 1e-3) / 1e9, 1),
+        "pct_hbm_coarse": round(100 * coarse_bytes / (ms["coarse"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "roofline": {"kernel": "vsa4_kernel with the coarse epilogue (bsa_forward_qouter, block mode)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profiled_traffic("vsa4_kernel_coarse.md",
+                                                  ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
+    }
+    ctx = dict(cfg=cfg, x=x, gate=gate)
+    return res, ctx
+
+
+def cpu_baseline_coarse(ctx, budget_s):
+    """Oracle on a bounded sample: head 0's route and coarse branch over all
+    blocks, and the attention plus gated branch for as many query blocks as fit."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg, x = ctx["cfg"], ctx["x"]
+    T, H, W = cfg["grid"]
+    D, R = cfg["D"], cfg["R"]
+    Q = x["q"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    K = x["k"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    V = x["v"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    g = ctx["gate"][:1].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    tab = oracle.tile_index(T, H, W, *cfg["block"])
+    J, M = tab["J"], tab["M"]
+    qbar = oracle.pool_blocks(Q, tab["perm"], tab["block_len"], M)
+    kbar = oracle.pool_blocks(K, tab["perm"], tab["block_len"], M)
+    E = oracle.routing_matrix(qbar, kbar)
+    idx, num, _ = oracle.select_topk(E, R)
+    C = oracle.coarse_attention(E, oracle.pool_blocks(V, tab["perm"], tab["block_len"], M))
+    t_prep = time.perf_counter() - t0
+    done = 0
+    t1 = time.perf_counter()
+    while done < J and time.perf_counter() - t1 < budget_s:
+        items = [(0, 0, i) for i in range(done, min(J, done + 32))]
+        O, _ = oracle.vsa_attention(Q, K, V, tab["perm"], tab["block_len"], M, idx, num, items=items)
+        oracle.add_coarse(np.nan_to_num(O), C, g, tab["perm"], tab["block_len"], M)
+        done += len(items)
+    t_attn = time.perf_counter() - t1
+    per_head_s = t_prep + t_attn * J / done
+    flops_head = 4.0 * (T * H * W) * D * R * M + 2.0 * J * J * D
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops_head / per_head_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "head 0 of the video workload: float64 route, TopK and coarse branch over all %d blocks "
+                      "(%.1f s) and attention plus the gated branch for %d of %d query blocks (%.1f s), scaled "
+                      "to one head" % (J, t_prep, done, J, t_attn),
+            "ms_per_head": round(per_head_s * 1e3, 1)}
+
+
 def _time(fn, steps, warmup, stream):
     """Average ms of fn() over `steps` launches, HIP events on `stream`."""
     import torch
@@ -473,7 +632,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight"])
+    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight", "coarse"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -501,6 +660,10 @@ def main(argv=None):
         res, ctx = bench_reweight(args)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_reweight(ctx, args.cpu_seconds)
+    elif args.workload == "coarse":
+        res, ctx = bench_coarse(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_coarse(ctx, args.cpu_seconds)
     else:
         res, ctx = bench_video(args)
         if not args.no_cpu_baseline:

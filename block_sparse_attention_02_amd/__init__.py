@@ -14,6 +14,7 @@ from .api import (
     pool_route_topk,
     route_workspace_bytes,
     attention_vsa,
+    coarse_attention,
     spark_summaries,
     attention_nsa,
     kvouter,
@@ -32,6 +33,7 @@ __all__ = [
     "pool_route_topk",
     "route_workspace_bytes",
     "attention_vsa",
+    "coarse_attention",
     "spark_summaries",
     "attention_nsa",
     "kvouter",

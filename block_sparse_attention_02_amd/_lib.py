@@ -59,7 +59,13 @@ class QOuterArgs(ctypes.Structure):
                 ("q2k_idx", _p), ("q2k_num", _p), ("kmax", _i32),
                 ("blk_idx", _p), ("blk_cnt", _p), ("S", _i32), ("BS", _i32), ("causal", _i32),
                 ("lse", _p), ("item_order", _p),
-                ("k_sum", _p), ("v_sum", _p), ("b_sum", _p)]
+                ("k_sum", _p), ("v_sum", _p), ("b_sum", _p),
+                ("coarse", _p), ("gate", _p)]
+
+
+class CoarseArgs(ctypes.Structure):
+    _fields_ = [("v", _p), ("d", TDesc), ("dt", _i32), ("perm", _p), ("block_len", _p),
+                ("J", _i32), ("M", _i32), ("E", _p), ("vbar", _p), ("C", _p)]
 
 
 class SummaryArgs(ctypes.Structure):
@@ -91,6 +97,8 @@ PROTOTYPES = {
     "vsa_pool_route_topk_ws": (_i32, [ctypes.POINTER(RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_pool_route_topk": (_i32, [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]),
     "bsa_forward_qouter": (_i32, [ctypes.POINTER(QOuterArgs), _p]),
+    "vsa_coarse_ws": (_i32, [ctypes.POINTER(CoarseArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "vsa_coarse": (_i32, [ctypes.POINTER(CoarseArgs), _p, ctypes.c_size_t, _p]),
     "spark_summaries_ws": (_i32, [ctypes.POINTER(SummaryArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "spark_summaries": (_i32, [ctypes.POINTER(SummaryArgs), _p, ctypes.c_size_t, _p]),
     "bsa_kvouter_ws": (_i32, [ctypes.POINTER(KvOuterArgs), ctypes.POINTER(ctypes.c_size_t)]),

@@ -15,7 +15,7 @@ from . import _lib as L
 
 __all__ = [
     "tile_dims", "tile_index", "keep_budget", "pool_route_topk", "route_workspace_bytes",
-    "attention_vsa", "attention_nsa", "kvouter", "combine", "VsaGeometry", "vsa_forward",
+    "attention_vsa", "attention_nsa", "coarse_attention", "spark_summaries", "kvouter", "combine", "VsaGeometry", "vsa_forward",
 ]
 
 
@@ -97,13 +97,14 @@ def route_workspace_bytes(q, J, M, R, kmax=None, debug=False):
 
 
 def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug=False,
-                    out=None, workspace=None, item_order=None):
+                    out=None, workspace=None, item_order=None, scores=None):
     """Per-block means, routing scores and TopK index table.
 
     q, k: [B, N, H, D] (bf16 or float32).  Returns (q2k_idx [B,H,J,kmax],
     q2k_num [B,H,J]) and, with ``debug``, also (qbar, kbar, E) in float32.
     ``item_order`` (optional int32 [B,H,J] tensor) is filled with a processing
-    order of the query blocks for attention_vsa.
+    order of the query blocks for attention_vsa.  ``scores`` (optional
+    contiguous float32 [B,H,J,J] tensor) receives E without the debug outputs.
     """
     _need_cuda(q, k, perm, block_len)
     B, N, H, D = q.shape
@@ -120,6 +121,13 @@ def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug
         qbar = torch.empty((B, H, J, D), dtype=torch.float32, device=dev)
         kbar = torch.empty_like(qbar)
         E = torch.empty((B, H, J, J), dtype=torch.float32, device=dev)
+    if scores is not None:
+        _need_cuda(scores)
+        if scores.dtype != torch.float32 or scores.numel() != B * H * J * J or not scores.is_contiguous():
+            raise ValueError("scores must be a contiguous float32 tensor of B*H*J*J elements")
+        if E is not None:
+            raise ValueError("scores and debug are exclusive")
+        E = scores
     if item_order is not None:
         _need_cuda(item_order)
         if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
@@ -138,6 +146,29 @@ def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug
 def _qouter_args(q, k, v, out, scale, mode, lse):
     return L.QOuterArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), out=_ptr(out), dq=_desc(q), dkv=_desc(k),
                         dout=_desc(out), dt=_dtype(q), scale=scale, mode=mode, lse=_ptr(lse))
+
+
+def coarse_attention(v, perm, block_len, J, M, E, need_vbar=False, out=None):
+    """Coarse pooled-V branch: C [B, H, J, D] fp32 = softmax(E) V_bar, with
+    V_bar the per-block means of v [B, N, H, D] (bf16 or float32) and E the
+    fp32 [B, H, J, J] routing scores.  With ``need_vbar`` also returns V_bar."""
+    _need_cuda(v, perm, block_len, E)
+    B, N, H, D = v.shape
+    if E.dtype != torch.float32 or E.numel() != B * H * J * J or not E.is_contiguous():
+        raise ValueError("E must be a contiguous float32 tensor of B*H*J*J elements")
+    dev = v.device
+    C = torch.empty((B, H, J, D), dtype=torch.float32, device=dev) if out is None else out
+    if C.dtype != torch.float32 or C.numel() != B * H * J * D or not C.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of B*H*J*D elements")
+    vbar = torch.empty((B, H, J, D), dtype=torch.float32, device=dev) if need_vbar else None
+    a = L.CoarseArgs(v=_ptr(v), d=_desc(v), dt=_dtype(v), perm=_ptr(perm), block_len=_ptr(block_len), J=J, M=M,
+                     E=_ptr(E), vbar=_ptr(vbar), C=_ptr(C))
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    L.check(lib.vsa_coarse_ws(ctypes.byref(a), ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev) if n.value else None
+    L.check(lib.vsa_coarse(ctypes.byref(a), _ptr(ws), n.value, _stream(dev)))
+    return (C, vbar) if need_vbar else C
 
 
 def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, need_anchor=False):
@@ -172,11 +203,13 @@ def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, nee
 
 
 def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
-                  item_order=None, summaries=None):
+                  item_order=None, summaries=None, coarse=None):
     """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
     ``item_order``: optional processing order (from pool_route_topk).
     ``summaries``: optional (k_sum, v_sum, b_sum) from spark_summaries; every
-    block a query block does not keep then enters through its virtual token."""
+    block a query block does not keep then enters through its virtual token.
+    ``coarse``: optional (C, gate) -- C fp32 [B,H,J,D] from coarse_attention,
+    gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -200,6 +233,13 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
                 or not (k_sum.is_contiguous() and v_sum.is_contiguous() and b_sum.is_contiguous())):
             raise ValueError("summaries must be contiguous bf16 [B,H,J,D] k_sum/v_sum and float32 [B,H,J] b_sum")
         a.k_sum, a.v_sum, a.b_sum = _ptr(k_sum), _ptr(v_sum), _ptr(b_sum)
+    if coarse is not None:
+        C, gate = coarse
+        _need_cuda(C, gate)
+        if (C.dtype != torch.float32 or gate.dtype != torch.float32 or C.numel() != B * H * J * D
+                or gate.numel() != H * D or not (C.is_contiguous() and gate.is_contiguous())):
+            raise ValueError("coarse must be a contiguous float32 C [B,H,J,D] and gate [H,D]")
+        a.coarse, a.gate = _ptr(C), _ptr(gate)
     L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
     return (out, lse) if need_lse else out
 
@@ -276,16 +316,23 @@ class VsaGeometry:
         self.perm, self.block_len, self.inv = tile_index(T, H, W, bT, bH, bW, device=device)
 
 
-def vsa_forward(q, k, v, geom, R, kmax=None, scale=None, need_lse=False, workspace=None, index_out=None):
+def vsa_forward(q, k, v, geom, R, kmax=None, scale=None, need_lse=False, workspace=None, index_out=None,
+                gate=None):
     """Routed block-sparse attention: pool -> route -> TopK -> exact attention.
+    ``gate`` (optional fp32 [H, D]) adds the coarse pooled-V branch.
 
     Returns (out, q2k_idx, q2k_num) (plus lse with ``need_lse``)."""
     B, _, H, _ = q.shape
     order = torch.empty((B, H, geom.J), dtype=torch.int32, device=q.device)
+    E = None if gate is None else torch.empty((B, H, geom.J, geom.J), dtype=torch.float32, device=q.device)
     q2k_idx, q2k_num = pool_route_topk(q, k, geom.perm, geom.block_len, geom.J, geom.M, R, kmax=kmax,
-                                       scale=scale, workspace=workspace, out=index_out, item_order=order)
+                                       scale=scale, workspace=workspace, out=index_out, item_order=order,
+                                       scores=E)
+    coarse = None
+    if gate is not None:
+        coarse = (coarse_attention(v, geom.perm, geom.block_len, geom.J, geom.M, E), gate)
     res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
-                        need_lse=need_lse, item_order=order)
+                        need_lse=need_lse, item_order=order, coarse=coarse)
     if need_lse:
         return res[0], q2k_idx, q2k_num, res[1]
     return res, q2k_idx, q2k_num

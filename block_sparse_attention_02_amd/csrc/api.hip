@@ -202,12 +202,18 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
       if (!aligned16(a->k_sum) || !aligned16(a->v_sum) || (reinterpret_cast<uintptr_t>(a->b_sum) & 3))
         return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: k_sum/v_sum must be 16-byte and b_sum 4-byte aligned");
     }
+    if (a->coarse || a->gate) {
+      if (!a->coarse || !a->gate) return fail(BSA_ERR_ARG, "bsa_forward_qouter: coarse and gate go together");
+      if (!aligned16(a->coarse) || !aligned16(a->gate))
+        return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: coarse and gate must be 16-byte aligned");
+    }
     bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
                          a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
                          a->dout.sB, a->dout.sN, a->dout.sH,
                          a->perm, a->block_len, a->q2k_idx, a->q2k_num,
                          (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
-                         scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum};
+                         scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum,
+                         a->coarse, a->gate};
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   if (a->mode == BSA_SEL_TOKEN) {
@@ -228,6 +234,48 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
     return hip_status(bsa::launch_nsa_attention(p, false, s), "nsa attention launch");
   }
   return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
+}
+
+// ------------------------------------------------------------------ coarse branch
+static bsa_status check_coarse(const vsa_coarse_args* a) {
+  if (!a) return fail(BSA_ERR_ARG, "vsa_coarse: null args");
+  if (!a->v || !a->perm || !a->block_len || !a->E || !a->C)
+    return fail(BSA_ERR_ARG, "vsa_coarse: v, perm, block_len, E and C are required");
+  if (a->dt != BSA_BF16 && a->dt != BSA_F32) return fail(BSA_ERR_ARG, "vsa_coarse: bad dtype");
+  bsa_status st = check_desc(a->d, "v", 1, false);
+  if (st != BSA_OK) return st;
+  if (a->d.D != 64 && a->d.D != 128) return fail(BSA_ERR_UNSUPPORTED, "vsa_coarse: D must be 64 or 128");
+  if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "vsa_coarse: J and M must be positive");
+  if ((int64_t)a->d.B * a->d.H > 65535) return fail(BSA_ERR_UNSUPPORTED, "vsa_coarse: B*H must be <= 65535");
+  return BSA_OK;
+}
+
+bsa_status vsa_coarse_ws(const vsa_coarse_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "vsa_coarse_ws: null output");
+  bsa_status st = check_coarse(a);
+  if (st != BSA_OK) return st;
+  *bytes = a->vbar ? 0 : round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  return ok();
+}
+
+bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  bsa_status st = vsa_coarse_ws(a, &need);
+  if (st != BSA_OK) return st;
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace of %zu bytes required", need);
+  float* vbar = a->vbar ? a->vbar : static_cast<float*>(ws);
+  const int vec = 16 / elem_bytes(a->dt);
+  const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
+                      aligned16(a->v);
+  // the pooling kernel of the routing step, run on V alone
+  bsa::PoolParams pp{a->v, a->v, a->d.sB, a->d.sN, a->d.sH, (int)a->d.B, (int)a->d.H, (int)a->d.D, a->J, a->M,
+                     a->perm, a->block_len, vbar, vbar};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s, 1);
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  bsa::CoarseParams cp{a->E, vbar, a->C, (int)(a->d.B * a->d.H), a->J, (int)a->d.D};
+  return hip_status(bsa::launch_coarse(cp, s), "coarse launch");
 }
 
 // ------------------------------------------------------------ Spark-Reweight summaries

@@ -35,6 +35,16 @@ constexpr int kSumMaskWords = 128;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
+// Gated coarse term gate[h, d..d+3] * C[b, h, i, d..d+3] of the pooled-V
+// branch ("VSA 实现详解" section 6.7), added to the normalised output of every
+// token of query block i; zero when the branch is off.
+__device__ __forceinline__ f32x4 coarse_term(const VsaAttnParams& p, int64_t bh, int hh, int i, int d) {
+  if (!p.coarse) return f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 c = *reinterpret_cast<const f32x4*>(p.coarse + (bh * p.J + i) * p.D + d);
+  const f32x4 g = *reinterpret_cast<const f32x4*>(p.gate + (int64_t)hh * p.D + d);
+  return f32x4{g[0] * c[0], g[1] * c[1], g[2] * c[2], g[3] * c[3]};
+}
+
 // Workgroup barrier that first retires this wave's outstanding LDS reads, so a
 // buffer can be refilled right after it.  Asynchronous global->LDS copies are
 // ordered separately with wait_vmcnt<>().
@@ -399,8 +409,9 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d = 32 * dt + 8 * jj + 4 * h2;
-        bf16x4 v4 = {(__bf16)(oacc[dt][4 * jj + 0] * inv), (__bf16)(oacc[dt][4 * jj + 1] * inv),
-                     (__bf16)(oacc[dt][4 * jj + 2] * inv), (__bf16)(oacc[dt][4 * jj + 3] * inv)};
+        const f32x4 cg = coarse_term(p, bh, hh, i, d);
+        bf16x4 v4 = {(__bf16)fmaf(oacc[dt][4 * jj + 0], inv, cg[0]), (__bf16)fmaf(oacc[dt][4 * jj + 1], inv, cg[1]),
+                     (__bf16)fmaf(oacc[dt][4 * jj + 2], inv, cg[2]), (__bf16)fmaf(oacc[dt][4 * jj + 3], inv, cg[3])};
         *reinterpret_cast<bf16x4*>(og + d) = v4;
       }
     if constexpr (LSE) {
@@ -961,8 +972,9 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int dd = 32 * d + 8 * jj + 4 * h2;
-          bf16x4 v4 = {(__bf16)(oacc[d][4 * jj + 0] * inv), (__bf16)(oacc[d][4 * jj + 1] * inv),
-                       (__bf16)(oacc[d][4 * jj + 2] * inv), (__bf16)(oacc[d][4 * jj + 3] * inv)};
+          const f32x4 cg = coarse_term(p, bh, hh, i, dd);
+          bf16x4 v4 = {(__bf16)fmaf(oacc[d][4 * jj + 0], inv, cg[0]), (__bf16)fmaf(oacc[d][4 * jj + 1], inv, cg[1]),
+                       (__bf16)fmaf(oacc[d][4 * jj + 2], inv, cg[2]), (__bf16)fmaf(oacc[d][4 * jj + 3], inv, cg[3])};
           *reinterpret_cast<bf16x4*>(og + dd) = v4;
         }
       if constexpr (LSE) {
@@ -1064,8 +1076,10 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   if (row < ni) {
     const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
     float* og = reinterpret_cast<float*>(p.o) + b * p.o_sB + (int64_t)qtok * p.o_sN + hh * p.o_sH + half * HD;
+    const float* cr = p.coarse ? p.coarse + (bh * p.J + i) * D + half * HD : nullptr;
+    const float* gr = p.gate ? p.gate + (int64_t)hh * D + half * HD : nullptr;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) og[d] = ov[d] * inv;
+    for (int d = 0; d < HD; ++d) og[d] = cr ? fmaf(ov[d], inv, gr[d] * cr[d]) : ov[d] * inv;
     if (p.lse && half == 0) p.lse[bh * p.N + qtok] = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }

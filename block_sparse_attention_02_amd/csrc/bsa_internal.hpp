@@ -23,8 +23,18 @@ struct PoolParams {
   float* qbar;  // [B, H, J, D]
   float* kbar;
 };
-// `vec`: D, strides and base pointers allow 16-byte vector loads.
-hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s);
+// `vec`: D, strides and base pointers allow 16-byte vector loads.  ntensors:
+// 2 pools q and k, 1 pools q only.
+hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s, int ntensors = 2);
+
+// Coarse branch: C[bh, i, :] = sum_j softmax_j(E[bh, i, :]) vbar[bh, j, :].
+struct CoarseParams {
+  const float* E;     // [BH, J, J]
+  const float* vbar;  // [BH, J, D]
+  float* C;           // [BH, J, D]
+  int BH, J, D;
+};
+hipError_t launch_coarse(const CoarseParams& p, hipStream_t s);
 
 struct RouteParams {
   const float* qbar;  // [B, H, J, D]
@@ -86,6 +96,9 @@ struct VsaAttnParams {
   const void* k_sum;
   const void* v_sum;
   const float* b_sum;
+  // optional coarse branch (M = 64, bf16): out += gate[h, :] * C[b, h, i, :]
+  const float* coarse;  // [B, H, J, D]
+  const float* gate;    // [H, D]
 };
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
 

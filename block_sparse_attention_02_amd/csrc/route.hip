@@ -50,7 +50,8 @@ hipError_t launch_tile_index(int T, int H, int W, int bT, int bH, int bW, int J,
 }
 
 // ============================================================================
-// Pool: one workgroup per (block i, batch b, tensor).  Each token row of all
+// Pool: one workgroup per (block i, batch b, tensor) -- tensor 0 is q (into
+// qbar), tensor 1 is k (into kbar); a single-tensor launch pools q only.  Each token row of all
 // heads is read with 16-byte loads (VW elements) and accumulated in fp32; the
 // sum is divided by the block's true length.  Loads are unconditional (lanes
 // past the row read a clamped address and discard it) so that the UT x CPT
@@ -116,10 +117,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 }
 
 template <typename T, int VW>
-static hipError_t launch_pool_t(const PoolParams& p, hipStream_t s) {
+static hipError_t launch_pool_t(const PoolParams& p, int ntensors, hipStream_t s) {
   const int nch = p.H * (p.D / VW);
   const int cpt = (nch + 255) / 256;
-  dim3 grid(p.J, p.B, 2);
+  dim3 grid(p.J, p.B, ntensors);
   if (cpt <= 1)
     pool_kernel<T, VW, 1><<<grid, 256, 0, s>>>(p);
   else if (cpt <= 2)
@@ -131,13 +132,13 @@ static hipError_t launch_pool_t(const PoolParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s) {
+hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_t s, int ntensors) {
   if (f32_input) {
-    if (vec) return launch_pool_t<float, 4>(p, s);
-    return launch_pool_t<float, 1>(p, s);
+    if (vec) return launch_pool_t<float, 4>(p, ntensors, s);
+    return launch_pool_t<float, 1>(p, ntensors, s);
   }
-  if (vec) return launch_pool_t<__bf16, 8>(p, s);
-  return launch_pool_t<__bf16, 1>(p, s);
+  if (vec) return launch_pool_t<__bf16, 8>(p, ntensors, s);
+  return launch_pool_t<__bf16, 1>(p, ntensors, s);
 }
 
 // ============================================================================

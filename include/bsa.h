@@ -122,7 +122,8 @@ int vsa_budget(double drop_ratio, int J);
  * q2k_idx   int32 [B, H, J, kmax] contiguous, kmax >= R
  * q2k_num   int32 [B, H, J] contiguous
  * qbar, kbar  optional fp32 [B, H, J, D] outputs (NULL: kept in the workspace)
- * E         optional fp32 [B, H, J, J] output of the scores (debug; NULL: none)
+ * E         optional fp32 [B, H, J, J] output of the scores (NULL: none); the
+ *           input of vsa_coarse
  * item_order  optional int32 [B, H, J] output (NULL: not computed): for each
  *           (b, h) a permutation of 0..J-1 that places query blocks with
  *           similar kept sets next to each other (ascending Morton code of the
@@ -216,9 +217,49 @@ typedef struct {
   const void* k_sum;
   const void* v_sum;
   const float* b_sum;
+  /* optional, BSA_SEL_BLOCK: coarse pooled-V branch ([VSA] section 6.7).  When
+   * set, every token a of query block i gets, before the bf16 rounding,
+   *   out[b, a, h, :] += gate[h, :] * coarse[b, h, i, :]
+   * with coarse fp32 [B, H, J, D] from vsa_coarse and gate fp32 [H, D], both
+   * contiguous and 16-byte aligned; both or neither. */
+  const float* coarse;
+  const float* gate;
 } bsa_qouter_args;
 
 bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Coarse pooled-V branch ([VSA] section 6.7, with the pooling of section 2.1).
+ *
+ * For every batch b, head h and query block i:
+ *   vbar_j = (1/n_j) * sum_{r < n_j} V[b, perm[j*M + r], h, :]
+ *   C[b,h,i,:] = sum_j softmax_j(E[b,h,i,:]) vbar_j      (over all J blocks)
+ * E is the fp32 [B, H, J, J] score matrix of vsa_pool_route_topk (or any
+ * finite scores of that layout).  The branch is merged into the attention
+ * output by bsa_forward_qouter (fields coarse and gate).
+ *   v        strided view (dtype dt: bf16 or fp32) [B, N, H, D]
+ *   perm, block_len  tiling tables of J blocks of capacity M
+ *   E        fp32 [B, H, J, J] contiguous input
+ *   vbar     optional fp32 [B, H, J, D] contiguous output (NULL: workspace)
+ *   C        fp32 [B, H, J, D] contiguous output
+ * Supported: D in {64, 128}, B*H <= 65535.  The softmax weights and the sums
+ * are fp32.  The workspace holds vbar when it is not an output:
+ * vsa_coarse_ws() bytes.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* v;
+  bsa_tdesc d;
+  bsa_dtype dt;
+  const int32_t* perm;
+  const int32_t* block_len;
+  int J, M;
+  const float* E;
+  float* vbar;
+  float* C;
+} vsa_coarse_args;
+
+bsa_status vsa_coarse_ws(const vsa_coarse_args* a, size_t* bytes);
+bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
  * Spark-Reweight block summaries ([Spark] sections 07 and 08).

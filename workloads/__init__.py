@@ -14,10 +14,11 @@ exactly the tensors the device computed on.
 """
 
 from .configs import WORKLOADS, workload, scaled
-from .gen import vsa_inputs, nsa_inputs, msa_inputs, kept_lists
+from .gen import vsa_inputs, nsa_inputs, msa_inputs, kept_lists, coarse_gate
 
 __all__ = [
     "kept_lists",
+    "coarse_gate",
     "WORKLOADS",
     "workload",
     "scaled",

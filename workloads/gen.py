@@ -83,6 +83,13 @@ def kept_lists(B, h, J, kmax, seed, device="cpu"):
     return torch.from_numpy(idx).to(device), torch.from_numpy(num).to(device)
 
 
+def coarse_gate(h, D, seed, device="cpu"):
+    """Gate of the coarse pooled-V branch, float32 [h, D]: N(0, 0.5^2) per
+    head and channel (a stand-in for a trained gate; zero means no branch)."""
+    g = _gen(device, seed)
+    return torch.randn((h, D), generator=g, device=device, dtype=torch.float32) * 0.5
+
+
 def _sorted_padded(sel, limit):
     """Sort a row ascending and turn entries >= limit into -1 (at the end)."""
     sel = torch.sort(sel, dim=-1).values

@@ -247,6 +247,8 @@ static bsa_status check_coarse(const vsa_coarse_args* a) {
   if (a->d.D != 64 && a->d.D != 128) return fail(BSA_ERR_UNSUPPORTED, "vsa_coarse: D must be 64 or 128");
   if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "vsa_coarse: J and M must be positive");
   if ((int64_t)a->d.B * a->d.H > 65535) return fail(BSA_ERR_UNSUPPORTED, "vsa_coarse: B*H must be <= 65535");
+  if (!aligned16(a->C) || (a->vbar && !aligned16(a->vbar)))
+    return fail(BSA_ERR_SHAPE, "vsa_coarse: C and vbar must be 16-byte aligned");
   return BSA_OK;
 }
 
@@ -264,6 +266,7 @@ bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void*
   if (st != BSA_OK) return st;
   if (need && (!ws || ws_bytes < need))
     return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace of %zu bytes required", need);
+  if (need && !aligned16(ws)) return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace must be 16-byte aligned");
   float* vbar = a->vbar ? a->vbar : static_cast<float*>(ws);
   const int vec = 16 / elem_bytes(a->dt);
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&

@@ -5,35 +5,44 @@
 // matrix of section 2.2 and V_bar the per-block means of V; each query block's
 // row of C is added to its tokens under a gate, outside the main kernel).
 //
-// Design (MI355X): one 256-thread workgroup per (batch*head, 32 query blocks).
-// Pass 1: each wave takes 4 rows of E and reduces max and sum of exp with
-// wave shuffles.  Pass 2: the normalised weights of 64 columns at a time are
-// staged in LDS ([column][row], so one 16-byte read gives four rows); thread t
-// owns channel t % D of rows (t / D) * R0 .. +R0 and accumulates in fp32 while
-// V_bar rows stream from L2 (a head's V_bar is J*D*4 bytes).  E is read twice,
-// V_bar once per workgroup.
+// Design (MI355X): one 256-thread workgroup per (batch*head, ROWS query
+// blocks), ROWS = 4096 / D, so the C tile is ROWS x D = 4096 values and each
+// thread owns a 4 x 4 register tile (4 query blocks x 4 channels).
+//   pass 1: each wave reduces ROWS/4 rows of E to max and 1 / sum of exp
+//           (wave shuffles), kept in LDS;
+//   pass 2: per chunk of KC = 32 columns, the normalised weights (ROWS x KC)
+//           and the V_bar rows (KC x D) are staged in LDS, then every thread
+//           runs KC steps of one 16-byte weight read (4 rows, a broadcast
+//           within the wave), one 16-byte V_bar read (4 channels) and 16 FMAs.
+// Weight rows are XOR-swizzled by column so that the 16-byte staging writes of
+// 8 consecutive columns cover all banks.  All arithmetic is fp32; E is read
+// twice (max/sum, then weights), V_bar once per workgroup from L2.
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
 namespace bsa {
 
-constexpr int kCoarseRows = 32;  // query blocks per workgroup
-constexpr int kCoarseCols = 64;  // columns of E staged per step
+constexpr int kCoarseCols = 32;  // columns of E per staged chunk
 
 template <int D>
 __global__ __launch_bounds__(256) void coarse_kernel(CoarseParams p) {
-  constexpr int RG = 256 / D;              // row groups
-  constexpr int R0 = kCoarseRows / RG;     // rows per thread
-  __shared__ float mrow[kCoarseRows], zinv[kCoarseRows];
-  __shared__ __align__(16) float wgt[kCoarseCols][kCoarseRows];
+  constexpr int ROWS = 4096 / D;  // query blocks per workgroup (32 or 64)
+  constexpr int CG = D / 4;       // 4-channel groups
+  constexpr int RG = ROWS / 4;    // 4-row groups
+  static_assert(CG * RG == 256, "one 4x4 tile per thread");
+  constexpr int KC = kCoarseCols;
+  __shared__ float mrow[ROWS], zinv[ROWS];
+  __shared__ __align__(16) float Wt[KC * ROWS];  // [column][row group ^ (column & 7)][4]
+  __shared__ __align__(16) float Vs[KC * D];     // [column][channel]
   const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * kCoarseRows;
+  const int i0 = blockIdx.x * ROWS;
   const int J = p.J;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* __restrict__ Eb = p.E + (int64_t)bh * J * J;
+  const float* __restrict__ vb = p.vbar + (int64_t)bh * J * D;
 
   // ---- pass 1: row maximum and 1 / sum of exp ----
-  for (int r = w; r < kCoarseRows; r += 4) {
+  for (int r = w; r < ROWS; r += 4) {
     const int i = i0 + r;
     float m = -INFINITY, z = 0.f;
     if (i < J) {
@@ -52,41 +61,56 @@ __global__ __launch_bounds__(256) void coarse_kernel(CoarseParams p) {
   }
   __syncthreads();
 
-  // ---- pass 2: C = W V_bar ----
-  const int d = threadIdx.x % D, rg = threadIdx.x / D;
-  const float* __restrict__ vb = p.vbar + (int64_t)bh * J * D + d;
-  float acc[R0];
+  // ---- pass 2: C tile = W V_bar ----
+  const int cg = tid % CG, rg = tid / CG;
+  // staging roles: weights -- column sc, row group sr (4 rows, one 16-byte
+  // write); V_bar -- 16-byte chunks e = tid + 256k of the KC x D chunk
+  const int sc = tid % KC, sr0 = tid / KC;  // sr = sr0 + (256/KC) * k
+  f32x4 acc[4];
 #pragma unroll
-  for (int r = 0; r < R0; ++r) acc[r] = 0.f;
-  for (int j0 = 0; j0 < J; j0 += kCoarseCols) {
-    // stage the weights of columns j0 .. j0+63 for the 32 rows
-    for (int e = threadIdx.x; e < kCoarseCols * kCoarseRows; e += 256) {
-      const int r = e / kCoarseCols, c = e % kCoarseCols;
-      const int i = i0 + r, j = j0 + c;
-      wgt[c][r] = (i < J && j < J) ? __expf(Eb[(int64_t)i * J + j] - mrow[r]) * zinv[r] : 0.f;
+  for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < J; j0 += KC) {
+    const int j = j0 + sc;
+#pragma unroll
+    for (int k = 0; k < RG / (256 / KC); ++k) {
+      const int sr = sr0 + (256 / KC) * k;
+      f32x4 wv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * sr + e, i = i0 + r;
+        wv[e] = (i < J && j < J) ? __expf(Eb[(int64_t)i * J + j] - mrow[r]) * zinv[r] : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(&Wt[sc * ROWS + 4 * (sr ^ (sc & 7))]) = wv;
+    }
+#pragma unroll
+    for (int k = 0; k < KC * D / 4 / 256; ++k) {
+      const int e = tid + 256 * k, c = e / CG, dq = e % CG;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j0 + c < J) v = *reinterpret_cast<const f32x4*>(vb + (int64_t)(j0 + c) * D + 4 * dq);
+      *reinterpret_cast<f32x4*>(&Vs[c * D + 4 * dq]) = v;
     }
     __syncthreads();
-    const int nc = min(kCoarseCols, J - j0);
-    for (int c = 0; c < nc; ++c) {
-      const float v = vb[(int64_t)(j0 + c) * D];
+#pragma unroll 8
+    for (int c = 0; c < KC; ++c) {
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(&Wt[c * ROWS + 4 * (rg ^ (c & 7))]);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&Vs[c * D + 4 * cg]);
 #pragma unroll
-      for (int r4 = 0; r4 < R0; r4 += 4) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(&wgt[c][rg * R0 + r4]);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r4 + e] += wv[e] * v;
-      }
+        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(wv[r], v[e], acc[r][e]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int r = 0; r < R0; ++r) {
-    const int i = i0 + rg * R0 + r;
-    if (i < J) p.C[((int64_t)bh * J + i) * D + d] = acc[r];
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + 4 * rg + r;
+    if (i < J) *reinterpret_cast<f32x4*>(p.C + ((int64_t)bh * J + i) * D + 4 * cg) = acc[r];
   }
 }
 
 hipError_t launch_coarse(const CoarseParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((p.J + kCoarseRows - 1) / kCoarseRows), (unsigned)p.BH);
+  const int rows = 4096 / p.D;
+  const dim3 grid((unsigned)((p.J + rows - 1) / rows), (unsigned)p.BH);
   if (p.D == 128)
     coarse_kernel<128><<<grid, dim3(256), 0, s>>>(p);
   else

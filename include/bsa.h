@@ -242,9 +242,9 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
  *   E        fp32 [B, H, J, J] contiguous input
  *   vbar     optional fp32 [B, H, J, D] contiguous output (NULL: workspace)
  *   C        fp32 [B, H, J, D] contiguous output
- * Supported: D in {64, 128}, B*H <= 65535.  The softmax weights and the sums
- * are fp32.  The workspace holds vbar when it is not an output:
- * vsa_coarse_ws() bytes.
+ * Supported: D in {64, 128}, B*H <= 65535; C, vbar and the workspace 16-byte
+ * aligned.  The softmax weights and the sums are fp32.  The workspace holds
+ * vbar when it is not an output: vsa_coarse_ws() bytes.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* v;

@@ -8,8 +8,8 @@ it is written directly from the source pages:
 
 * "VSA 实现详解：三维分块、均值路由与块稀疏 Attention" (maple.link) -- 3D tiling,
   per-block mean pooling, the routing matrix, TopK with a keep budget, the
-  index-table format, exact sparse attention over the selected blocks and the
-  coarse pooled-V branch.
+  index-table format, exact sparse attention over the selected blocks, the
+  coarse pooled-V branch and the H3 multi-region layout with grouped routing.
 * "NSA 算子解析（Torch/Tilelang）" (devpress.csdn.net) -- the selected-attention
   branch with externally supplied block indices/counts and GQA.
 * "MSA 为什么采用 KV-outer Sparse Attention Forward" (notes.kuangjux.top) -- the
@@ -34,8 +34,11 @@ from .attention import (
 )
 from .reweight import anchor_queries, block_summaries, virtual_logit, reweight_attention
 from .coarse import coarse_attention, add_coarse
+from .h3 import h3_layout, h3_route
 
 __all__ = [
+    "h3_layout",
+    "h3_route",
     "tile_dims",
     "tile_index",
     "keep_budget",

@@ -21,6 +21,9 @@ from .api import (
     combine,
     VsaGeometry,
     vsa_forward,
+    H3Geometry,
+    h3_pool_route_topk,
+    h3_forward,
 )
 from . import metrics
 
@@ -40,5 +43,8 @@ __all__ = [
     "combine",
     "VsaGeometry",
     "vsa_forward",
+    "H3Geometry",
+    "h3_pool_route_topk",
+    "h3_forward",
     "metrics",
 ]

@@ -63,6 +63,21 @@ class QOuterArgs(ctypes.Structure):
                 ("coarse", _p), ("gate", _p)]
 
 
+class Segment(ctypes.Structure):
+    _fields_ = [("video", _i32), ("T", _i32), ("H", _i32), ("W", _i32)]
+
+
+H3_MAX_SEGMENTS = 16
+
+
+class H3RouteArgs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k", _p), ("d", TDesc), ("dt", _i32),
+                ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
+                ("num_prefix", _i32), ("nregions", _i32), ("spans", _p), ("budgets", _p),
+                ("kmax", _i32), ("scale", _f32), ("q2k_idx", _p), ("q2k_num", _p),
+                ("qbar", _p), ("kbar", _p), ("item_order", _p)]
+
+
 class CoarseArgs(ctypes.Structure):
     _fields_ = [("v", _p), ("d", TDesc), ("dt", _i32), ("perm", _p), ("block_len", _p),
                 ("J", _i32), ("M", _i32), ("E", _p), ("vbar", _p), ("C", _p)]
@@ -97,6 +112,10 @@ PROTOTYPES = {
     "vsa_pool_route_topk_ws": (_i32, [ctypes.POINTER(RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_pool_route_topk": (_i32, [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]),
     "bsa_forward_qouter": (_i32, [ctypes.POINTER(QOuterArgs), _p]),
+    "h3_tile_dims": (_i32, [ctypes.POINTER(Segment), _i32, _i32, _i32, _i32] + [ctypes.POINTER(_i32)] * 6),
+    "h3_tile_index": (_i32, [ctypes.POINTER(Segment), _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "h3_pool_route_topk_ws": (_i32, [ctypes.POINTER(H3RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "h3_pool_route_topk": (_i32, [ctypes.POINTER(H3RouteArgs), _p, ctypes.c_size_t, _p]),
     "vsa_coarse_ws": (_i32, [ctypes.POINTER(CoarseArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_coarse": (_i32, [ctypes.POINTER(CoarseArgs), _p, ctypes.c_size_t, _p]),
     "spark_summaries_ws": (_i32, [ctypes.POINTER(SummaryArgs), ctypes.POINTER(ctypes.c_size_t)]),

@@ -15,7 +15,8 @@ from . import _lib as L
 
 __all__ = [
     "tile_dims", "tile_index", "keep_budget", "pool_route_topk", "route_workspace_bytes",
-    "attention_vsa", "attention_nsa", "coarse_attention", "spark_summaries", "kvouter", "combine", "VsaGeometry", "vsa_forward",
+    "attention_vsa", "attention_nsa", "coarse_attention", "spark_summaries", "H3Geometry",
+    "h3_pool_route_topk", "h3_forward", "kvouter", "combine", "VsaGeometry", "vsa_forward",
 ]
 
 
@@ -333,6 +334,101 @@ def vsa_forward(q, k, v, geom, R, kmax=None, scale=None, need_lse=False, workspa
         coarse = (coarse_attention(v, geom.perm, geom.block_len, geom.J, geom.M, E), gate)
     res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
                         need_lse=need_lse, item_order=order, coarse=coarse)
+    if need_lse:
+        return res[0], q2k_idx, q2k_num, res[1]
+    return res, q2k_idx, q2k_num
+
+
+def _segments(segments):
+    """ctypes array of bsa_segment from ints (dense token counts) and (T, H, W) tuples."""
+    arr = (L.Segment * len(segments))()
+    for k, sg in enumerate(segments):
+        if isinstance(sg, int):
+            arr[k] = L.Segment(0, sg, 0, 0)
+        else:
+            T, H, W = sg
+            arr[k] = L.Segment(1, int(T), int(H), int(W))
+    return arr
+
+
+class H3Geometry:
+    """Tables of a multi-region layout (dense prefix chunks, then the video
+    regions), built once on a device.  ``segments``: ints (dense segments of
+    that many tokens) and (T, H, W) tuples (video regions) in original order."""
+
+    def __init__(self, segments, block, device="cuda"):
+        bT, bH, bW = block
+        self.segments, self.block = list(segments), tuple(block)
+        seg = _segments(self.segments)
+        J, M, N, P, nr = (ctypes.c_int() for _ in range(5))
+        spans = (ctypes.c_int * (2 * L.H3_MAX_SEGMENTS))()
+        L.check(_lib().h3_tile_dims(seg, len(seg), bT, bH, bW, ctypes.byref(J), ctypes.byref(M), ctypes.byref(N),
+                                    ctypes.byref(P), ctypes.byref(nr), spans))
+        self.J, self.M, self.N, self.num_prefix = J.value, M.value, N.value, P.value
+        self.spans = [(spans[2 * r], spans[2 * r + 1]) for r in range(nr.value)]
+        self.perm = torch.empty(self.J * self.M, dtype=torch.int32, device=device)
+        self.block_len = torch.empty(self.J, dtype=torch.int32, device=device)
+        self.inv = torch.empty(self.N, dtype=torch.int32, device=device)
+        L.check(_lib().h3_tile_index(seg, len(seg), bT, bH, bW, _ptr(self.perm), _ptr(self.block_len),
+                                     _ptr(self.inv), _stream(self.perm.device)))
+
+    def budgets(self, drop_ratio):
+        """Keep budget of every video region for one drop ratio (or a list)."""
+        ratios = drop_ratio if isinstance(drop_ratio, (list, tuple)) else [drop_ratio] * len(self.spans)
+        return [keep_budget(r, b1 - b0) for r, (b0, b1) in zip(ratios, self.spans)]
+
+
+def h3_pool_route_topk(q, k, geom, budgets, kmax=None, scale=None, item_order=None, debug=False, out=None,
+                       workspace=None):
+    """Grouped routing over an H3 layout: context query blocks keep every
+    block, video query blocks keep the prefix plus each region's TopK.
+    Returns (q2k_idx [B,H,J,kmax], q2k_num [B,H,J]) (plus qbar, kbar with debug)."""
+    _need_cuda(q, k)
+    B, N, H, D = q.shape
+    J = geom.J
+    kmax = J if kmax is None else int(kmax)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        q2k_idx = torch.empty((B, H, J, kmax), dtype=torch.int32, device=dev)
+        q2k_num = torch.empty((B, H, J), dtype=torch.int32, device=dev)
+    else:
+        q2k_idx, q2k_num = out
+    qbar = kbar = None
+    if debug:
+        qbar = torch.empty((B, H, J, D), dtype=torch.float32, device=dev)
+        kbar = torch.empty_like(qbar)
+    if item_order is not None:
+        _need_cuda(item_order)
+        if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
+            raise ValueError("item_order must be a contiguous int32 tensor of B*H*J elements")
+    nr = len(geom.spans)
+    spans = (ctypes.c_int32 * max(1, 2 * nr))(*[v for sp in geom.spans for v in sp])
+    buds = (ctypes.c_int32 * max(1, nr))(*[int(b) for b in budgets])
+    a = L.H3RouteArgs(q=_ptr(q), k=_ptr(k), d=_desc(q), dt=_dtype(q), perm=_ptr(geom.perm),
+                      block_len=_ptr(geom.block_len), J=J, M=geom.M, num_prefix=geom.num_prefix, nregions=nr,
+                      spans=ctypes.cast(spans, ctypes.c_void_p), budgets=ctypes.cast(buds, ctypes.c_void_p),
+                      kmax=kmax, scale=scale, q2k_idx=_ptr(q2k_idx), q2k_num=_ptr(q2k_num), qbar=_ptr(qbar),
+                      kbar=_ptr(kbar), item_order=_ptr(item_order))
+    lib = _lib()
+    n = ctypes.c_size_t()
+    L.check(lib.h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    L.check(lib.h3_pool_route_topk(ctypes.byref(a), _ptr(workspace), n.value, _stream(dev)))
+    if debug:
+        return q2k_idx, q2k_num, qbar, kbar
+    return q2k_idx, q2k_num
+
+
+def h3_forward(q, k, v, geom, budgets, scale=None, need_lse=False, workspace=None):
+    """Multi-region routed attention: pool -> grouped route -> exact attention
+    over the union of kept blocks (one softmax).  Returns (out, q2k_idx, q2k_num)."""
+    B, _, H, _ = q.shape
+    order = torch.empty((B, H, geom.J), dtype=torch.int32, device=q.device)
+    q2k_idx, q2k_num = h3_pool_route_topk(q, k, geom, budgets, scale=scale, item_order=order, workspace=workspace)
+    res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
+                        need_lse=need_lse, item_order=order)
     if need_lse:
         return res[0], q2k_idx, q2k_num, res[1]
     return res, q2k_idx, q2k_num

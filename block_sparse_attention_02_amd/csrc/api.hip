@@ -149,11 +149,185 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   bsa::RouteParams rp{qbar, kbar, (int)a->d.B, (int)a->d.H, a->J, (int)a->d.D, a->R, a->kmax, a->scale,
-                      a->q2k_idx, a->q2k_num, a->E};
+                      a->q2k_idx, a->q2k_num, a->E, 0, a->J, 0, a->J, 0, 1};
   e = bsa::launch_route_topk(rp, s);
   if (e != hipSuccess || !a->item_order) return hip_status(e, "route/topk launch");
   return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, (int)(a->d.B * a->d.H), a->J, a->kmax,
                                            a->item_order, s),
+                    "item order launch");
+}
+
+// ------------------------------------------------------------------ H3 multi-region layout
+// Builds the layout parts (dense chunks first, then the videos) of a segment
+// list, with the totals.
+static bsa_status h3_build(const bsa_segment* seg, int nseg, int bT, int bH, int bW, bsa::H3Layout* L, int* J,
+                           int* N, int* num_prefix, int* nreg, int* spans) {
+  if (!seg) return fail(BSA_ERR_ARG, "h3 layout: null segment list");
+  if (nseg < 1 || nseg > BSA_H3_MAX_SEGMENTS)
+    return fail(BSA_ERR_UNSUPPORTED, "h3 layout: 1 to %d segments", BSA_H3_MAX_SEGMENTS);
+  if (bT < 1 || bH < 1 || bW < 1) return fail(BSA_ERR_SHAPE, "h3 layout: block sizes must be positive");
+  const int64_t M = (int64_t)bT * bH * bW;
+  if (M >= (int64_t)1 << 20) return fail(BSA_ERR_UNSUPPORTED, "h3 layout: block capacity too large");
+  int64_t tok0[BSA_H3_MAX_SEGMENTS];
+  int64_t off = 0;
+  for (int k = 0; k < nseg; ++k) {
+    const bsa_segment& g = seg[k];
+    tok0[k] = off;
+    if (g.video == 0) {
+      if (g.T < 0) return fail(BSA_ERR_SHAPE, "h3 layout: segment %d has a negative token count", k);
+      off += g.T;
+    } else if (g.video == 1) {
+      if (g.T < 1 || g.H < 1 || g.W < 1) return fail(BSA_ERR_SHAPE, "h3 layout: video segment %d is empty", k);
+      off += (int64_t)g.T * g.H * g.W;
+    } else {
+      return fail(BSA_ERR_ARG, "h3 layout: segment %d: video must be 0 or 1", k);
+    }
+    if (off >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "h3 layout: too many tokens");
+  }
+  L->nparts = 0;
+  L->M = (int)M;
+  L->bT = bT, L->bH = bH, L->bW = bW;
+  int64_t b = 0;
+  int np = 0, nr = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int k = 0; k < nseg; ++k) {
+      const bsa_segment& g = seg[k];
+      if (g.video != pass || (pass == 0 && g.T == 0)) continue;
+      bsa::H3Part P{};
+      P.video = pass;
+      P.tok0 = (int)tok0[k];
+      P.b0 = (int)b;
+      int64_t nb;
+      if (pass == 0) {
+        P.n = g.T;
+        nb = (g.T + M - 1) / M;
+      } else {
+        P.T = g.T, P.H = g.H, P.W = g.W;
+        P.JH = (g.H + bH - 1) / bH, P.JW = (g.W + bW - 1) / bW;
+        nb = (int64_t)((g.T + bT - 1) / bT) * P.JH * P.JW;
+      }
+      b += nb;
+      if (b * M >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "h3 layout: grid too large for int32 tables");
+      P.b1 = (int)b;
+      L->part[L->nparts++] = P;
+      if (pass == 0) {
+        np = (int)b;
+      } else {
+        if (spans) spans[2 * nr] = P.b0, spans[2 * nr + 1] = P.b1;
+        ++nr;
+      }
+    }
+  if (b < 1) return fail(BSA_ERR_SHAPE, "h3 layout: no tokens");
+  *J = (int)b;
+  *N = (int)off;
+  *num_prefix = np;
+  *nreg = nr;
+  return BSA_OK;
+}
+
+bsa_status h3_tile_dims(const bsa_segment* seg, int nseg, int bT, int bH, int bW, int* J, int* M, int* N,
+                        int* num_prefix, int* nregions, int* spans) {
+  if (!J || !M || !N || !num_prefix || !nregions) return fail(BSA_ERR_ARG, "h3_tile_dims: null output pointer");
+  bsa::H3Layout L;
+  bsa_status st = h3_build(seg, nseg, bT, bH, bW, &L, J, N, num_prefix, nregions, spans);
+  if (st != BSA_OK) return st;
+  *M = L.M;
+  return ok();
+}
+
+bsa_status h3_tile_index(const bsa_segment* seg, int nseg, int bT, int bH, int bW, int32_t* perm,
+                         int32_t* block_len, int32_t* inv, void* stream) {
+  bsa::H3Layout L;
+  int J = 0, N = 0, np = 0, nr = 0;
+  bsa_status st = h3_build(seg, nseg, bT, bH, bW, &L, &J, &N, &np, &nr, nullptr);
+  if (st != BSA_OK) return st;
+  if (!perm || !block_len) return fail(BSA_ERR_ARG, "h3_tile_index: perm and block_len are required");
+  return hip_status(bsa::launch_h3_tile_index(L, J, perm, block_len, inv, (hipStream_t)stream),
+                    "h3 tile index launch");
+}
+
+static bsa_status check_h3_route(const h3_route_args* a, int* nsel) {
+  if (!a) return fail(BSA_ERR_ARG, "h3_pool_route_topk: null args");
+  if (!a->q || !a->k || !a->perm || !a->block_len || !a->q2k_idx || !a->q2k_num)
+    return fail(BSA_ERR_ARG, "h3_pool_route_topk: q, k, perm, block_len, q2k_idx and q2k_num are required");
+  if (a->dt != BSA_BF16 && a->dt != BSA_F32) return fail(BSA_ERR_ARG, "h3_pool_route_topk: bad dtype");
+  bsa_status st = check_desc(a->d, "q/k", 1, false);
+  if (st != BSA_OK) return st;
+  if (a->d.D > 256) return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: D must be <= 256");
+  if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: J and M must be positive");
+  if (a->J > bsa::kRouteMaxJ)
+    return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: J=%d exceeds %d blocks", a->J, bsa::kRouteMaxJ);
+  if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "h3_pool_route_topk: scale must be finite");
+  if ((int64_t)a->d.B * a->d.H > 65535) return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: B*H must be <= 65535");
+  if (a->num_prefix < 0 || a->num_prefix > a->J)
+    return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: num_prefix must lie in [0, J]");
+  if (a->nregions < 0 || a->nregions > BSA_H3_MAX_SEGMENTS)
+    return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: 0 to %d regions", BSA_H3_MAX_SEGMENTS);
+  if ((a->nregions == 0) != (a->num_prefix == a->J))
+    return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: the regions must cover blocks [num_prefix, J)");
+  if (a->nregions > 0 && (!a->spans || !a->budgets))
+    return fail(BSA_ERR_ARG, "h3_pool_route_topk: spans and budgets are required");
+  int at = a->num_prefix, sel = a->num_prefix;
+  for (int r = 0; r < a->nregions; ++r) {
+    const int b0 = a->spans[2 * r], b1 = a->spans[2 * r + 1];
+    if (b0 != at || b1 <= b0 || b1 > a->J)
+      return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: region %d [%d, %d) does not continue the tiling at %d", r, b0,
+                  b1, at);
+    if (a->budgets[r] < 1 || a->budgets[r] > b1 - b0)
+      return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: budget of region %d must lie in [1, %d]", r, b1 - b0);
+    at = b1;
+    sel += a->budgets[r];
+  }
+  if (at != a->J) return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: the regions must end at J");
+  if (a->kmax < sel || (a->num_prefix > 0 && a->kmax < a->J))
+    return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: kmax must be >= %d", a->num_prefix > 0 ? a->J : sel);
+  *nsel = sel;
+  return BSA_OK;
+}
+
+bsa_status h3_pool_route_topk_ws(const h3_route_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "h3_pool_route_topk_ws: null output");
+  int nsel = 0;
+  bsa_status st = check_h3_route(a, &nsel);
+  if (st != BSA_OK) return st;
+  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  *bytes = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  return ok();
+}
+
+bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes, void* stream) {
+  int nsel = 0;
+  bsa_status st = check_h3_route(a, &nsel);
+  if (st != BSA_OK) return st;
+  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  const size_t need = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "h3_pool_route_topk: workspace of %zu bytes required", need);
+  char* w = static_cast<char*>(ws);
+  float* qbar = a->qbar;
+  float* kbar = a->kbar;
+  if (!qbar) { qbar = reinterpret_cast<float*>(w); w += one; }
+  if (!kbar) { kbar = reinterpret_cast<float*>(w); w += one; }
+  const int vec = 16 / elem_bytes(a->dt);
+  const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
+                      aligned16(a->q) && aligned16(a->k);
+  const int B = (int)a->d.B, H = (int)a->d.H, D = (int)a->d.D, J = a->J, P = a->num_prefix;
+  bsa::PoolParams pp{a->q, a->k, a->d.sB, a->d.sN, a->d.sH, B, H, D, J, a->M, a->perm, a->block_len, qbar, kbar};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  int out_off = P;
+  for (int r = 0; r < a->nregions; ++r) {
+    const int b0 = a->spans[2 * r], b1 = a->spans[2 * r + 1];
+    bsa::RouteParams rp{qbar, kbar, B, H, J, D, a->budgets[r], a->kmax, a->scale, a->q2k_idx, a->q2k_num, nullptr,
+                        P, J - P, b0, b1 - b0, out_off, 0};
+    e = bsa::launch_route_topk(rp, s);
+    if (e != hipSuccess) return hip_status(e, "grouped route/topk launch");
+    out_off += a->budgets[r];
+  }
+  e = bsa::launch_h3_fill(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, P, nsel, s);
+  if (e != hipSuccess || !a->item_order) return hip_status(e, "grouped index fill launch");
+  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, a->item_order, s),
                     "item order launch");
 }
 

@@ -44,10 +44,35 @@ struct RouteParams {
   int32_t* q2k_idx;  // [B, H, J, kmax]
   int32_t* q2k_num;  // [B, H, J]
   float* E;          // optional [B, H, J, J]
+  // Sub-problem (grouped routing): query blocks [row0, row0 + nrows) against
+  // key blocks [col0, col0 + ncols), R of them written (as global ids) to
+  // entries [out_off, out_off + R) of each row; `tail` also writes the -1
+  // fill and q2k_num = R.  The whole square: 0, J, 0, J, 0, 1.
+  int row0, nrows, col0, ncols, out_off, tail;
 };
 // Largest J the fused route + TopK kernel handles.
 constexpr int kRouteMaxJ = 4096;
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
+
+// ---- H3 multi-region layout and grouped routing ------------------------------
+constexpr int kH3MaxParts = 16;
+struct H3Part {
+  int video;       // 0: dense chunks, 1: 3D-tiled video
+  int tok0;        // first original position of the segment
+  int b0, b1;      // its block range in the layout
+  int n;           // dense: token count
+  int T, H, W, JH, JW;
+};
+struct H3Layout {
+  int nparts, M, bT, bH, bW;
+  H3Part part[kH3MaxParts];  // in layout order (dense chunks first)
+};
+hipError_t launch_h3_tile_index(const H3Layout& L, int J, int32_t* perm, int32_t* block_len, int32_t* inv,
+                                hipStream_t s);
+// Rows < num_prefix: every block; other rows: blocks [0, num_prefix), the
+// region entries already written at [num_prefix, nsel), then -1; q2k_num.
+hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int kmax, int num_prefix, int nsel,
+                          hipStream_t s);
 // Processing order of the query blocks of every (b, h): Morton order of the
 // quartile entries of their kept lists ([B*H, J] int32 output).
 hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,

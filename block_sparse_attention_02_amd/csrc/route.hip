@@ -185,8 +185,9 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   constexpr int MW = kRouteWaves * CW / 32;  // 32-bit mask words per row
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * BM;
-  const int J = p.J, D = p.D;
+  const int i0 = blockIdx.x * BM;  // local query block (global row p.row0 + i)
+  const int J = p.ncols, D = p.D;  // local key blocks j < J (global column p.col0 + j)
+  const int NR = p.nrows, JT = p.J;
   const int KS = (D + 31) / 32;
   const int DP = KS * 32 + 8;  // padded LDS row (bf16 elements)
 
@@ -197,14 +198,14 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   uint32_t* eqm = gtm + BM * MW;
   int* red = reinterpret_cast<int*>(eqm + BM * MW);  // [2][8][BM]
 
-  const float* __restrict__ qb = p.qbar + (int64_t)bh * J * D;
-  const float* __restrict__ kb = p.kbar + (int64_t)bh * J * D;
+  const float* __restrict__ qb = p.qbar + ((int64_t)bh * JT + p.row0) * D;
+  const float* __restrict__ kb = p.kbar + ((int64_t)bh * JT + p.col0) * D;
 
   // ---- stage the band's pooled queries as hi/lo bf16 (zero padded) -------------
   for (int e = threadIdx.x; e < BM * KS * 32; e += 512) {
     const int r = e / (KS * 32), d = e % (KS * 32);
     const int i = i0 + r;
-    const float x = (i < J && d < D) ? qb[(int64_t)i * D + d] : 0.f;
+    const float x = (i < NR && d < D) ? qb[(int64_t)i * D + d] : 0.f;
     const __bf16 hi = (__bf16)x;
     qhi[r * DP + d] = hi;
     qlo[r * DP + d] = (__bf16)(x - (float)hi);
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int i = i0 + 16 * rt + l16, j = w * CW + 16 * t + 4 * g + v;
-          if (i < J && j < J) p.E[((int64_t)bh * J + i) * J + j] = key_float(key[rt][t][v]);
+          if (i < NR && j < J) p.E[((int64_t)bh * JT + p.row0 + i) * JT + p.col0 + j] = key_float(key[rt][t][v]);
         }
   }
 
@@ -456,8 +457,8 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   // ---- emit kept ids in increasing order, one wave per row ----------------------
   for (int row = w; row < BM; row += kRouteWaves) {
     const int i = i0 + row;
-    if (i >= J) continue;
-    int32_t* __restrict__ out = p.q2k_idx + ((int64_t)bh * J + i) * p.kmax;
+    if (i >= NR) continue;
+    int32_t* __restrict__ out = p.q2k_idx + ((int64_t)bh * JT + p.row0 + i) * p.kmax + p.out_off;
     int ngt = 0;
     for (int wb = 0; wb < MW; wb += 64) {
       const int word = wb + lane;
@@ -483,21 +484,23 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
       int pos = sel_carry + wave_excl_scan(ns);
       while (sel) {
         const int bitpos = __ffs(sel) - 1;
-        out[pos++] = word * 32 + bitpos;
+        out[pos++] = p.col0 + word * 32 + bitpos;
         sel &= sel - 1u;
       }
       eq_carry += wave_sum(ne);
       sel_carry += wave_sum(ns);
     }
-    for (int q = p.R + lane; q < p.kmax; q += 64) out[q] = -1;
-    if (lane == 0) p.q2k_num[(int64_t)bh * J + i] = p.R;
+    if (p.tail) {
+      for (int q = p.R + lane; q < p.kmax; q += 64) out[q] = -1;
+      if (lane == 0) p.q2k_num[(int64_t)bh * JT + p.row0 + i] = p.R;
+    }
   }
 }
 
 template <int NT, int RT, int KD>
 static hipError_t launch_route_k(const RouteParams& p, size_t smem, hipStream_t s) {
   constexpr int BM = 16 * RT;
-  dim3 grid((p.J + BM - 1) / BM, p.B * p.H);
+  dim3 grid((p.nrows + BM - 1) / BM, p.B * p.H);
   route_topk_kernel<NT, RT, KD><<<grid, 512, smem, s>>>(p);
   return hipGetLastError();
 }
@@ -584,8 +587,81 @@ hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int
   return hipGetLastError();
 }
 
+// ============================================================================
+// H3 multi-region layout ("VSA 实现详解" section 5.2): dense segments cut into 1D
+// chunks of M tokens (each segment on its own) form the prefix; the video
+// regions follow, each tiled in 3D like a single video.  One thread per packed
+// slot; the block's part is found by a short scan of the (at most 16) parts.
+// ============================================================================
+__global__ void h3_tile_index_kernel(H3Layout L, int J, int32_t* __restrict__ perm,
+                                     int32_t* __restrict__ block_len, int32_t* __restrict__ inv) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int M = L.M;
+  if (p >= (int64_t)J * M) return;
+  const int b = (int)(p / M), r = (int)(p % M);
+  int k = 0;
+  while (k + 1 < L.nparts && b >= L.part[k].b1) ++k;
+  const H3Part& P = L.part[k];
+  const int lb = b - P.b0;
+  int n, tok = -1;
+  if (!P.video) {
+    n = min(M, P.n - lb * M);
+    if (r < n) tok = P.tok0 + lb * M + r;
+  } else {
+    const int bt = lb / (P.JH * P.JW), rem = lb % (P.JH * P.JW), by = rem / P.JW, bx = rem % P.JW;
+    const int t0 = bt * L.bT, y0 = by * L.bH, x0 = bx * L.bW;
+    const int nt = min(L.bT, P.T - t0), ny = min(L.bH, P.H - y0), nx = min(L.bW, P.W - x0);
+    n = nt * ny * nx;
+    if (r < n) {
+      const int dt = r / (ny * nx), rr = r % (ny * nx), dy = rr / nx, dx = rr % nx;
+      tok = P.tok0 + ((t0 + dt) * P.H + (y0 + dy)) * P.W + (x0 + dx);
+    }
+  }
+  if (r == 0) block_len[b] = n;
+  perm[p] = tok;
+  if (tok >= 0 && inv) inv[tok] = (int32_t)p;
+}
+
+hipError_t launch_h3_tile_index(const H3Layout& L, int J, int32_t* perm, int32_t* block_len, int32_t* inv,
+                                hipStream_t s) {
+  const int64_t total = (int64_t)J * L.M;
+  const int64_t blocks = (total + 255) / 256;
+  h3_tile_index_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(L, J, perm, block_len, inv);
+  return hipGetLastError();
+}
+
+// Grouped routing ("VSA 实现详解" section 5.3, exempt rule): the per-region TopK
+// launches write the region entries of every video row; this kernel writes the
+// rest -- a context row keeps every block, a video row the prefix blocks in
+// front of its region entries -- the -1 fill and the counts.  One wave per row.
+__global__ __launch_bounds__(256) void h3_fill_kernel(int32_t* __restrict__ q2k_idx, int32_t* __restrict__ q2k_num,
+                                                      int64_t rows, int J, int kmax, int num_prefix, int nsel) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int i = (int)(row % J);
+  int32_t* out = q2k_idx + row * kmax;
+  const bool context = i < num_prefix;
+  const int keep = context ? J : nsel;
+  for (int q = lane; q < kmax; q += 64) {
+    if (context ? q < J : q < num_prefix)
+      out[q] = q;
+    else if (q >= keep)
+      out[q] = -1;
+  }
+  if (lane == 0) q2k_num[row] = keep;
+}
+
+hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int kmax, int num_prefix, int nsel,
+                          hipStream_t s) {
+  const int64_t rows = (int64_t)BH * J;
+  h3_fill_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(q2k_idx, q2k_num, rows, J, kmax, num_prefix,
+                                                                       nsel);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s) {
-  const int cols_per_wave = (p.J + kRouteWaves - 1) / kRouteWaves;
+  const int cols_per_wave = (p.ncols + kRouteWaves - 1) / kRouteWaves;
   if (cols_per_wave <= 16) return launch_route_t<1, 2>(p, s);
   if (cols_per_wave <= 32) return launch_route_t<2, 2>(p, s);
   if (cols_per_wave <= 64) return launch_route_t<4, 2>(p, s);

@@ -155,6 +155,76 @@ bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes);
 bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * H3 multi-region layout ([VSA] section 5.2) and grouped routing ([VSA]
+ * section 5.3, the default "exempt" rule).
+ *
+ * A packed sequence is a list of segments in their original order: a dense
+ * segment (text, reference image, audio; video = 0, T = its token count, may
+ * be 0) or a video region (video = 1, a T x H x W grid).  Layout: every dense
+ * segment is cut on its own into 1D chunks of M = bT*bH*bW tokens (the last
+ * chunk of each segment is short, no chunk mixes segments); all dense chunks
+ * come first, in segment order (the prefix, num_prefix blocks); then every
+ * video region in order, tiled in 3D exactly as vsa_tile_index tiles one
+ * grid.  Tables as for vsa_tile_index: perm [J*M] holds original positions
+ * (segment offset + position inside the segment, t slowest, x fastest inside
+ * a video), -1 padding; block_len [J]; inv [N] optional.
+ *
+ * h3_tile_dims (host only): J, M, N (total tokens), num_prefix, the number of
+ * video regions and, when spans is not NULL, their half-open block ranges
+ * spans[2r], spans[2r+1] (room for 2*BSA_H3_MAX_SEGMENTS ints).
+ * Supported: 1 <= nseg <= BSA_H3_MAX_SEGMENTS, N and J*M below 2^31.
+ * ------------------------------------------------------------------------- */
+#define BSA_H3_MAX_SEGMENTS 16
+
+typedef struct {
+  int video;
+  int T, H, W;
+} bsa_segment;
+
+bsa_status h3_tile_dims(const bsa_segment* seg, int nseg, int bT, int bH, int bW, int* J, int* M, int* N,
+                        int* num_prefix, int* nregions, int* spans);
+bsa_status h3_tile_index(const bsa_segment* seg, int nseg, int bT, int bH, int bW, int32_t* perm,
+                         int32_t* block_len, int32_t* inv, void* stream);
+
+/* Grouped routing over a multi-region layout.  Pooled means and scores as in
+ * vsa_pool_route_topk over all J blocks; then for every batch b and head h:
+ *   query block i < num_prefix (context): keeps every block 0..J-1;
+ *   query block i >= num_prefix (video): keeps blocks 0..num_prefix-1 and, for
+ *     every region r = [spans[2r], spans[2r+1]), the budgets[r] largest
+ *     E[i, j] over the region's j (ties: lower j first);
+ * written ascending to q2k_idx[b,h,i,:] with -1 fill, count in q2k_num.  The
+ * attention over the union is bsa_forward_qouter in block mode.
+ *   spans, budgets   host arrays [2*nregions], [nregions]: the regions must
+ *                    tile [num_prefix, J) in order; 1 <= budgets[r] <= size
+ *   kmax             >= J when num_prefix > 0, and >= num_prefix + sum budgets
+ * Supported as vsa_pool_route_topk (J <= 4096, D <= 256, B*H <= 65535),
+ * nregions <= BSA_H3_MAX_SEGMENTS; nregions = 0 only with num_prefix = J.
+ * The workspace holds the pooled means: h3_pool_route_topk_ws() bytes. */
+typedef struct {
+  const void* q;
+  const void* k;
+  bsa_tdesc d;
+  bsa_dtype dt;
+  const int32_t* perm;
+  const int32_t* block_len;
+  int J, M;
+  int num_prefix;
+  int nregions;
+  const int32_t* spans;
+  const int32_t* budgets;
+  int kmax;
+  float scale;
+  int32_t* q2k_idx;
+  int32_t* q2k_num;
+  float* qbar;
+  float* kbar;
+  int32_t* item_order;
+} h3_route_args;
+
+bsa_status h3_pool_route_topk_ws(const h3_route_args* a, size_t* bytes);
+bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
  * Exact sparse attention, query-outer order.
  *
  * mode BSA_SEL_BLOCK (VSA; [VSA] sections 4, 6.2, 6.3, 6.5): every valid query

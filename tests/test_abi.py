@@ -121,3 +121,78 @@ def test_qouter_shape_checks():
     bad = L.TDesc(1, 64, 2, 128, 64 * 2 * 128, 2 * 128 + 4, 128)
     a = _qouter_args(dq=bad)
     assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_SHAPE         # stride % 8
+
+
+H3_CASES = [
+    ([130, (2, 16, 16), 60, 200, (4, 16, 16)], (2, 8, 8)),   # the page's metadata example
+    ([5, (3, 5, 6), 9, (2, 3, 3), 1, (5, 4, 2)], (2, 2, 2)),
+    ([0, (7, 9, 13)], (4, 4, 4)),                            # an empty dense segment
+    ([300, 77], (4, 4, 4)),                                  # dense only
+]
+
+
+@pytest.mark.parametrize("case", range(len(H3_CASES)))
+def test_h3_dims_match_oracle(case):
+    import oracle
+    segments, block = H3_CASES[case]
+    seg = bsa.api._segments(segments)
+    J, M, N, P, nr = (ctypes.c_int() for _ in range(5))
+    spans = (ctypes.c_int * 32)()
+    assert L.load().h3_tile_dims(seg, len(seg), *block, ctypes.byref(J), ctypes.byref(M), ctypes.byref(N),
+                                 ctypes.byref(P), ctypes.byref(nr), spans) == L.BSA_OK
+    lay = oracle.h3_layout(segments, block)
+    assert (J.value, M.value, N.value, P.value) == (lay["J"], lay["M"], lay["N"], lay["num_prefix"])
+    assert [(spans[2 * r], spans[2 * r + 1]) for r in range(nr.value)] == lay["spans"]
+
+
+@pytest.mark.parametrize("segments,status", [
+    ([], L.BSA_ERR_ARG),                 # no segment list
+    ([8] * 17, L.BSA_ERR_UNSUPPORTED),
+    ([(0, 4, 4)], L.BSA_ERR_SHAPE),
+    ([-3, (1, 4, 4)], L.BSA_ERR_SHAPE),
+    ([0, 0], L.BSA_ERR_SHAPE),
+])
+def test_h3_layout_validation(segments, status):
+    lib = L.load()
+    seg = bsa.api._segments(segments) if segments else None
+    J, M, N, P, nr = (ctypes.c_int() for _ in range(5))
+    got = lib.h3_tile_dims(seg, len(segments), 4, 4, 4, ctypes.byref(J), ctypes.byref(M), ctypes.byref(N),
+                           ctypes.byref(P), ctypes.byref(nr), None)
+    assert got == status and lib.bsa_last_error()
+    bad = (L.Segment * 1)(L.Segment(2, 4, 4, 4))
+    assert lib.h3_tile_dims(bad, 1, 4, 4, 4, ctypes.byref(J), ctypes.byref(M), ctypes.byref(N), ctypes.byref(P),
+                            ctypes.byref(nr), None) == L.BSA_ERR_ARG
+
+
+def _h3_args(spans, budgets, num_prefix=2, J=10, kmax=10):
+    d = L.TDesc(1, 640, 1, 64, 640 * 64, 64, 64)
+    sp = (ctypes.c_int32 * max(1, len(spans)))(*spans)
+    bu = (ctypes.c_int32 * max(1, len(budgets)))(*budgets)
+    a = L.H3RouteArgs(q=ctypes.c_void_p(256), k=ctypes.c_void_p(256), d=d, dt=L.BSA_BF16, perm=ctypes.c_void_p(256),
+                      block_len=ctypes.c_void_p(256), J=J, M=64, num_prefix=num_prefix, nregions=len(budgets),
+                      spans=ctypes.cast(sp, ctypes.c_void_p), budgets=ctypes.cast(bu, ctypes.c_void_p), kmax=kmax,
+                      scale=0.125, q2k_idx=ctypes.c_void_p(256), q2k_num=ctypes.c_void_p(256))
+    return a, (sp, bu)
+
+
+@pytest.mark.parametrize("spans,budgets,kw,status", [
+    ([2, 5, 5, 10], [1, 2], {}, L.BSA_OK),
+    ([2, 5, 6, 10], [1, 2], {}, L.BSA_ERR_SHAPE),           # a gap between regions
+    ([3, 5, 5, 10], [1, 2], {}, L.BSA_ERR_SHAPE),           # does not start at num_prefix
+    ([2, 5, 5, 9], [1, 2], {}, L.BSA_ERR_SHAPE),            # does not end at J
+    ([2, 5, 5, 10], [0, 2], {}, L.BSA_ERR_SHAPE),           # empty budget
+    ([2, 5, 5, 10], [4, 2], {}, L.BSA_ERR_SHAPE),           # budget above the region size
+    ([2, 5, 5, 10], [1, 2], {"kmax": 9}, L.BSA_ERR_SHAPE),  # context rows need kmax >= J
+    ([2, 5, 5, 10], [1, 2], {"num_prefix": 0, "kmax": 2}, L.BSA_ERR_SHAPE),  # below the 1 + 2 kept
+    ([2, 5, 5, 10], [1, 2], {"num_prefix": 0, "kmax": 3}, L.BSA_OK),
+    ([], [], {}, L.BSA_ERR_SHAPE),                          # video rows without regions
+    ([], [], {"num_prefix": 10}, L.BSA_OK),                 # all context
+])
+def test_h3_route_validation(spans, budgets, kw, status):
+    if kw.get("num_prefix") == 0:
+        spans = [0, 5, 5, 10]
+    a, keep = _h3_args(spans, budgets, **kw)
+    n = ctypes.c_size_t()
+    assert L.load().h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    if status == L.BSA_OK:
+        assert n.value == 2 * 10 * 64 * 4

@@ -1,0 +1,157 @@
+"""GPU parity of the H3 multi-region path against the float64 oracle: layout
+tables (bit-exact), grouped routing (bit-exact outside near-tie rows, per
+region), attention over the union of kept blocks (bf16 tolerance), and the
+H3 workload at full size (routing of four heads in full, sampled query
+blocks of every kind)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import GAP_EXEMPT, assert_attn_close, to64
+from workloads import h3_inputs, scaled, workload
+
+pytestmark = pytest.mark.gpu
+
+bsa = pytest.importorskip("block_sparse_attention_02_amd")
+DEV = torch.device("cuda:0")
+
+LAYOUTS = [
+    ([130, (2, 16, 16), 60, 200, (4, 16, 16)], (2, 8, 8)),   # the page's example (capacity 128)
+    ([77, (4, 8, 12), 30, (6, 16, 20)], (4, 4, 4)),
+    ([5, (3, 5, 6), 9, (2, 3, 3), 1, (5, 4, 2)], (2, 2, 2)),
+    ([0, (7, 9, 13)], (4, 4, 4)),
+    ([300, 77], (4, 4, 4)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYOUTS)))
+def test_layout_tables_bit_exact(case):
+    segments, block = LAYOUTS[case]
+    geom = bsa.H3Geometry(segments, block, device=DEV)
+    torch.cuda.synchronize()
+    lay = oracle.h3_layout(segments, block)
+    assert (geom.J, geom.M, geom.N, geom.num_prefix) == (lay["J"], lay["M"], lay["N"], lay["num_prefix"])
+    assert geom.spans == lay["spans"]
+    assert np.array_equal(geom.perm.cpu().numpy(), lay["perm"])
+    assert np.array_equal(geom.block_len.cpu().numpy(), lay["block_len"])
+    assert np.array_equal(geom.inv.cpu().numpy(), lay["inv"])
+
+
+ROUTE_CFGS = {
+    "page_example_m128": scaled("h3", segments=[130, (2, 16, 16), 60, 200, (4, 16, 16)], block=(2, 8, 8), h=3,
+                                keep=0.25),
+    "r2v_small": scaled("h3", segments=[77, (4, 8, 12), 30, (6, 16, 20)], h=2, keep=0.25),
+    "two_refs_d64": scaled("h3", segments=[40, (4, 8, 8), (4, 8, 12), 19, (8, 12, 16)], h=2, D=64, keep=0.2),
+    "full_grid_h2": scaled("h3", h=2),
+}
+
+
+def _oracle_route(x, cfg, lay, budgets):
+    Q, K = to64(x["q"]), to64(x["k"])
+    qbar = oracle.pool_blocks(Q, lay["perm"], lay["block_len"], lay["M"])
+    kbar = oracle.pool_blocks(K, lay["perm"], lay["block_len"], lay["M"])
+    return oracle.h3_route(qbar, kbar, lay["num_prefix"], lay["spans"], budgets)
+
+
+def _check_tables(idx, num, ref_idx, ref_num, gap, what):
+    got_idx, got_num = idx.cpu().numpy(), num.cpu().numpy()
+    assert np.array_equal(got_num, ref_num), what + ": counts differ"
+    exempt = (gap < GAP_EXEMPT).any(-1)
+    bad = ((got_idx != ref_idx).any(-1) & ~exempt).sum()
+    print("%s: %d rows, %d exempt near-ties, %d mismatches" % (what, exempt.size, int(exempt.sum()), int(bad)),
+          flush=True)
+    assert bad == 0
+    # exempt rows are still valid tables: ascending, the prefix, the right count per region
+    return got_idx
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CFGS))
+def test_grouped_route_matches_oracle(name):
+    cfg = ROUTE_CFGS[name]
+    print("case", name, flush=True)
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=DEV)
+    lay = oracle.h3_layout(cfg["segments"], cfg["block"])
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    x = h3_inputs(cfg, device=DEV)
+    idx, num, qbar, kbar = bsa.h3_pool_route_topk(x["q"], x["k"], geom, budgets, debug=True)
+    torch.cuda.synchronize()
+    Q, K = to64(x["q"]), to64(x["k"])
+    rq = oracle.pool_blocks(Q, lay["perm"], lay["block_len"], lay["M"])
+    assert (np.abs(to64(qbar) - rq) / np.maximum(1.0, np.abs(rq))).max() <= 1e-5
+    ref_idx, ref_num, gap = _oracle_route(x, cfg, lay, budgets)
+    got = _check_tables(idx, num, ref_idx, ref_num, gap, name)
+    P = geom.num_prefix
+    for row, n in zip(got.reshape(-1, geom.J), num.cpu().numpy().reshape(-1)):
+        kept = row[:n]
+        assert (np.diff(kept) > 0).all() and (row[n:] == -1).all()
+        if n < geom.J:
+            assert (kept[:P] == np.arange(P)).all()
+            for (b0, b1), R in zip(geom.spans, budgets):
+                assert ((kept >= b0) & (kept < b1)).sum() == R
+
+
+ATTN_CFGS = {
+    "r2v_m64": scaled("h3", segments=[77, (4, 8, 12), 30, (6, 16, 20)], h=2, keep=0.25),
+    "r2v_m32": scaled("h3", segments=[77, (4, 8, 12), 30, (6, 16, 20)], block=(2, 4, 4), h=2, keep=0.25),
+    "two_refs_d64": scaled("h3", segments=[40, (4, 8, 8), (4, 8, 12), 19, (8, 12, 16)], h=2, D=64, keep=0.2),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_CFGS))
+def test_forward_matches_oracle(name):
+    """pool -> grouped route -> attention on the device against the oracle's
+    attention over the device's table (validated above), LSE included."""
+    cfg = ATTN_CFGS[name]
+    print("case", name, flush=True)
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=DEV)
+    lay = oracle.h3_layout(cfg["segments"], cfg["block"])
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    x = h3_inputs(cfg, device=DEV)
+    out, idx, num, lse = bsa.h3_forward(x["q"], x["k"], x["v"], geom, budgets, need_lse=True)
+    torch.cuda.synchronize()
+    Q, K, V = to64(x["q"]), to64(x["k"]), to64(x["v"])
+    ref, ref_lse = oracle.vsa_attention(Q, K, V, lay["perm"], lay["block_len"], lay["M"], idx.cpu().numpy(),
+                                        num.cpu().numpy())
+    assert_attn_close(out, ref, "h3 forward " + name)
+    assert np.abs(to64(lse) - ref_lse).max() <= 1e-3
+    # context tokens attend to everything: dense attention
+    ctx = lay["perm"][:geom.num_prefix * geom.M]
+    ctx = ctx[ctx >= 0]
+    for hh in range(cfg["h"]):
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q[0, ctx, hh])[None, None], torch.from_numpy(K[0, :, hh])[None, None],
+            torch.from_numpy(V[0, :, hh])[None, None])[0, 0].numpy()
+        assert_attn_close(out[0, torch.as_tensor(ctx, device=DEV), hh], dense, "h3 context rows, head %d" % hh)
+
+
+def test_h3_full_size_sampled():
+    """The H3 workload at full size (146676 tokens, J = 2412, 24 heads) in the
+    launch configuration of bench.py: grouped routing of heads 0, 7, 15, 23
+    against the oracle, attention on sampled context, reference and target
+    query blocks."""
+    cfg = workload("h3")
+    print("case h3 full size", flush=True)
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=DEV)
+    lay = oracle.h3_layout(cfg["segments"], cfg["block"])
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    x = h3_inputs(cfg, device=DEV)
+    out, idx, num = bsa.h3_forward(x["q"], x["k"], x["v"], geom, budgets)
+    torch.cuda.synchronize()
+    heads = [0, 7, 15, 23]
+    hsel = torch.tensor(heads, device=DEV)
+    sub = {k_: v_[:, :, hsel] for k_, v_ in x.items()}
+    ref_idx, ref_num, gap = _oracle_route(sub, cfg, lay, budgets)
+    _check_tables(idx[:, hsel], num[:, hsel], ref_idx, ref_num, gap, "h3 full size")
+    J, P = geom.J, geom.num_prefix
+    (r0, r1), (t0, t1) = geom.spans
+    rng = np.random.default_rng(7)
+    blocks = [0, P - 1, r0, r1 - 1, t0, J - 1] + [int(v) for v in rng.integers(r0, J, 4)]
+    items = [(0, hi, i) for hi in range(len(heads)) for i in blocks]
+    Q, K, V = (to64(t) for t in (sub["q"], sub["k"], sub["v"]))
+    ref, _ = oracle.vsa_attention(Q, K, V, lay["perm"], lay["block_len"], lay["M"], idx[:, hsel].cpu().numpy(),
+                                  num[:, hsel].cpu().numpy(), items=items)
+    got = to64(out[:, :, hsel])
+    mask = ~np.isnan(ref)
+    assert_attn_close(got[mask], ref[mask], "h3 full size, sampled blocks")

@@ -14,7 +14,7 @@ exactly the tensors the device computed on.
 """
 
 from .configs import WORKLOADS, workload, scaled
-from .gen import vsa_inputs, nsa_inputs, msa_inputs, kept_lists, coarse_gate
+from .gen import vsa_inputs, nsa_inputs, msa_inputs, kept_lists, coarse_gate, h3_inputs
 
 __all__ = [
     "kept_lists",
@@ -23,6 +23,7 @@ __all__ = [
     "workload",
     "scaled",
     "vsa_inputs",
+    "h3_inputs",
     "nsa_inputs",
     "msa_inputs",
 ]

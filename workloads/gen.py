@@ -8,6 +8,11 @@ vsa   Z_q, Z_k, Z_v ~ N(0,1) [B, N, h, D] float32 in token order
       ~ N(0, sigma^2) of shape [B, h, ceil(T/cT), ceil(H/cH), ceil(W/cW), D],
       constant over each (cT, cH, cW) cell of the grid and added to every
       token of the cell; finally cast to the workload dtype (bf16: RNE).
+h3    Z_q, Z_k, Z_v ~ N(0,1) [B, N, h, D] float32 over the whole sequence in
+      original order; then, when offset_sigma > 0, for each video region in
+      order and each of q, k, v, an offset field ~ N(0, sigma^2) of shape
+      [B, h, ceil(T/cT), ceil(H/cH), ceil(W/cW), D] added to the region's
+      tokens (dense segments get none); cast to the workload dtype.
 nsa   q [B,T,HQ,D], k [B,T,H,D], v [B,T,H,D] ~ N(0,1) -> bf16; block counts
       U{1..S} [B,T,H]; per chunk of tokens, uniform priorities [B,n,H,NB].
       A token's row holds its own block t // BS plus the c-1 lowest-priority
@@ -58,6 +63,34 @@ def vsa_inputs(cfg, device="cpu"):
             field = field.permute(0, 2, 3, 4, 1, 5).reshape(B, N, h, D)
             out[name] += field
             del c, field
+    dt = _DT[cfg["dtype"]]
+    return {k_: v_.to(dt) for k_, v_ in out.items()}
+
+
+def h3_inputs(cfg, device="cpu"):
+    """Q, K, V [B, N, h, D] of a multi-region sequence (dict of tensors)."""
+    B, h, D = cfg["B"], cfg["h"], cfg["D"]
+    segs = cfg["segments"]
+    sizes = [s if isinstance(s, int) else s[0] * s[1] * s[2] for s in segs]
+    N = sum(sizes)
+    g = _gen(device, cfg["seed"])
+    out = {name: torch.randn((B, N, h, D), generator=g, device=device, dtype=torch.float32)
+           for name in ("q", "k", "v")}
+    sigma = float(cfg.get("offset_sigma", 0.0))
+    if sigma > 0.0:
+        cT, cH, cW = cfg.get("offset_cell", cfg["block"])
+        off = 0
+        for s, n in zip(segs, sizes):
+            if not isinstance(s, int):
+                T, H, W = s
+                nT, nH, nW = -(-T // cT), -(-H // cH), -(-W // cW)
+                for name in ("q", "k", "v"):
+                    c = torch.randn((B, h, nT, nH, nW, D), generator=g, device=device, dtype=torch.float32) * sigma
+                    field = (c.repeat_interleave(cT, 2).repeat_interleave(cH, 3)
+                             .repeat_interleave(cW, 4)[:, :, :T, :H, :W])
+                    out[name][:, off:off + n] += field.permute(0, 2, 3, 4, 1, 5).reshape(B, n, h, D)
+                    del c, field
+            off += n
     dt = _DT[cfg["dtype"]]
     return {k_: v_.to(dt) for k_, v_ in out.items()}
 

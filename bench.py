@@ -1,6 +1,6 @@
 """Throughput of routed block-sparse attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight|coarse] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight|coarse|h3] [--no-cpu-baseline]
 
 A step is one pass of the routed block-sparse attention hot path over one
 batch of synthetic input already resident in HBM:
@@ -16,6 +16,11 @@ batch of synthetic input already resident in HBM:
   reweight  the video step with Spark-Reweight: block summaries from the mean
          query of each head, and attention over the kept blocks plus one
          virtual token for each of the other 1728 blocks.
+  h3     an H3 reference-to-video sequence (text 256, reference video
+         8x48x80, audio 500, target video 30x48x80; 146676 tokens, J = 2412):
+         multi-region tables -> pooling -> grouped routing (context rows
+         dense, video rows keep the prefix + 10 % of each video region) ->
+         exact attention over the union.
   coarse the video step with the coarse pooled-V branch: the routing scores
          are kept, V is pooled, C = softmax(E) V_bar over all 1920 blocks,
          and the attention epilogue adds gate * C to every token.
@@ -483,6 +488,158 @@ def cpu_baseline_coarse(ctx, budget_s):
             "ms_per_head": round(per_head_s * 1e3, 1)}
 
 
+def bench_h3(args):
+    """H3 multi-region sequence: layout tables, pooling, grouped routing and
+    attention over the union of kept blocks."""
+    import ctypes
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import h3_inputs, workload
+
+    cfg = workload("h3")
+    dev = torch.device("cuda:0")
+    B, h, D = cfg["B"], cfg["h"], cfg["D"]
+    x = h3_inputs(cfg, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=dev)
+    J, M, N, P = geom.J, geom.M, geom.N, geom.num_prefix
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    q2k_idx = torch.empty((B, h, J, J), dtype=torch.int32, device=dev)
+    q2k_num = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    order = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    L = bsa._lib
+    lib = L.load()
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = bsa.api._stream(dev)
+    Pp = bsa.api._ptr
+    seg = bsa.api._segments(cfg["segments"])
+
+    def tile():
+        L.check(lib.h3_tile_index(seg, len(seg), *cfg["block"], Pp(geom.perm), Pp(geom.block_len), Pp(geom.inv),
+                                  s_ptr))
+
+    nr = len(geom.spans)
+    spans = (ctypes.c_int32 * (2 * nr))(*[b for sp in geom.spans for b in sp])
+    buds = (ctypes.c_int32 * nr)(*budgets)
+    ra = L.H3RouteArgs(q=Pp(q), k=Pp(k), d=bsa.api._desc(q), dt=L.BSA_BF16, perm=Pp(geom.perm),
+                       block_len=Pp(geom.block_len), J=J, M=M, num_prefix=P, nregions=nr,
+                       spans=ctypes.cast(spans, ctypes.c_void_p), budgets=ctypes.cast(buds, ctypes.c_void_p),
+                       kmax=J, scale=1.0 / D ** 0.5, q2k_idx=Pp(q2k_idx), q2k_num=Pp(q2k_num), item_order=Pp(order))
+    nws = ctypes.c_size_t()
+    L.check(lib.h3_pool_route_topk_ws(ctypes.byref(ra), ctypes.byref(nws)))
+    ws = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+
+    def route():
+        L.check(lib.h3_pool_route_topk(ctypes.byref(ra), Pp(ws), nws.value, s_ptr))
+
+    qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
+    qa.perm, qa.block_len, qa.J, qa.M = Pp(geom.perm), Pp(geom.block_len), J, M
+    qa.q2k_idx, qa.q2k_num, qa.kmax = Pp(q2k_idx), Pp(q2k_num), J
+    qa.item_order = Pp(order)
+
+    def attend():
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+
+    stages = (("tile", tile), ("route", route), ("attn", attend))
+    ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
+
+    def step(i=None):
+        for name, fn in stages:
+            if i is not None:
+                ev[name][i][0].record(stream)
+            fn()
+            if i is not None:
+                ev[name][i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in ev}
+    pairs_nominal = float(q2k_num.sum().item())          # kept (query block, key block) pairs
+    flops = 4.0 * D * M * M * pairs_nominal              # every pair counted as full blocks
+    valid_flops = 4.0 * D * bsa.metrics.vsa_valid_pairs(geom.block_len, q2k_idx, q2k_num)
+    attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
+    route_bytes = 2 * q.numel() * q.element_size() + 2 * B * h * J * D * 4 + 4 * float(q2k_num.sum().item())
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + per-cell offsets in the video regions, no dataset or weights)",
+        "config": {"workload": "h3_r2v_multi_region", "B": B, "heads": h,
+                   "segments": [s_ if isinstance(s_, int) else list(s_) for s_ in cfg["segments"]],
+                   "block": list(cfg["block"]), "D": D, "J": J, "M": M, "tokens": N, "prefix_blocks": P,
+                   "video_spans": [list(sp) for sp in geom.spans], "budgets": budgets},
+        "ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "attn_tflops_nominal": round(attn_tflops, 2),
+        "attn_tflops_valid": round(valid_flops / (ms["attn"] * 1e-3) / 1e12, 2),
+        "route_gbps": round(route_bytes / (ms["route"] * 1e-3) / 1e9, 1),
+        "pct_hbm_route": round(100 * route_bytes / (ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "roofline": {"kernel": "vsa4_kernel over the grouped index table (bsa_forward_qouter, block mode)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profiled_traffic("vsa4_kernel_h3.md",
+                                                  ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
+    }
+    ctx = dict(cfg=cfg, x=x, budgets=budgets, pairs_per_head=pairs_nominal / (B * h))
+    return res, ctx
+
+
+def cpu_baseline_h3(ctx, budget_s):
+    """Oracle on a bounded sample: head 0's layout, pooling and grouped routing
+    over all blocks, and attention for as many query blocks as fit."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg, x = ctx["cfg"], ctx["x"]
+    D = cfg["D"]
+    Q = x["q"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    K = x["k"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    V = x["v"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    lay = oracle.h3_layout(cfg["segments"], cfg["block"])
+    J, M = lay["J"], lay["M"]
+    qbar = oracle.pool_blocks(Q, lay["perm"], lay["block_len"], M)
+    kbar = oracle.pool_blocks(K, lay["perm"], lay["block_len"], M)
+    idx, num, _ = oracle.h3_route(qbar, kbar, lay["num_prefix"], lay["spans"], ctx["budgets"])
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(J)  # a random sample of query blocks of every kind
+    done, pairs_done = 0, 0
+    t1 = time.perf_counter()
+    while done < J and time.perf_counter() - t1 < budget_s:
+        blocks = order[done:done + 16]
+        oracle.vsa_attention(Q, K, V, lay["perm"], lay["block_len"], M, idx, num,
+                             items=[(0, 0, int(i)) for i in blocks])
+        pairs_done += int(num[0, 0, blocks].sum())
+        done += len(blocks)
+    t_attn = time.perf_counter() - t1
+    pairs_head = float(num[0, 0].sum())
+    per_head_s = t_route + t_attn * pairs_head / max(pairs_done, 1)
+    flops_head = 4.0 * D * M * M * pairs_head
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops_head / per_head_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "head 0 of the h3 workload: float64 layout, pooling and grouped routing over all %d blocks "
+                      "(%.1f s) and attention for %d random query blocks (%d of %d kept pairs, %.1f s), scaled "
+                      "to one head by kept pairs" % (J, t_route, done, pairs_done, int(pairs_head), t_attn),
+            "ms_per_head": round(per_head_s * 1e3, 1)}
+
+
 def _time(fn, steps, warmup, stream):
     """Average ms of fn() over `steps` launches, HIP events on `stream`."""
     import torch
@@ -632,7 +789,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight", "coarse"])
+    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight", "coarse", "h3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -660,6 +817,10 @@ def main(argv=None):
         res, ctx = bench_reweight(args)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_reweight(ctx, args.cpu_seconds)
+    elif args.workload == "h3":
+        res, ctx = bench_h3(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_h3(ctx, args.cpu_seconds)
     elif args.workload == "coarse":
         res, ctx = bench_coarse(args)
         if not args.no_cpu_baseline:

@@ -16,7 +16,8 @@ it is written directly from the source pages:
   K1 local partials and the exact LSE combine of the KV-outer schedule.
 * "深度解读|Spark-H3：从注意力几何到稀疏内核代码" (jefxiong.cn) -- the
   Spark-Reweight block summaries and the joint softmax of exact tokens and
-  virtual tokens.
+  virtual tokens; the Spark-Reblock cross-moment metric and equal-capacity
+  hierarchical split.
 
 Every function computes the plain definition in float64 with NumPy: no online
 softmax, no blocking, no reverse index.  Each one is pinned by the ``not gpu``
@@ -35,10 +36,12 @@ from .attention import (
 from .reweight import anchor_queries, block_summaries, virtual_logit, reweight_attention
 from .coarse import coarse_attention, add_coarse
 from .h3 import h3_layout, h3_route
+from . import reblock
 
 __all__ = [
     "h3_layout",
     "h3_route",
+    "reblock",
     "tile_dims",
     "tile_index",
     "keep_budget",

@@ -19,7 +19,10 @@ the page's own equal-capacity binary grouping with landmark-estimated
 principal directions:
 
 * features: u_j = z_j / |z_j| with z_j = k_j^T L, L the lower Cholesky factor
-  of M_Q + ridge * tr(M_Q) / D * I (the ridge keeps the factor defined);
+  of M_Q + lam * I, lam = ridge * tr(M_Q) / D (ridge * 1 when the trace is 0;
+  the page mentions a ridge in the source without its value, 1e-4 here keeps
+  the factor well defined in fp32); a zero key has no score direction and
+  gets the zero feature;
 * tree: a node holding n tokens spans c = ceil(n / M) leaves; its first child
   takes floor(c / 2) leaves (floor(c / 2) * M tokens), the second the rest; a
   node with c <= 1 is a leaf.  The ranges depend on N and M only;
@@ -38,7 +41,7 @@ import numpy as np
 
 N_LANDMARKS = 32
 POWER_ITERS = 16
-DEFAULT_RIDGE = 1e-6
+DEFAULT_RIDGE = 1e-4
 
 
 def second_moment(X):
@@ -50,11 +53,13 @@ def second_moment(X):
 
 
 def metric_factor(M, ridge=DEFAULT_RIDGE):
-    """Lower Cholesky factor of M + ridge * tr(M) / D * I (last two axes)."""
+    """Lower Cholesky factor of M + lam * I, lam = ridge * tr(M) / D (ridge when
+    the trace is 0), over the last two axes."""
     M = np.asarray(M, dtype=np.float64)
     D = M.shape[-1]
     tr = np.trace(M, axis1=-2, axis2=-1)[..., None, None]
-    return np.linalg.cholesky(M + ridge * tr / D * np.eye(D))
+    lam = ridge * np.where(tr > 0, tr / D, 1.0)
+    return np.linalg.cholesky(M + lam * np.eye(D))
 
 
 def key_features(K, Q, ridge=DEFAULT_RIDGE):
@@ -62,7 +67,8 @@ def key_features(K, Q, ridge=DEFAULT_RIDGE):
     L = metric_factor(second_moment(Q), ridge)
     Kt = np.transpose(np.asarray(K, dtype=np.float64), (0, 2, 1, 3))
     z = np.matmul(Kt, L)
-    return z / np.linalg.norm(z, axis=-1, keepdims=True)
+    nrm = np.linalg.norm(z, axis=-1, keepdims=True)
+    return np.where(nrm > 0, z / np.where(nrm > 0, nrm, 1.0), 0.0)
 
 
 def tree_slots(N, M):

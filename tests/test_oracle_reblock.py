@@ -28,6 +28,16 @@ def test_factor_reproduces_the_ridged_moment():
     assert np.max(np.abs(L @ np.swapaxes(L, -1, -2) - (M + 1e-3 * tr / 6 * np.eye(6)))) < 1e-12
 
 
+def test_zero_trace_and_zero_key():
+    Q = np.zeros((1, 5, 1, 3))
+    L = rb.metric_factor(rb.second_moment(Q), ridge=0.25)
+    assert np.allclose(L[0, 0], 0.5 * np.eye(3))
+    K = np.ones((1, 5, 1, 3))
+    K[0, 2] = 0.0
+    U = rb.key_features(K, Q + 1.0)
+    assert np.array_equal(U[0, 0, 2], np.zeros(3)) and np.all(np.isfinite(U))
+
+
 def test_cosine_identity_with_score_profiles():
     """The cosine of two keys' features equals the cosine of their score
     profiles over all queries (no ridge: the identity is exact)."""

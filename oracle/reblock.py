@@ -28,8 +28,9 @@ principal directions:
   node with c <= 1 is a leaf.  The ranges depend on N and M only;
 * split of a node (its tokens in their current order): landmarks are the
   tokens at ranks floor((2s + 1) n / 64), s = 0..31; X = their features minus
-  the landmark mean; a = 16 power iterations of G = X X^T from the all-ones
-  vector (normalised each time); direction v = X^T a / |X^T a|, signed so
+  the landmark mean; a = 16 power iterations of G = X X^T from the ramp
+  a_s = s - 15.5 (normalised each time; the all-ones vector would be useless,
+  centring puts it in G's null space); direction v = X^T a / |X^T a|, signed so
   that its largest-magnitude entry (lowest index on ties) is positive; the
   node's tokens are stably sorted by u . v, the first floor(c / 2) * M go to
   the first child, the rest to the second;
@@ -96,7 +97,8 @@ def split_direction(U):
     X = U[ranks]
     X = X - X.mean(axis=0)
     G = X @ X.T
-    a = np.ones(N_LANDMARKS) / np.sqrt(N_LANDMARKS)
+    a = np.arange(N_LANDMARKS) - (N_LANDMARKS - 1) / 2.0
+    a = a / np.linalg.norm(a)
     for _ in range(POWER_ITERS):
         a = G @ a
         nrm = np.linalg.norm(a)
@@ -152,7 +154,8 @@ def check_orders(U, orders, M, eps):
     more than eps is a violation), and the children are the cut of that order.
     A node whose order is the reverse one (the direction's sign taken the other
     way at a near-tie of the largest entry) counts as a flip.
-    Returns (splits, violations, flips)."""
+    Returns (splits, violations, flips, worst): worst is the largest amount by
+    which a consecutive pair of an accepted split is out of order."""
     N = U.shape[0]
     slots = tree_slots(N, M)
     if len(orders) != len(slots):
@@ -160,6 +163,7 @@ def check_orders(U, orders, M, eps):
     if not np.array_equal(orders[0], np.arange(N)):
         raise ValueError("level 0 must be the token order")
     splits = violations = flips = 0
+    worst = 0.0
     for li, lvl in enumerate(slots[:-1]):
         cur, nxt = orders[li], orders[li + 1]
         for (s, e, c) in lvl:
@@ -173,10 +177,67 @@ def check_orders(U, orders, M, eps):
                 continue
             v = split_direction(U[members])
             p = U[nxt[s:e]] @ v
-            if np.all(np.diff(p) >= -eps):
+            dp = np.diff(p)
+            if np.all(dp >= -eps):
+                worst = max(worst, float(-dp.min()) if len(dp) else 0.0)
                 continue
-            if np.all(np.diff(p) <= eps):
+            if np.all(dp <= eps):
                 flips += 1
+                worst = max(worst, float(dp.max()) if len(dp) else 0.0)
                 continue
             violations += 1
-    return splits, violations, flips
+    return splits, violations, flips, worst
+
+
+def check_splits(U, orders, dirs, M, eps, tau):
+    """Validity of a device's tree given its own split directions.
+
+    The top principal direction of 32 nearly isotropic landmarks is ill
+    conditioned (close leading eigenvalues), so fp32 and float64 runs of the
+    same 16 power iterations may end on different, equally principal axes.
+    What is unique is the quality of the axis; the rest must be valid.  At every
+    split, with the node's tokens in the device's current order and the
+    oracle's features U: the device's direction v (dirs[level][slot]) must
+    (a) have unit length and lie in the span of the centred landmarks (relative
+    residual <= 1e-3), (b) have its largest-magnitude entry positive, (c) be as
+    principal as the oracle's own direction v_o: |X v|^2 >= (1 - tau) |X v_o|^2,
+    and (d) order the node's tokens: the device's next order sorted by U . v up
+    to eps.  Unsplit nodes must keep their order.
+    Returns (splits, violations, worst inversion, worst quotient shortfall)."""
+    N = U.shape[0]
+    slots = tree_slots(N, M)
+    if len(orders) != len(slots) or not np.array_equal(orders[0], np.arange(N)):
+        raise ValueError("expected %d levels starting from the token order" % len(slots))
+    splits = violations = 0
+    worst_inv = worst_short = 0.0
+    for li, lvl in enumerate(slots[:-1]):
+        cur, nxt = orders[li], orders[li + 1]
+        for si, (s, e, c) in enumerate(lvl):
+            if c <= 1:
+                violations += int(not np.array_equal(cur[s:e], nxt[s:e]))
+                continue
+            splits += 1
+            members = cur[s:e]
+            if not np.array_equal(np.sort(members), np.sort(nxt[s:e])):
+                violations += 1
+                continue
+            n = e - s
+            ranks = [(2 * t + 1) * n // (2 * N_LANDMARKS) for t in range(N_LANDMARKS)]
+            X = U[members[ranks]]
+            X = X - X.mean(axis=0)
+            v = np.asarray(dirs[li][si], dtype=np.float64)
+            coef, *_ = np.linalg.lstsq(X.T, v, rcond=None)
+            resid = np.linalg.norm(X.T @ coef - v)
+            vo = split_direction(U[members])
+            qo = float(np.sum((X @ vo) ** 2))
+            qg = float(np.sum((X @ v) ** 2))
+            short = (qo - qg) / qo if qo > 0 else 0.0
+            worst_short = max(worst_short, short)
+            ok = abs(np.linalg.norm(v) - 1.0) <= 1e-5 and resid <= 1e-3 and v[int(np.argmax(np.abs(v)))] > 0
+            ok = ok and short <= tau
+            dp = np.diff(U[nxt[s:e]] @ v)
+            inv = float(-dp.min()) if len(dp) else 0.0
+            worst_inv = max(worst_inv, inv)
+            ok = ok and inv <= eps
+            violations += int(not ok)
+    return splits, violations, worst_inv, worst_short

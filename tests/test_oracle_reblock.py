@@ -84,6 +84,18 @@ def test_principal_axis_of_landmarks():
     assert v[np.argmax(np.abs(v))] > 0
 
 
+def test_centred_gram_null_space_and_ramp_start():
+    """Centring puts the all-ones vector in the landmark Gram matrix's null
+    space, so the iteration starts from the ramp s - 15.5, which is not."""
+    rng = np.random.default_rng(57)
+    X = rng.standard_normal((32, 16))
+    X -= X.mean(axis=0)
+    G = X @ X.T
+    assert np.max(np.abs(G @ np.ones(32))) < 1e-12
+    ramp = np.arange(32) - 15.5
+    assert np.linalg.norm(G @ ramp) > 1.0 and abs(ramp @ ramp - 2728.0) < 1e-12
+
+
 def test_interleaved_clusters_are_separated():
     """Keys of two score patterns interleaved in token order (a seeded random
     half each); the root's equal-capacity split puts each pattern in one child
@@ -127,11 +139,44 @@ def test_checker_accepts_the_rule_and_catches_swaps():
     U = rng.standard_normal((N, D))
     U /= np.linalg.norm(U, axis=1, keepdims=True)
     orders = rb.reblock_orders(U, M)
-    assert rb.check_orders(U, orders, M, 1e-9) == (len([1 for lvl in rb.tree_slots(N, M)[:-1]
-                                                         for (s, e, c) in lvl if c > 1]), 0, 0)
+    splits, viol, flips, worst = rb.check_orders(U, orders, M, 1e-9)
+    assert (splits, viol, flips) == (len([1 for lvl in rb.tree_slots(N, M)[:-1] for (s, e, c) in lvl if c > 1]), 0, 0)
+    assert worst == 0.0
     # a planted swap of two far-apart positions of the root's sorted order
     # breaks the root split
     bad = [o.copy() for o in orders]
     bad[1][[0, 150]] = bad[1][[150, 0]]
-    _, viol, _ = rb.check_orders(U, bad, M, 1e-9)
+    _, viol, _, _ = rb.check_orders(U, bad, M, 1e-9)
     assert viol > 0
+
+
+def test_split_checker_on_oracle_directions():
+    """check_splits accepts the oracle's own tree with its own directions and
+    rejects a direction that is valid but not principal."""
+    rng = np.random.default_rng(56)
+    N, D, M = 400, 6, 64
+    U = rng.standard_normal((N, D)) * np.array([3.0, 1.0, 1.0, 0.5, 0.5, 0.2])
+    U /= np.linalg.norm(U, axis=1, keepdims=True)
+    orders = rb.reblock_orders(U, M)
+    slots = rb.tree_slots(N, M)
+    dirs = []
+    for li, lvl in enumerate(slots[:-1]):
+        level = np.zeros((len(lvl), D))
+        for si, (s, e, c) in enumerate(lvl):
+            if c > 1:
+                level[si] = rb.split_direction(U[orders[li][s:e]])
+        dirs.append(level)
+    splits, viol, inv, short = rb.check_splits(U, orders, dirs, M, 1e-12, 1e-9)
+    assert viol == 0 and inv == 0.0 and short <= 1e-12 and splits > 0
+    # the root's direction replaced by its least principal landmark axis
+    n = N
+    ranks = [(2 * t + 1) * n // 64 for t in range(32)]
+    X = U[ranks] - U[ranks].mean(axis=0)
+    w, V = np.linalg.eigh(X.T @ X)
+    weak = V[:, 0] * np.sign(V[np.argmax(np.abs(V[:, 0])), 0])
+    bad_dirs = [d.copy() for d in dirs]
+    bad_dirs[0][0] = weak
+    bad_orders = [o.copy() for o in orders]
+    bad_orders[1] = orders[0][np.argsort(U @ weak, kind="stable")]
+    _, viol, _, short = rb.check_splits(U, bad_orders, bad_dirs, M, 1e-12, 1e-3)
+    assert viol >= 1 and short > 0.5

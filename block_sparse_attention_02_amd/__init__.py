@@ -24,6 +24,8 @@ from .api import (
     H3Geometry,
     h3_pool_route_topk,
     h3_forward,
+    spark_reblock,
+    reblock_forward,
 )
 from . import metrics
 
@@ -46,5 +48,7 @@ __all__ = [
     "H3Geometry",
     "h3_pool_route_topk",
     "h3_forward",
+    "spark_reblock",
+    "reblock_forward",
     "metrics",
 ]

@@ -48,7 +48,7 @@ class RouteArgs(ctypes.Structure):
                 ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
                 ("R", _i32), ("kmax", _i32), ("scale", _f32),
                 ("q2k_idx", _p), ("q2k_num", _p),
-                ("qbar", _p), ("kbar", _p), ("E", _p), ("item_order", _p)]
+                ("qbar", _p), ("kbar", _p), ("E", _p), ("item_order", _p), ("perm_bh_stride", _i64)]
 
 
 class QOuterArgs(ctypes.Structure):
@@ -60,7 +60,7 @@ class QOuterArgs(ctypes.Structure):
                 ("blk_idx", _p), ("blk_cnt", _p), ("S", _i32), ("BS", _i32), ("causal", _i32),
                 ("lse", _p), ("item_order", _p),
                 ("k_sum", _p), ("v_sum", _p), ("b_sum", _p),
-                ("coarse", _p), ("gate", _p)]
+                ("coarse", _p), ("gate", _p), ("perm_bh_stride", _i64)]
 
 
 class Segment(ctypes.Structure):
@@ -76,6 +76,12 @@ class H3RouteArgs(ctypes.Structure):
                 ("num_prefix", _i32), ("nregions", _i32), ("spans", _p), ("budgets", _p),
                 ("kmax", _i32), ("scale", _f32), ("q2k_idx", _p), ("q2k_num", _p),
                 ("qbar", _p), ("kbar", _p), ("item_order", _p)]
+
+
+class ReblockArgs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k", _p), ("d", TDesc), ("dt", _i32), ("M", _i32), ("ridge", _f32),
+                ("perm", _p), ("block_len", _p), ("moment", _p), ("factor", _p), ("features", _p),
+                ("levels", _p), ("dirs", _p)]
 
 
 class CoarseArgs(ctypes.Structure):
@@ -116,6 +122,9 @@ PROTOTYPES = {
     "h3_tile_index": (_i32, [ctypes.POINTER(Segment), _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
     "h3_pool_route_topk_ws": (_i32, [ctypes.POINTER(H3RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "h3_pool_route_topk": (_i32, [ctypes.POINTER(H3RouteArgs), _p, ctypes.c_size_t, _p]),
+    "spark_reblock_dims": (_i32, [_i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "spark_reblock_ws": (_i32, [ctypes.POINTER(ReblockArgs), ctypes.POINTER(ctypes.c_size_t)]),
+    "spark_reblock": (_i32, [ctypes.POINTER(ReblockArgs), _p, ctypes.c_size_t, _p]),
     "vsa_coarse_ws": (_i32, [ctypes.POINTER(CoarseArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "vsa_coarse": (_i32, [ctypes.POINTER(CoarseArgs), _p, ctypes.c_size_t, _p]),
     "spark_summaries_ws": (_i32, [ctypes.POINTER(SummaryArgs), ctypes.POINTER(ctypes.c_size_t)]),

@@ -16,7 +16,7 @@ from . import _lib as L
 __all__ = [
     "tile_dims", "tile_index", "keep_budget", "pool_route_topk", "route_workspace_bytes",
     "attention_vsa", "attention_nsa", "coarse_attention", "spark_summaries", "H3Geometry",
-    "h3_pool_route_topk", "h3_forward", "kvouter", "combine", "VsaGeometry", "vsa_forward",
+    "h3_pool_route_topk", "h3_forward", "spark_reblock", "reblock_forward", "kvouter", "combine", "VsaGeometry", "vsa_forward",
 ]
 
 
@@ -98,7 +98,7 @@ def route_workspace_bytes(q, J, M, R, kmax=None, debug=False):
 
 
 def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug=False,
-                    out=None, workspace=None, item_order=None, scores=None):
+                    out=None, workspace=None, item_order=None, scores=None, perm_bh_stride=0):
     """Per-block means, routing scores and TopK index table.
 
     q, k: [B, N, H, D] (bf16 or float32).  Returns (q2k_idx [B,H,J,kmax],
@@ -106,6 +106,8 @@ def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug
     ``item_order`` (optional int32 [B,H,J] tensor) is filled with a processing
     order of the query blocks for attention_vsa.  ``scores`` (optional
     contiguous float32 [B,H,J,J] tensor) receives E without the debug outputs.
+    ``perm_bh_stride``: 0 (one shared table) or the distance between the
+    per-(b, h) tables of ``perm`` (e.g. J*M for spark_reblock's layouts).
     """
     _need_cuda(q, k, perm, block_len)
     B, N, H, D = q.shape
@@ -134,6 +136,7 @@ def pool_route_topk(q, k, perm, block_len, J, M, R, kmax=None, scale=None, debug
         if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
             raise ValueError("item_order must be a contiguous int32 tensor of B*H*J elements")
     a = _route_args(q, k, perm, block_len, J, M, R, kmax, scale, q2k_idx, q2k_num, qbar, kbar, E, item_order)
+    a.perm_bh_stride = int(perm_bh_stride)
     n = ctypes.c_size_t()
     L.check(_lib().vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None or workspace.numel() < n.value:
@@ -204,13 +207,14 @@ def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, nee
 
 
 def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
-                  item_order=None, summaries=None, coarse=None):
+                  item_order=None, summaries=None, coarse=None, perm_bh_stride=0):
     """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
     ``item_order``: optional processing order (from pool_route_topk).
     ``summaries``: optional (k_sum, v_sum, b_sum) from spark_summaries; every
     block a query block does not keep then enters through its virtual token.
     ``coarse``: optional (C, gate) -- C fp32 [B,H,J,D] from coarse_attention,
-    gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added."""
+    gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added.
+    ``perm_bh_stride``: per-(b, h) tables in ``perm`` (as in pool_route_topk)."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -221,6 +225,7 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
     a = _qouter_args(q, k, v, out, scale, L.BSA_SEL_BLOCK, lse)
     a.perm, a.block_len, a.J, a.M = _ptr(perm), _ptr(block_len), J, M
     a.q2k_idx, a.q2k_num, a.kmax = _ptr(q2k_idx), _ptr(q2k_num), q2k_idx.shape[-1]
+    a.perm_bh_stride = int(perm_bh_stride)
     if item_order is not None:
         _need_cuda(item_order)
         if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
@@ -432,3 +437,59 @@ def h3_forward(q, k, v, geom, budgets, scale=None, need_lse=False, workspace=Non
     if need_lse:
         return res[0], q2k_idx, q2k_num, res[1]
     return res, q2k_idx, q2k_num
+
+
+def spark_reblock(q, k, M=64, ridge=1e-4, debug=False, workspace=None):
+    """Spark-Reblock key layout per (batch, head), reused by the queries.
+
+    q, k: bf16 [B, N, H, D] with the same strides.  Returns (perm int32
+    [B*H, J*M], block_len int32 [J]); with ``debug`` also the fp32 moment and
+    factor [B*H, D, D], the unit features [B*H, N, D], the per-level token
+    orders int32 [nlevels, B*H, N] and split directions fp32
+    [nlevels-1, B*H, 2^(nlevels-2), D].  Use with perm_bh_stride = J*M."""
+    _need_cuda(q, k)
+    if q.stride() != k.stride() or q.shape != k.shape:
+        raise ValueError("q and k must share shape and strides")
+    B, N, H, D = q.shape
+    dev = q.device
+    J, nl = ctypes.c_int(), ctypes.c_int()
+    lib = _lib()
+    L.check(lib.spark_reblock_dims(N, int(M), ctypes.byref(J), ctypes.byref(nl)))
+    J, nl = J.value, nl.value
+    perm = torch.empty((B * H, J * M), dtype=torch.int32, device=dev)
+    block_len = torch.empty(J, dtype=torch.int32, device=dev)
+    moment = factor = features = levels = dirs = None
+    if debug:
+        moment = torch.empty((B * H, D, D), dtype=torch.float32, device=dev)
+        factor = torch.empty_like(moment)
+        features = torch.empty((B * H, N, D), dtype=torch.float32, device=dev)
+        levels = torch.empty((nl, B * H, N), dtype=torch.int32, device=dev)
+        dirs = torch.zeros((max(nl - 1, 1), B * H, 1 << max(nl - 2, 0), D), dtype=torch.float32, device=dev)
+    a = L.ReblockArgs(q=_ptr(q), k=_ptr(k), d=_desc(q), dt=_dtype(q), M=int(M), ridge=float(ridge), perm=_ptr(perm),
+                      block_len=_ptr(block_len), moment=_ptr(moment), factor=_ptr(factor),
+                      features=_ptr(features), levels=_ptr(levels), dirs=_ptr(dirs))
+    n = ctypes.c_size_t()
+    L.check(lib.spark_reblock_ws(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    L.check(lib.spark_reblock(ctypes.byref(a), _ptr(workspace), n.value, _stream(dev)))
+    if debug:
+        return perm, block_len, moment, factor, features, levels, dirs
+    return perm, block_len
+
+
+def reblock_forward(q, k, v, R, M=64, ridge=1e-4, scale=None, need_lse=False):
+    """Reblocked routed attention: Spark-Reblock key layout (reused by the
+    queries) -> pool -> route -> TopK -> exact attention, outputs at the
+    tokens' positions.  Returns (out, perm, q2k_idx, q2k_num)."""
+    B, N, H, _ = q.shape
+    perm, block_len = spark_reblock(q, k, M=M, ridge=ridge)
+    J = block_len.numel()
+    order = torch.empty((B, H, J), dtype=torch.int32, device=q.device)
+    q2k_idx, q2k_num = pool_route_topk(q, k, perm, block_len, J, M, R, scale=scale, item_order=order,
+                                       perm_bh_stride=J * M)
+    res = attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=scale, need_lse=need_lse,
+                        item_order=order, perm_bh_stride=J * M)
+    if need_lse:
+        return res[0], perm, q2k_idx, q2k_num, res[1]
+    return res, perm, q2k_idx, q2k_num

@@ -116,6 +116,8 @@ static bsa_status check_route(const vsa_route_args* a) {
   if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "vsa_pool_route_topk: scale must be finite");
   if ((int64_t)a->d.B * a->d.H > 65535)
     return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: B*H must be <= 65535");
+  if (a->perm_bh_stride < 0 || (a->perm_bh_stride > 0 && a->perm_bh_stride < (int64_t)a->J * a->M))
+    return fail(BSA_ERR_SHAPE, "vsa_pool_route_topk: perm_bh_stride must be 0 or >= J*M");
   return BSA_OK;
 }
 
@@ -144,7 +146,7 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
                       aligned16(a->q) && aligned16(a->k);
   bsa::PoolParams pp{a->q, a->k, a->d.sB, a->d.sN, a->d.sH, (int)a->d.B, (int)a->d.H, (int)a->d.D, a->J, a->M,
-                     a->perm, a->block_len, qbar, kbar};
+                     a->perm, a->block_len, qbar, kbar, a->perm_bh_stride};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
@@ -312,7 +314,7 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
                       aligned16(a->q) && aligned16(a->k);
   const int B = (int)a->d.B, H = (int)a->d.H, D = (int)a->d.D, J = a->J, P = a->num_prefix;
-  bsa::PoolParams pp{a->q, a->k, a->d.sB, a->d.sN, a->d.sH, B, H, D, J, a->M, a->perm, a->block_len, qbar, kbar};
+  bsa::PoolParams pp{a->q, a->k, a->d.sB, a->d.sN, a->d.sH, B, H, D, J, a->M, a->perm, a->block_len, qbar, kbar, 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
@@ -376,6 +378,10 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
       if (!aligned16(a->k_sum) || !aligned16(a->v_sum) || (reinterpret_cast<uintptr_t>(a->b_sum) & 3))
         return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: k_sum/v_sum must be 16-byte and b_sum 4-byte aligned");
     }
+    if (a->perm_bh_stride < 0 || (a->perm_bh_stride > 0 && a->perm_bh_stride < (int64_t)a->J * a->M))
+      return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: perm_bh_stride must be 0 or >= J*M");
+    if (a->perm_bh_stride && a->k_sum)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: summaries need one shared perm table");
     if (a->coarse || a->gate) {
       if (!a->coarse || !a->gate) return fail(BSA_ERR_ARG, "bsa_forward_qouter: coarse and gate go together");
       if (!aligned16(a->coarse) || !aligned16(a->gate))
@@ -387,7 +393,7 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
                          a->perm, a->block_len, a->q2k_idx, a->q2k_num,
                          (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
                          scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum,
-                         a->coarse, a->gate};
+                         a->coarse, a->gate, a->perm_bh_stride};
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   if (a->mode == BSA_SEL_TOKEN) {
@@ -447,7 +453,7 @@ bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void*
                       aligned16(a->v);
   // the pooling kernel of the routing step, run on V alone
   bsa::PoolParams pp{a->v, a->v, a->d.sB, a->d.sN, a->d.sH, (int)a->d.B, (int)a->d.H, (int)a->d.D, a->J, a->M,
-                     a->perm, a->block_len, vbar, vbar};
+                     a->perm, a->block_len, vbar, vbar, 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s, 1);
   if (e != hipSuccess) return hip_status(e, "pool launch");
@@ -514,6 +520,102 @@ bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_byte
   bsa::SummaryParams sp{a->k, a->v, a->d.sB, a->d.sN, a->d.sH, B, H, D, a->J, a->M,
                         a->perm, a->block_len, anchor, a->scale, a->k_sum, a->v_sum, a->b_sum};
   return hip_status(bsa::launch_summaries(sp, s), "summary launch");
+}
+
+// ------------------------------------------------------------------------ Spark-Reblock
+bsa_status spark_reblock_dims(int N, int M, int* J, int* nlevels) {
+  if (!J || !nlevels) return fail(BSA_ERR_ARG, "spark_reblock_dims: null output pointer");
+  if (N < 1 || M < 1) return fail(BSA_ERR_SHAPE, "spark_reblock_dims: N and M must be positive");
+  const int64_t jj = ((int64_t)N + M - 1) / M;
+  if (jj > 65536 || jj * M >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "spark_reblock_dims: at most 65536 leaves");
+  *J = (int)jj;
+  *nlevels = bsa::reblock_levels(N, M);
+  return ok();
+}
+
+namespace {
+struct ReblockWs {
+  size_t part, moment, factor, features, dirs, keys, vals, order, sort, total;
+};
+
+ReblockWs reblock_ws_layout(const spark_reblock_args* a) {
+  const int64_t BH = a->d.B * a->d.H, N = a->d.N, D = a->d.D;
+  const int64_t nc = (N + 2047) / 2048;
+  const int nlev = bsa::reblock_levels((int)N, a->M);
+  const int64_t slots = (int64_t)1 << (nlev > 1 ? nlev - 2 : 0);
+  ReblockWs w{};
+  w.part = round_up((size_t)(nc * BH * D * D * 4));
+  w.moment = 0;
+  w.factor = a->factor ? 0 : round_up((size_t)(BH * D * D * 4));
+  w.features = a->features ? 0 : round_up((size_t)(BH * N * D * 4));
+  w.dirs = round_up((size_t)(BH * slots * D * 4));
+  w.keys = round_up((size_t)(BH * N * 8));
+  w.vals = round_up((size_t)(BH * N * 4));
+  w.order = round_up((size_t)(BH * N * 4));
+  w.sort = round_up(bsa::reblock_sort_bytes(BH * N, (int)BH));
+  w.total = w.part + w.factor + w.features + w.dirs + 2 * w.keys + w.vals + 2 * w.order + w.sort;
+  return w;
+}
+}  // namespace
+
+static bsa_status check_reblock(const spark_reblock_args* a) {
+  if (!a) return fail(BSA_ERR_ARG, "spark_reblock: null args");
+  if (!a->q || !a->k || !a->perm || !a->block_len)
+    return fail(BSA_ERR_ARG, "spark_reblock: q, k, perm and block_len are required");
+  if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "spark_reblock: bf16 only");
+  bsa_status st = check_desc(a->d, "q/k", 8, true);
+  if (st != BSA_OK) return st;
+  if (a->d.D != 64 && a->d.D != 128) return fail(BSA_ERR_UNSUPPORTED, "spark_reblock: D must be 64 or 128");
+  if (a->M != 16 && a->M != 32 && a->M != 64) return fail(BSA_ERR_UNSUPPORTED, "spark_reblock: M must be 16, 32 or 64");
+  if (a->d.B * a->d.H > 65535) return fail(BSA_ERR_UNSUPPORTED, "spark_reblock: B*H must be <= 65535");
+  if (a->d.B * a->d.H * a->d.N >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "spark_reblock: B*H*N must be below 2^31");
+  int J = 0, nl = 0;
+  if ((st = spark_reblock_dims((int)a->d.N, a->M, &J, &nl)) != BSA_OK) return st;
+  if (!(a->ridge > 0.f) || !std::isfinite(a->ridge)) return fail(BSA_ERR_ARG, "spark_reblock: ridge must be > 0");
+  if (!aligned16(a->q) || !aligned16(a->k) || (a->factor && !aligned16(a->factor)) ||
+      (a->features && !aligned16(a->features)) || (a->dirs && !aligned16(a->dirs)))
+    return fail(BSA_ERR_SHAPE, "spark_reblock: q, k, factor, features and dirs must be 16-byte aligned");
+  return BSA_OK;
+}
+
+bsa_status spark_reblock_ws(const spark_reblock_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "spark_reblock_ws: null output");
+  bsa_status st = check_reblock(a);
+  if (st != BSA_OK) return st;
+  *bytes = reblock_ws_layout(a).total;
+  return ok();
+}
+
+bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes, void* stream) {
+  bsa_status st = check_reblock(a);
+  if (st != BSA_OK) return st;
+  const ReblockWs w = reblock_ws_layout(a);
+  if (!ws || ws_bytes < w.total) return fail(BSA_ERR_WORKSPACE, "spark_reblock: workspace of %zu bytes required", w.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(BSA_ERR_WORKSPACE, "spark_reblock: workspace must be 256-byte aligned");
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t n) { char* r = p; p += n; return r; };
+  bsa::ReblockParams rp{};
+  rp.q = a->q, rp.k = a->k, rp.sB = a->d.sB, rp.sN = a->d.sN, rp.sH = a->d.sH;
+  rp.B = (int)a->d.B, rp.H = (int)a->d.H, rp.N = (int)a->d.N, rp.D = (int)a->d.D, rp.M = a->M;
+  rp.ridge = a->ridge;
+  rp.part = reinterpret_cast<float*>(take(w.part));
+  rp.moment = a->moment;
+  rp.factor = a->factor ? a->factor : reinterpret_cast<float*>(take(w.factor));
+  rp.features = a->features ? a->features : reinterpret_cast<float*>(take(w.features));
+  rp.dirs = reinterpret_cast<float*>(take(w.dirs));
+  rp.keys0 = reinterpret_cast<uint64_t*>(take(w.keys));
+  rp.keys1 = reinterpret_cast<uint64_t*>(take(w.keys));
+  rp.vals0 = reinterpret_cast<int32_t*>(take(w.vals));
+  rp.order0 = reinterpret_cast<int32_t*>(take(w.order));
+  rp.order1 = reinterpret_cast<int32_t*>(take(w.order));
+  rp.sort_tmp = take(w.sort);
+  rp.sort_bytes = w.sort;
+  rp.levels = a->levels, rp.perm = a->perm, rp.block_len = a->block_len;
+  rp.dirs_out = a->dirs;
+  return hip_status(bsa::launch_reblock(rp, (hipStream_t)stream), "reblock launch");
 }
 
 // ------------------------------------------------------------------------ KV-outer

@@ -193,6 +193,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int M = p.M;
+  const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
 
   const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
   const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
@@ -218,7 +219,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
 
   // ---- query rows: B operand of S^T, lane l holds row 32w + l%32 ----
   const int qrow = 32 * w + (lane & 31);
-  const int qtok = p.perm[(int64_t)i * M + min(qrow, ni - 1)];
+  const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
   bf16x8 qop[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
@@ -240,7 +241,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
   // Copies in flight, oldest first, at the top of iteration pc:
   //   K(pc) [LPT], ids(pc+1) [1], V(pc) [LPT]
   // ids(pc+1) land before K(pc+1) is staged (after QK^T); V(pc) before PV.
-  const i32x4 prs = make_rsrc(p.perm, (uint32_t)p.J * (uint32_t)M * 4u);
+  const i32x4 prs = make_rsrc(perm, (uint32_t)p.J * (uint32_t)M * 4u);
   int* ids = Ids + 64 * w;
   const uint32_t ids_lds = lds_offset(ids);
   uint32_t rows[LPT];
@@ -673,6 +674,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   constexpr int M = 64;
+  const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
 
   const __bf16* __restrict__ qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
   const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
@@ -680,7 +682,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const uint32_t row_bytes = (uint32_t)(p.kv_sN * 2);
   const uint32_t slice_bytes = (uint32_t)((p.N - 1) * p.kv_sN * 2 + D * 2);
   const i32x4 krs = make_rsrc(kg, slice_bytes), vrs = make_rsrc(vg, slice_bytes);
-  const i32x4 prs = make_rsrc(p.perm, (uint32_t)p.J * (uint32_t)M * 4u);
+  const i32x4 prs = make_rsrc(perm, (uint32_t)p.J * (uint32_t)M * 4u);
   const uint32_t kv_lds = lds_offset(KV);
   // buffer x: K tile at kv_lds + x*4*TILE bytes, V tile TILE*2 bytes after it
   auto kbuf = [&](int x) { return kv_lds + (uint32_t)(x * 4 * TILE); };
@@ -731,7 +733,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 
   // ---- query rows: B operand of S^T, lane l holds row 32hq + l%32 ----
   const int qrow = 32 * hq + (lane & 31);
-  const int qtok = p.perm[(int64_t)i * M + min(qrow, ni - 1)];
+  const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
   bf16x8 qop[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
@@ -1032,6 +1034,7 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   if (i < 0) return;  // not a block index (whole workgroup)
   const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
+  const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
   const int ni = p.block_len[i];
   const int num = min(p.q2k_num[bh * p.J + i], p.kmax);
@@ -1039,7 +1042,7 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   const float* qg = reinterpret_cast<const float*>(p.q) + b * p.q_sB + hh * p.q_sH;
   const float* kg = reinterpret_cast<const float*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
   const float* vg = reinterpret_cast<const float*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
-  const int qtok = p.perm[(int64_t)i * p.M + min(row, ni - 1)];
+  const int qtok = perm[(int64_t)i * p.M + min(row, ni - 1)];
   float qv[HD], ov[HD];
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
@@ -1054,7 +1057,7 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
     __syncthreads();
     for (int e = threadIdx.x; e < nj * D; e += 128) {
       const int r = e / D, d = e % D;
-      const int64_t tok = p.perm[(int64_t)j * p.M + r];
+      const int64_t tok = perm[(int64_t)j * p.M + r];
       Kt[e] = kg[tok * p.kv_sN + d];
       Vt[e] = vg[tok * p.kv_sN + d];
     }

@@ -22,6 +22,7 @@ struct PoolParams {
   const int32_t* block_len;
   float* qbar;  // [B, H, J, D]
   float* kbar;
+  int64_t perm_bh_stride;  // elements between the tables of consecutive (b, h); 0: one shared table
 };
 // `vec`: D, strides and base pointers allow 16-byte vector loads.  ntensors:
 // 2 pools q and k, 1 pools q only.
@@ -53,6 +54,34 @@ struct RouteParams {
 // Largest J the fused route + TopK kernel handles.
 constexpr int kRouteMaxJ = 4096;
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
+
+// ---- Spark-Reblock ------------------------------------------------------------------
+struct ReblockParams {
+  const void* q;  // bf16 [B, N, H, D] views sharing strides
+  const void* k;
+  int64_t sB, sN, sH;
+  int B, H, N, D, M;
+  float ridge;
+  float* part;      // [ceil(N/2048), BH, D, D] partial moments
+  float* moment;    // optional [BH, D, D]
+  float* factor;    // [BH, D, D]
+  float* features;  // [BH, N, D]
+  float* dirs;      // [BH, max slots, D]
+  float* dirs_out;  // optional [nlevels - 1, BH, max slots, D]: every level's directions
+  uint64_t* keys0;  // [BH*N] each
+  uint64_t* keys1;
+  int32_t* vals0;
+  int32_t* order0;
+  int32_t* order1;
+  void* sort_tmp;
+  size_t sort_bytes;
+  int32_t* levels;     // optional [nlevels, BH, N]
+  int32_t* perm;       // [BH, J*M]
+  int32_t* block_len;  // [J]
+};
+int reblock_levels(int N, int M);
+size_t reblock_sort_bytes(int64_t total, int BH);
+hipError_t launch_reblock(const ReblockParams& p, hipStream_t s);
 
 // ---- H3 multi-region layout and grouped routing ------------------------------
 constexpr int kH3MaxParts = 16;
@@ -124,6 +153,7 @@ struct VsaAttnParams {
   // optional coarse branch (M = 64, bf16): out += gate[h, :] * C[b, h, i, :]
   const float* coarse;  // [B, H, J, D]
   const float* gate;    // [H, D]
+  int64_t perm_bh_stride;  // elements between the perm tables of consecutive (b, h); 0: shared
 };
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
 

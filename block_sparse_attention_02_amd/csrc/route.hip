@@ -67,15 +67,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const int n = p.block_len[i];
   const int cpr = p.D / VW;  // vector chunks per head row
   const int nch = p.H * cpr;
-  const int32_t* __restrict__ members = p.perm + (int64_t)i * p.M;
   const T* __restrict__ xb = x + (int64_t)b * p.sB;
   for (int c0 = 0; c0 < nch; c0 += 256 * CPT) {
     float acc[CPT][VW];
     int64_t off[CPT];
+    const int32_t* members[CPT];  // the block's members in this chunk's head (per-head tables)
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = min(c0 + (int)threadIdx.x + 256 * u, nch - 1);
       off[u] = (int64_t)(c / cpr) * p.sH + (int64_t)(c % cpr) * VW;
+      members[u] = p.perm + ((int64_t)b * p.H + c / cpr) * p.perm_bh_stride + (int64_t)i * p.M;
 #pragma unroll
       for (int e = 0; e < VW; ++e) acc[u][e] = 0.f;
     }
@@ -83,9 +84,11 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
       Vec v[UT][CPT];
 #pragma unroll
       for (int rr = 0; rr < UT; ++rr) {
-        const T* row = xb + (int64_t)members[min(r + rr, n - 1)] * p.sN;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) v[rr][u] = *reinterpret_cast<const Vec*>(row + off[u]);
+        for (int u = 0; u < CPT; ++u) {
+          const T* row = xb + (int64_t)members[u][min(r + rr, n - 1)] * p.sN;
+          v[rr][u] = *reinterpret_cast<const Vec*>(row + off[u]);
+        }
       }
 #pragma unroll
       for (int rr = 0; rr < UT; ++rr) {

@@ -130,6 +130,10 @@ int vsa_budget(double drop_ratio, int J);
  *           quartile entries q2k_idx[.., (n-1)/4], [(n-1)/2], [3(n-1)/4],
  *           each scaled to 10 bits, ties by block index).  It is a processing
  *           order for bsa_forward_qouter and changes no result.
+ * perm_bh_stride  0: perm is one table shared by every (b, h); else each
+ *           (b, h) has its own table at perm + (b*H + h) * perm_bh_stride
+ *           (>= J*M; per-head layouts such as spark_reblock's), block_len is
+ *           shared.
  * Supported: 1 <= R <= J <= 4096, D <= 256, any N.  The workspace holds the
  * pooled means: vsa_pool_route_topk_ws() bytes.
  * ------------------------------------------------------------------------- */
@@ -149,6 +153,7 @@ typedef struct {
   float* kbar;
   float* E;
   int32_t* item_order;
+  int64_t perm_bh_stride;
 } vsa_route_args;
 
 bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes);
@@ -294,6 +299,9 @@ typedef struct {
    * contiguous and 16-byte aligned; both or neither. */
   const float* coarse;
   const float* gate;
+  /* optional, BSA_SEL_BLOCK: per-(b, h) tables, as in vsa_route_args (0:
+   * shared); not with summaries. */
+  int64_t perm_bh_stride;
 } bsa_qouter_args;
 
 bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
@@ -372,6 +380,58 @@ typedef struct {
 
 bsa_status spark_summaries_ws(const spark_summary_args* a, size_t* bytes);
 bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Spark-Reblock key layout ([Spark] sections 04, 05, 06).
+ *
+ * For every batch b and head h (the key layout, reused by the queries):
+ *   M_Q = Q^T Q / N (uncentred, fp32), L = chol(M_Q + lam I) with
+ *   lam = ridge * tr(M_Q) / D (ridge when the trace is 0; a pivot that fp32
+ *   rounding pushes below lam is clamped to lam);
+ *   u_j = z_j / |z_j|, z_j = k_j^T L (0 for a zero key): cos(u_i, u_j) is the
+ *   cosine of keys i and j's score profiles over all queries;
+ *   an equal-capacity binary tree of leaves of M tokens: a node of n tokens
+ *   spans c = ceil(n/M) leaves, its first child takes floor(c/2)*M of them;
+ *   at each split the node's tokens (in their current order, the root in
+ *   token order) give 32 landmarks at ranks floor((2s+1) n / 64), the top
+ *   principal direction of the centred landmarks (16 power iterations on
+ *   their Gram matrix from the ramp s - 15.5; largest entry positive), and
+ *   are stably sorted by u . v (fp32); the first child is the first part.
+ *   perm[(b*H + h)*J*M + j*M + r] = token r of leaf j (left to right), -1 past
+ *   N; block_len[j] = M except the last leaf's N - (J-1)*M.  Use the tables
+ *   with perm_bh_stride = J*M in vsa_pool_route_topk and bsa_forward_qouter.
+ *   q, k       bf16 [B, N, H, D] views sharing the descriptor d; D in {64, 128},
+ *              strides multiples of 8 elements, 16-byte aligned
+ *   M          16, 32 or 64; J = ceil(N / M) <= 65536; B*H <= 65535
+ *   ridge      > 0 (1e-4 is the documented default)
+ *   moment, factor  optional fp32 [B*H, D, D] outputs (factor lower-triangular)
+ *   features        optional fp32 [B*H, N, D] output (else in the workspace)
+ *   levels          optional int32 [nlevels, B*H, N]: the token order after
+ *                   every level (level 0 = token order), for checking
+ *   dirs            optional fp32 [nlevels - 1, B*H, S, D], S = 2^(nlevels-2):
+ *                   the split direction of node (slot) s of every level
+ *                   (entries of nodes that do not split are left untouched)
+ * spark_reblock_dims (host only): J and the number of levels for N and M.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  bsa_tdesc d;
+  bsa_dtype dt;
+  int M;
+  float ridge;
+  int32_t* perm;
+  int32_t* block_len;
+  float* moment;
+  float* factor;
+  float* features;
+  int32_t* levels;
+  float* dirs;
+} spark_reblock_args;
+
+bsa_status spark_reblock_dims(int N, int M, int* J, int* nlevels);
+bsa_status spark_reblock_ws(const spark_reblock_args* a, size_t* bytes);
+bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
  * KV-outer schedule ([MSA] sections 5-8).

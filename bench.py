@@ -1,6 +1,7 @@
 """Throughput of routed block-sparse attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight|coarse|h3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload video|nsa|msa|reweight|coarse|h3|reblock]
+                    [--no-cpu-baseline]
 
 A step is one pass of the routed block-sparse attention hot path over one
 batch of synthetic input already resident in HBM:
@@ -21,6 +22,9 @@ batch of synthetic input already resident in HBM:
          multi-region tables -> pooling -> grouped routing (context rows
          dense, video rows keep the prefix + 10 % of each video region) ->
          exact attention over the union.
+  reblock the video step on Spark-Reblock layouts: per head the query-side
+         second moment, key features and an equal-capacity tree of 64-token
+         leaves, then pool/route/TopK and attention over the per-head tables.
   coarse the video step with the coarse pooled-V branch: the routing scores
          are kept, V is pooled, C = softmax(E) V_bar over all 1920 blocks,
          and the attention epilogue adds gate * C to every token.
@@ -640,6 +644,149 @@ def cpu_baseline_h3(ctx, budget_s):
             "ms_per_head": round(per_head_s * 1e3, 1)}
 
 
+def bench_reblock(args):
+    """Video workload on Spark-Reblock key layouts (reused by the queries)."""
+    import ctypes
+    import torch
+    import block_sparse_attention_02_amd as bsa
+    from workloads import vsa_inputs, workload
+
+    cfg = workload("video")
+    dev = torch.device("cuda:0")
+    T, H, W = cfg["grid"]
+    B, h, D, R = cfg["B"], cfg["h"], cfg["D"], cfg["R"]
+    N = T * H * W
+    M = 64
+    x = vsa_inputs(cfg, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    L = bsa._lib
+    lib = L.load()
+    Jc, nl = ctypes.c_int(), ctypes.c_int()
+    L.check(lib.spark_reblock_dims(N, M, ctypes.byref(Jc), ctypes.byref(nl)))
+    J = Jc.value
+    perm = torch.empty((B * h, J * M), dtype=torch.int32, device=dev)
+    block_len = torch.empty(J, dtype=torch.int32, device=dev)
+    q2k_idx = torch.empty((B, h, J, R), dtype=torch.int32, device=dev)
+    q2k_num = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    order = torch.empty((B, h, J), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = bsa.api._stream(dev)
+    P = bsa.api._ptr
+    rb = L.ReblockArgs(q=P(q), k=P(k), d=bsa.api._desc(q), dt=L.BSA_BF16, M=M, ridge=1e-4, perm=P(perm),
+                       block_len=P(block_len))
+    nrb = ctypes.c_size_t()
+    L.check(lib.spark_reblock_ws(ctypes.byref(rb), ctypes.byref(nrb)))
+    rws = torch.empty(nrb.value, dtype=torch.uint8, device=dev)
+
+    def reblock():
+        L.check(lib.spark_reblock(ctypes.byref(rb), P(rws), nrb.value, s_ptr))
+
+    ra = bsa.api._route_args(q, k, perm, block_len, J, M, R, R, 1.0 / D ** 0.5, q2k_idx, q2k_num, None, None, None,
+                             order)
+    ra.perm_bh_stride = J * M
+    ws = torch.empty(bsa.route_workspace_bytes(q, J, M, R), dtype=torch.uint8, device=dev)
+
+    def route():
+        L.check(lib.vsa_pool_route_topk(ctypes.byref(ra), P(ws), ws.numel(), s_ptr))
+
+    qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
+    qa.perm, qa.block_len, qa.J, qa.M = P(perm), P(block_len), J, M
+    qa.q2k_idx, qa.q2k_num, qa.kmax = P(q2k_idx), P(q2k_num), R
+    qa.item_order = P(order)
+    qa.perm_bh_stride = J * M
+
+    def attend():
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+
+    stages = (("reblock", reblock), ("route", route), ("attn", attend))
+    ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
+
+    def step(i=None):
+        for name, fn in stages:
+            if i is not None:
+                ev[name][i][0].record(stream)
+            fn()
+            if i is not None:
+                ev[name][i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in ev}
+    flops = 4.0 * B * h * N * D * R * M
+    attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + per-cell offsets, no dataset or weights)",
+        "config": {"workload": "video_dit_vsa_spark_reblock", "B": B, "heads": h, "grid": list(cfg["grid"]),
+                   "D": D, "J": J, "M": M, "R": R, "tokens": N, "tree_levels": nl.value},
+        "ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "roofline": {"kernel": "vsa4_kernel over per-head reblocked tables (bsa_forward_qouter, block mode)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profiled_traffic("vsa4_kernel_reblock.md",
+                                                  ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
+    }
+    return res, dict(cfg=cfg, x=x)
+
+
+def cpu_baseline_reblock(ctx, budget_s):
+    """Oracle on a bounded sample: head 0's moment, features and tree over all
+    115200 tokens, then pooling, routing and attention for as many query
+    blocks as fit."""
+    import numpy as np
+    import oracle
+    from oracle import reblock as rbo
+    from threadpoolctl import threadpool_info
+
+    cfg, x = ctx["cfg"], ctx["x"]
+    D, R, M = cfg["D"], cfg["R"], 64
+    Q = x["q"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    K = x["k"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    V = x["v"][:, :, :1].float().cpu().numpy().astype(np.float64)
+    N = Q.shape[1]
+    t0 = time.perf_counter()
+    U = rbo.key_features(K, Q)[0, 0]
+    perm, block_len = rbo.reblock_tables(rbo.reblock_orders(U, M)[-1], M)
+    J = len(block_len)
+    qbar = oracle.pool_blocks(Q, perm, block_len, M)
+    kbar = oracle.pool_blocks(K, perm, block_len, M)
+    idx, num, _ = oracle.select_topk(oracle.routing_matrix(qbar, kbar), R)
+    t_prep = time.perf_counter() - t0
+    done = 0
+    t1 = time.perf_counter()
+    while done < J and time.perf_counter() - t1 < budget_s:
+        items = [(0, 0, i) for i in range(done, min(J, done + 32))]
+        oracle.vsa_attention(Q, K, V, perm, block_len, M, idx, num, items=items)
+        done += len(items)
+    t_attn = time.perf_counter() - t1
+    per_head_s = t_prep + t_attn * J / done
+    flops_head = 4.0 * N * D * R * M
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops_head / per_head_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "head 0 of the video workload: float64 reblock layout, pooling, routing and TopK over all "
+                      "%d blocks (%.1f s) and attention for %d of %d query blocks (%.1f s), scaled to one head"
+                      % (J, t_prep, done, J, t_attn),
+            "ms_per_head": round(per_head_s * 1e3, 1)}
+
+
 def _time(fn, steps, warmup, stream):
     """Average ms of fn() over `steps` launches, HIP events on `stream`."""
     import torch
@@ -789,7 +936,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight", "coarse", "h3"])
+    ap.add_argument("--workload", default="video", choices=["video", "nsa", "msa", "reweight", "coarse", "h3", "reblock"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -817,6 +964,10 @@ def main(argv=None):
         res, ctx = bench_reweight(args)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_reweight(ctx, args.cpu_seconds)
+    elif args.workload == "reblock":
+        res, ctx = bench_reblock(args)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_reblock(ctx, args.cpu_seconds)
     elif args.workload == "h3":
         res, ctx = bench_h3(args)
         if not args.no_cpu_baseline:

@@ -546,15 +546,15 @@ ReblockWs reblock_ws_layout(const spark_reblock_args* a) {
   const int64_t slots = (int64_t)1 << (nlev > 1 ? nlev - 2 : 0);
   ReblockWs w{};
   w.part = round_up((size_t)(nc * BH * D * D * 4));
-  w.moment = 0;
+  w.moment = a->moment ? 0 : round_up((size_t)(BH * D * D * 4));
   w.factor = a->factor ? 0 : round_up((size_t)(BH * D * D * 4));
-  w.features = a->features ? 0 : round_up((size_t)(BH * N * D * 4));
+  w.features = round_up((size_t)(BH * N * D * 2));  // fp16 features (the debug output is a copy)
   w.dirs = round_up((size_t)(BH * slots * D * 4));
   w.keys = round_up((size_t)(BH * N * 8));
   w.vals = round_up((size_t)(BH * N * 4));
   w.order = round_up((size_t)(BH * N * 4));
   w.sort = round_up(bsa::reblock_sort_bytes(BH * N, (int)BH));
-  w.total = w.part + w.factor + w.features + w.dirs + 2 * w.keys + w.vals + 2 * w.order + w.sort;
+  w.total = w.part + w.moment + w.factor + w.features + w.dirs + 2 * w.keys + w.vals + 2 * w.order + w.sort;
   return w;
 }
 }  // namespace
@@ -602,9 +602,10 @@ bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes,
   rp.B = (int)a->d.B, rp.H = (int)a->d.H, rp.N = (int)a->d.N, rp.D = (int)a->d.D, rp.M = a->M;
   rp.ridge = a->ridge;
   rp.part = reinterpret_cast<float*>(take(w.part));
-  rp.moment = a->moment;
+  rp.moment = a->moment ? a->moment : reinterpret_cast<float*>(take(w.moment));
   rp.factor = a->factor ? a->factor : reinterpret_cast<float*>(take(w.factor));
-  rp.features = a->features ? a->features : reinterpret_cast<float*>(take(w.features));
+  rp.features = reinterpret_cast<_Float16*>(take(w.features));
+  rp.features32 = a->features;
   rp.dirs = reinterpret_cast<float*>(take(w.dirs));
   rp.keys0 = reinterpret_cast<uint64_t*>(take(w.keys));
   rp.keys1 = reinterpret_cast<uint64_t*>(take(w.keys));

@@ -65,7 +65,8 @@ struct ReblockParams {
   float* part;      // [ceil(N/2048), BH, D, D] partial moments
   float* moment;    // optional [BH, D, D]
   float* factor;    // [BH, D, D]
-  float* features;  // [BH, N, D]
+  _Float16* features;   // [BH, N, D] fp16 unit features
+  float* features32;  // optional fp32 copy of the same values
   float* dirs;      // [BH, max slots, D]
   float* dirs_out;  // optional [nlevels - 1, BH, max slots, D]: every level's directions
   uint64_t* keys0;  // [BH*N] each

@@ -82,77 +82,87 @@ int reblock_levels(int N, int M) {
   return depth + 1;
 }
 
-// ---- second moment -----------------------------------------------------------------
+// ---- second moment ---------------------------------------------------------------------
+// Partial Q^T Q over a 2048-token chunk on the matrix cores: bf16 products are
+// exact in fp32, accumulation in fp32.  The chunk is staged transposed
+// (QT[d][t]) so that one 16-byte read gives a lane its 8 consecutive tokens of
+// one channel, which is both the A fragment (rows d1) and, for C = Q^T Q, the
+// B fragment (columns d2) of a 32 x 32 x 16 product.
 template <int D>
 __global__ __launch_bounds__(256) void moment_partial_kernel(const __bf16* __restrict__ q, int64_t sB, int64_t sN,
                                                              int64_t sH, int H, int N, float* __restrict__ part) {
-  constexpr int T = D / 16;  // tile edge per thread
-  constexpr int TOK = 32;    // tokens staged per step
-  __shared__ __align__(16) float xs[TOK][D];
+  constexpr int DT = D / 32;       // 32-channel tiles
+  constexpr int TOK = 64;          // tokens staged per step
+  constexpr int TPAD = TOK + 8;    // padded row of the transposed stage
+  constexpr int TILES = DT * DT;   // output tiles, spread over the 4 waves
+  constexpr int TPWV = (TILES + 3) / 4;
+  __shared__ __align__(16) __bf16 QT[D][TPAD];
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / H, h = bh % H;
   const int t0 = c * kMomentChunk, t1 = min(N, t0 + kMomentChunk);
-  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __bf16* __restrict__ src = q + b * sB + h * sH;
-  float acc[T][T];
+  f32x16 acc[TPWV];
 #pragma unroll
-  for (int i = 0; i < T; ++i)
+  for (int x = 0; x < TPWV; ++x)
 #pragma unroll
-    for (int j = 0; j < T; ++j) acc[i][j] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
   for (int base = t0; base < t1; base += TOK) {
     for (int e = threadIdx.x; e < TOK * D / 8; e += 256) {
       const int r = e / (D / 8), cc = e % (D / 8);
       const int tok = base + r;
-      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-      if (tok < t1) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (int64_t)tok * sN + cc * 8);
-        lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
-      }
-      *reinterpret_cast<f32x4*>(&xs[r][cc * 8]) = lo;
-      *reinterpret_cast<f32x4*>(&xs[r][cc * 8 + 4]) = hi;
+      bf16x8 v = {};
+      if (tok < t1) v = *reinterpret_cast<const bf16x8*>(src + (int64_t)tok * sN + cc * 8);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) QT[cc * 8 + x][r] = v[x];
     }
     __syncthreads();
-    for (int r = 0; r < TOK; ++r) {
-      float a[T], bb[T];
 #pragma unroll
-      for (int i = 0; i < T; i += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&xs[r][ti * T + i]);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(&xs[r][tj * T + i]);
+    for (int ks = 0; ks < TOK / 16; ++ks) {
+      bf16x8 f[DT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[i + e] = x[e], bb[i + e] = y[e];
+      for (int i = 0; i < DT; ++i)
+        f[i] = *reinterpret_cast<const bf16x8*>(&QT[32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int x = 0; x < TPWV; ++x) {
+        const int tile = w * TPWV + x;
+        if (tile < TILES) acc[x] = mfma32(f[tile / DT], f[tile % DT], acc[x]);
       }
-#pragma unroll
-      for (int i = 0; i < T; ++i)
-#pragma unroll
-        for (int j = 0; j < T; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
     }
     __syncthreads();
   }
   float* __restrict__ dst = part + ((int64_t)c * BH + bh) * D * D;
 #pragma unroll
-  for (int i = 0; i < T; ++i)
+  for (int x = 0; x < TPWV; ++x) {
+    const int tile = w * TPWV + x;
+    if (tile >= TILES) continue;
+    const int i = tile / DT, j = tile % DT;
 #pragma unroll
-    for (int j = 0; j < T; ++j) dst[(ti * T + i) * D + tj * T + j] = acc[i][j];
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      dst[row * D + 32 * j + (lane & 31)] = acc[x][r];
+    }
+  }
 }
 
-// Sum of the partials in chunk order, / N, ridge, Cholesky (right-looking,
-// column by column, in LDS).  A pivot that rounding drives below the ridge is
-// clamped to it.
+// Sum of the partials in chunk order, divided by N (one thread per entry).
+__global__ void moment_reduce_kernel(const float* __restrict__ part, int nc, int DD, int N, float* __restrict__ moment) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x, bh = blockIdx.y, BH = gridDim.y;
+  if (e >= DD) return;
+  float sum = 0.f;
+  for (int c = 0; c < nc; ++c) sum += part[((int64_t)c * BH + bh) * DD + e];
+  moment[(int64_t)bh * DD + e] = sum / (float)N;
+}
+
+// Ridge and Cholesky (right-looking, column by column, in LDS).  A pivot that
+// rounding drives below the ridge is clamped to it.
 template <int D>
-__global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __restrict__ part, int nc, int N,
-                                                             float ridge, float* __restrict__ moment,
+__global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __restrict__ moment, float ridge,
                                                              float* __restrict__ factor) {
   __shared__ float A[D][D + 1];
   __shared__ float lam_sh;
-  const int bh = blockIdx.x, BH = gridDim.x;
-  for (int e = threadIdx.x; e < D * D; e += 1024) {
-    float s = 0.f;
-    for (int c = 0; c < nc; ++c) s += part[((int64_t)c * BH + bh) * D * D + e];
-    s /= (float)N;
-    A[e / D][e % D] = s;
-    if (moment) moment[(int64_t)bh * D * D + e] = s;
-  }
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < D * D; e += 1024) A[e / D][e % D] = moment[(int64_t)bh * D * D + e];
   __syncthreads();
   if (threadIdx.x < 64) {
     float t = 0.f;
@@ -185,95 +195,113 @@ __global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __rest
 }
 
 // ---- key features: u = z / |z|, z_d = sum_e k_e L[e][d] ----------------------------
+// On the matrix cores: K is exact in bf16 and L is split into bf16 hi + lo
+// (two products; the dropped remainder is below 2^-17 of L), staged
+// transposed in LDS once per workgroup.  Wave w takes 4 tiles of 32 tokens;
+// a tile is D/32 products of 32 x 32 outputs per 16-channel step.  Stored in
+// fp16 (unit vectors: |u_d| <= 1), which is what every later decision reads;
+// `u32` (optional) receives the same values in fp32.
+constexpr int kFeatTiles = 4;  // 32-token tiles per wave
+
 template <int D>
 __global__ __launch_bounds__(256) void key_feature_kernel(const __bf16* __restrict__ k, int64_t sB, int64_t sN,
                                                           int64_t sH, int H, int N, const float* __restrict__ factor,
-                                                          float* __restrict__ u) {
-  constexpr int TOKS = 64;   // tokens per workgroup (4 threads each)
-  constexpr int QD = D / 4;  // channels per thread
-  __shared__ __align__(16) float Ls[D * D];
-  __shared__ __align__(16) float ks[TOKS][D + 4];
+                                                          _Float16* __restrict__ u, float* __restrict__ u32) {
+  constexpr int DT = D / 32, KS = D / 16, LP = D + 8;
+  __shared__ __align__(16) __bf16 LThi[D * LP];
+  __shared__ __align__(16) __bf16 LTlo[D * LP];
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int tok0 = blockIdx.x * TOKS;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* __restrict__ Lg = factor + (int64_t)bh * D * D;
-  for (int e = threadIdx.x; e < D * D / 4; e += 256)
-    *reinterpret_cast<f32x4*>(&Ls[4 * e]) = *reinterpret_cast<const f32x4*>(Lg + 4 * e);
-  const __bf16* __restrict__ src = k + b * sB + h * sH;
-  for (int e = threadIdx.x; e < TOKS * D / 8; e += 256) {
-    const int r = e / (D / 8), cc = e % (D / 8);
-    const int tok = tok0 + r;
-    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    if (tok < N) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (int64_t)tok * sN + cc * 8);
-      lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-      hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
-    }
-    *reinterpret_cast<f32x4*>(&ks[r][cc * 8]) = lo;
-    *reinterpret_cast<f32x4*>(&ks[r][cc * 8 + 4]) = hi;
+  for (int idx = threadIdx.x; idx < D * D; idx += 256) {
+    const int e = idx / D, d = idx % D;
+    const float x = Lg[idx];
+    const __bf16 hi = (__bf16)x;
+    LThi[d * LP + e] = hi;
+    LTlo[d * LP + e] = (__bf16)(x - (float)hi);
   }
   __syncthreads();
-  const int r = threadIdx.x / 4, qd = threadIdx.x % 4;
-  float z[QD];
+  const __bf16* __restrict__ src = k + b * sB + h * sH;
+  for (int tt = 0; tt < kFeatTiles; ++tt) {
+    const int t0 = ((blockIdx.x * 4 + w) * kFeatTiles + tt) * 32;
+    if (t0 >= N) break;  // whole wave
+    f32x16 acc[DT];
 #pragma unroll
-  for (int d = 0; d < QD; ++d) z[d] = 0.f;
-  for (int e = 0; e < D; ++e) {
-    const float ke = ks[r][e];
-    const float* Lrow = Ls + e * D + qd * QD;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int d = 0; d < QD; d += 4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lrow + d);
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    const __bf16* __restrict__ krow = src + (int64_t)min(t0 + (lane & 31), N - 1) * sN + 8 * (lane >> 5);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) z[d + x] = fmaf(ke, l4[x], z[d + x]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int off = (32 * dt + (lane & 31)) * LP + 16 * ks + 8 * (lane >> 5);
+        acc[dt] = mfma32(a, *reinterpret_cast<const bf16x8*>(&LThi[off]), acc[dt]);
+        acc[dt] = mfma32(a, *reinterpret_cast<const bf16x8*>(&LTlo[off]), acc[dt]);
+      }
     }
-  }
-  float ss = 0.f;
+    // token row of register r: 8*(r/4) + 4*(lane/32) + r%4; its D values sit in
+    // the 32 lanes of this half-wave across the DT tiles
+    float inv[16];
 #pragma unroll
-  for (int d = 0; d < QD; ++d) ss = fmaf(z[d], z[d], ss);
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
-  const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
-  const int tok = tok0 + r;
-  if (tok < N) {
-    float* __restrict__ dst = u + ((int64_t)bh * N + tok) * D + qd * QD;
+    for (int r = 0; r < 16; ++r) {
+      float sq = 0.f;
 #pragma unroll
-    for (int d = 0; d < QD; d += 4)
-      *reinterpret_cast<f32x4*>(dst + d) = f32x4{z[d] * inv, z[d + 1] * inv, z[d + 2] * inv, z[d + 3] * inv};
+      for (int dt = 0; dt < DT; ++dt) sq = fmaf(acc[dt][r], acc[dt][r], sq);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      inv[r] = (sq > 0.f) ? 1.f / sqrtf(sq) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = t0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (tok >= N) continue;
+      const int64_t row = ((int64_t)bh * N + tok) * D + (lane & 31);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const _Float16 hv = (_Float16)(acc[dt][r] * inv[r]);
+        u[row + 32 * dt] = hv;
+        if (u32) u32[row + 32 * dt] = (float)hv;
+      }
+    }
   }
 }
 
-// ---- one level: split directions --------------------------------------------------------
+// ---- split direction of one node (all 256 threads of the workgroup) -----------------------
 template <int D>
-__global__ __launch_bounds__(256) void reblock_direction_kernel(const float* __restrict__ u,
-                                                                const int32_t* __restrict__ order, int N, int M,
-                                                                int level, int max_slots, float* __restrict__ dirs) {
-  const int slot = blockIdx.x, bh = blockIdx.y;
-  int start, n, c;
-  slot_range(N, M, level, slot, &start, &n, &c);
-  if (c <= 1) return;  // whole workgroup
-  __shared__ float X[kLandmarks][D + 1];
-  __shared__ float G[kLandmarks][kLandmarks + 1];
-  __shared__ float a_sh[kLandmarks];
-  __shared__ float red_v[256];
-  __shared__ int red_i[256];
-  const int32_t* __restrict__ ord = order + (int64_t)bh * N + start;
+struct DirScratch {
+  float X[kLandmarks][D + 1];
+  float G[kLandmarks][kLandmarks + 1];
+  float a[kLandmarks];
+  float red_v[256];
+  int red_i[256];
+  float sgn;
+};
+
+// ord: the node's tokens in their current order (global or LDS); ub: the
+// head's features.  Leaves the unit direction in v (LDS, D floats).
+template <int D>
+__device__ void node_direction(const _Float16* __restrict__ ub, const int32_t* ord, int n, DirScratch<D>& sh,
+                               float* v) {
   for (int e = threadIdx.x; e < kLandmarks * D; e += 256) {
     const int s = e / D, d = e % D;
     const int tok = ord[(int)(((int64_t)(2 * s + 1) * n) / (2 * kLandmarks))];
-    X[s][d] = u[((int64_t)bh * N + tok) * D + d];
+    sh.X[s][d] = (float)ub[(int64_t)tok * D + d];
   }
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += 256) {
     float m = 0.f;
-    for (int s = 0; s < kLandmarks; ++s) m += X[s][d];
+    for (int s = 0; s < kLandmarks; ++s) m += sh.X[s][d];
     m /= (float)kLandmarks;
-    for (int s = 0; s < kLandmarks; ++s) X[s][d] -= m;
+    for (int s = 0; s < kLandmarks; ++s) sh.X[s][d] -= m;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < kLandmarks * kLandmarks; e += 256) {
     const int s = e / kLandmarks, t = e % kLandmarks;
     float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(X[s][d], X[t][d], acc);
-    G[s][t] = acc;
+    for (int d = 0; d < D; ++d) acc = fmaf(sh.X[s][d], sh.X[t][d], acc);
+    sh.G[s][t] = acc;
   }
   __syncthreads();
   if (threadIdx.x < 64) {  // power iteration, one wave, lane s < 32 holds a_s
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(256) void reblock_direction_kernel(const float* __r
       float w = 0.f;
       for (int t = 0; t < kLandmarks; ++t) {
         const float at = __shfl(a, t, 64);
-        if (lane < kLandmarks) w = fmaf(G[lane][t], at, w);
+        if (lane < kLandmarks) w = fmaf(sh.G[lane][t], at, w);
       }
       float n2 = w * w;
 #pragma unroll
@@ -295,50 +323,82 @@ __global__ __launch_bounds__(256) void reblock_direction_kernel(const float* __r
       }
       a = w / sqrtf(n2);
     }
-    if (lane < kLandmarks) a_sh[lane] = a;
+    if (lane < kLandmarks) sh.a[lane] = a;
   }
   __syncthreads();
   float vd = 0.f;
   const int d = threadIdx.x;
   if (d < D)
-    for (int s = 0; s < kLandmarks; ++s) vd = fmaf(X[s][d], a_sh[s], vd);
-  red_v[threadIdx.x] = vd * vd;
+    for (int s = 0; s < kLandmarks; ++s) vd = fmaf(sh.X[s][d], sh.a[s], vd);
+  sh.red_v[threadIdx.x] = vd * vd;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red_v[threadIdx.x] += red_v[threadIdx.x + o];
+    if (threadIdx.x < o) sh.red_v[threadIdx.x] += sh.red_v[threadIdx.x + o];
     __syncthreads();
   }
-  const float nrm = sqrtf(red_v[0]);
+  const float nrm = sqrtf(sh.red_v[0]);
   __syncthreads();
   // largest |v_d|, lowest d on ties
-  red_v[threadIdx.x] = (d < D) ? fabsf(vd) : -1.f;
-  red_i[threadIdx.x] = d;
+  sh.red_v[threadIdx.x] = (d < D) ? fabsf(vd) : -1.f;
+  sh.red_i[threadIdx.x] = d;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (threadIdx.x < o) {
-      const float x = red_v[threadIdx.x + o];
-      const int xi = red_i[threadIdx.x + o];
-      if (x > red_v[threadIdx.x] || (x == red_v[threadIdx.x] && xi < red_i[threadIdx.x]))
-        red_v[threadIdx.x] = x, red_i[threadIdx.x] = xi;
+      const float x = sh.red_v[threadIdx.x + o];
+      const int xi = sh.red_i[threadIdx.x + o];
+      if (x > sh.red_v[threadIdx.x] || (x == sh.red_v[threadIdx.x] && xi < sh.red_i[threadIdx.x]))
+        sh.red_v[threadIdx.x] = x, sh.red_i[threadIdx.x] = xi;
     }
     __syncthreads();
   }
-  __shared__ float sgn_sh;
-  if (threadIdx.x == red_i[0]) sgn_sh = (vd < 0.f) ? -1.f : 1.f;
+  if (threadIdx.x == sh.red_i[0]) sh.sgn = (vd < 0.f) ? -1.f : 1.f;
   __syncthreads();
-  if (d < D) {
-    const float scale = (nrm > 0.f) ? sgn_sh / nrm : sgn_sh;
-    dirs[((int64_t)bh * max_slots + slot) * D + d] = vd * scale;
-  }
+  if (d < D) v[d] = vd * ((nrm > 0.f) ? sh.sgn / nrm : sh.sgn);
+  __syncthreads();
 }
 
-// ---- one level: projection keys (16 lanes per position) ------------------------------------
+// Projection u . v of one member, 16 lanes (8 fp16 channels each for D = 128,
+// 4 for D = 64); every lane of the 16 ends with the sum.
 template <int D>
-__global__ __launch_bounds__(256) void reblock_key_kernel(const float* __restrict__ u, const int32_t* __restrict__ order,
+__device__ __forceinline__ float project16(const _Float16* __restrict__ ur, const float* v, int l16) {
+  constexpr int PER = D / 16;
+  float acc = 0.f;
+  if constexpr (PER == 8) {
+    const half8 h = *reinterpret_cast<const half8*>(ur + l16 * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[l16 * 8 + e], acc);
+  } else {
+    const half4 h = *reinterpret_cast<const half4*>(ur + l16 * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf((float)h[e], v[l16 * 4 + e], acc);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
+  return acc;
+}
+
+// ---- one level, large nodes: split directions ----------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void reblock_direction_kernel(const _Float16* __restrict__ u,
+                                                                const int32_t* __restrict__ order, int N, int M,
+                                                                int level, int max_slots, float* __restrict__ dirs) {
+  const int slot = blockIdx.x, bh = blockIdx.y;
+  int start, n, c;
+  slot_range(N, M, level, slot, &start, &n, &c);
+  if (c <= 1) return;  // whole workgroup
+  __shared__ DirScratch<D> sh;
+  __shared__ float v[D];
+  node_direction<D>(u + (int64_t)bh * N * D, order + (int64_t)bh * N + start, n, sh, v);
+  for (int d = threadIdx.x; d < D; d += 256) dirs[((int64_t)bh * max_slots + slot) * D + d] = v[d];
+}
+
+// ---- one level, large nodes: projection keys (16 lanes per position) ------------------------
+template <int D>
+__global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __restrict__ u,
+                                                          const int32_t* __restrict__ order,
                                                           const float* __restrict__ dirs, int N, int M, int level,
                                                           int max_slots, int64_t total, uint64_t* __restrict__ keys,
                                                           int32_t* __restrict__ vals) {
-  constexpr int PER = D / 16;  // channels per lane
   const int64_t g = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
   const int l16 = threadIdx.x % 16;
   if (g >= total) return;  // the 16 lanes of a position leave together
@@ -347,25 +407,64 @@ __global__ __launch_bounds__(256) void reblock_key_kernel(const float* __restric
   const int slot = slot_of(N, M, level, pos, &c);
   const int tok = order[g];
   uint32_t fk = 0u;
-  if (c > 1) {
-    const float* __restrict__ ur = u + ((int64_t)bh * N + tok) * D + l16 * PER;
-    const float* __restrict__ vr = dirs + ((int64_t)bh * max_slots + slot) * D + l16 * PER;
-    float acc = 0.f;
-#pragma unroll
-    for (int x = 0; x < PER; x += 4) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ur + x);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(vr + x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = fmaf(a[e], b[e], acc);
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
-    fk = float_key(acc);
-  }
+  if (c > 1)
+    fk = float_key(project16<D>(u + ((int64_t)bh * N + tok) * D, dirs + ((int64_t)bh * max_slots + slot) * D, l16));
   if (l16 == 0) {
     keys[g] = ((uint64_t)bh << 48) | ((uint64_t)slot << 32) | fk;
     vals[g] = tok;
   }
+}
+
+// ---- one level, nodes of at most kLocalCap tokens: direction, projections and a
+// stable bitonic sort of (projection key, position) in LDS, one workgroup per node.
+constexpr int kLocalCap = 4096;
+
+template <int D, int CAP>
+__global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16* __restrict__ u,
+                                                                  const int32_t* __restrict__ cur,
+                                                                  int32_t* __restrict__ nxt, int N, int M, int level,
+                                                                  int max_slots, float* __restrict__ dirs_out) {
+  const int slot = blockIdx.x, bh = blockIdx.y;
+  int start, n, c;
+  slot_range(N, M, level, slot, &start, &n, &c);
+  if (n == 0) return;  // empty slot (whole workgroup)
+  const int32_t* __restrict__ src = cur + (int64_t)bh * N + start;
+  int32_t* __restrict__ dst = nxt + (int64_t)bh * N + start;
+  if (c <= 1) {  // a leaf keeps its order
+    for (int i = threadIdx.x; i < n; i += 256) dst[i] = src[i];
+    return;
+  }
+  __shared__ int32_t ord[CAP];
+  __shared__ uint64_t keys[CAP];
+  __shared__ DirScratch<D> sh;
+  __shared__ float v[D];
+  for (int i = threadIdx.x; i < n; i += 256) ord[i] = src[i];
+  __syncthreads();
+  const _Float16* __restrict__ ub = u + (int64_t)bh * N * D;
+  node_direction<D>(ub, ord, n, sh, v);
+  if (dirs_out)
+    for (int d = threadIdx.x; d < D; d += 256) dirs_out[((int64_t)bh * max_slots + slot) * D + d] = v[d];
+  int P = 1;
+  while (P < n) P <<= 1;
+  const int l16 = threadIdx.x % 16;
+  for (int i = threadIdx.x / 16; i < P; i += 16) {  // 16 members per pass, 16 lanes each
+    uint64_t key = ~0ull;
+    if (i < n) key = ((uint64_t)float_key(project16<D>(ub + (int64_t)ord[i] * D, v, l16)) << 32) | (uint32_t)i;
+    if (l16 == 0) keys[i] = key;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1)
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += 256) {
+        const int ij = i ^ j;
+        if (ij > i) {
+          const uint64_t a = keys[i], b = keys[ij];
+          if ((a > b) == ((i & kk) == 0)) keys[i] = b, keys[ij] = a;
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = ord[(int)(keys[i] & 0xffffffffu)];
 }
 
 __global__ void iota_kernel(int32_t* __restrict__ order, int N, int64_t total) {
@@ -404,9 +503,12 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
   const int nc = (N + kMomentChunk - 1) / kMomentChunk;
   moment_partial_kernel<D><<<dim3((unsigned)nc, (unsigned)BH), 256, 0, s>>>(
       reinterpret_cast<const __bf16*>(p.q), p.sB, p.sN, p.sH, p.H, N, p.part);
-  moment_factor_kernel<D><<<dim3((unsigned)BH), 1024, 0, s>>>(p.part, nc, N, p.ridge, p.moment, p.factor);
-  key_feature_kernel<D><<<dim3((unsigned)((N + 63) / 64), (unsigned)BH), 256, 0, s>>>(
-      reinterpret_cast<const __bf16*>(p.k), p.sB, p.sN, p.sH, p.H, N, p.factor, p.features);
+  moment_reduce_kernel<<<dim3((unsigned)((D * D + 255) / 256), (unsigned)BH), 256, 0, s>>>(p.part, nc, D * D, N,
+                                                                                         p.moment);
+  moment_factor_kernel<D><<<dim3((unsigned)BH), 1024, 0, s>>>(p.moment, p.ridge, p.factor);
+  const int ftok = 4 * kFeatTiles * 32;  // tokens per feature workgroup
+  key_feature_kernel<D><<<dim3((unsigned)((N + ftok - 1) / ftok), (unsigned)BH), 256, 0, s>>>(
+      reinterpret_cast<const __bf16*>(p.k), p.sB, p.sN, p.sH, p.H, N, p.factor, p.features, p.features32);
   iota_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(p.order0, N, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -419,19 +521,34 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
   const int end_bit = sort_end_bit(BH);
   const int nlev = reblock_levels(N, M);
   const int max_slots = 1 << (nlev > 1 ? nlev - 2 : 0);
-  for (int lev = 0; lev + 1 < nlev; ++lev) {
+  int cmax = (N + M - 1) / M;  // most leaves of a node at the current level
+  for (int lev = 0; lev + 1 < nlev; ++lev, cmax = (cmax + 1) / 2) {
     const int nslots = 1 << lev;
-    // directions of this level: the caller's per-level copy, else the workspace
-    float* dirs = p.dirs_out ? p.dirs_out + (int64_t)lev * BH * max_slots * D : p.dirs;
-    reblock_direction_kernel<D><<<dim3((unsigned)nslots, (unsigned)BH), 256, 0, s>>>(p.features, cur, N, M, lev,
-                                                                                      max_slots, dirs);
-    reblock_key_kernel<D><<<dim3((unsigned)((total + 15) / 16)), 256, 0, s>>>(p.features, cur, dirs, N, M, lev,
-                                                                             max_slots, total, p.keys0, p.vals0);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    size_t bytes = p.sort_bytes;
-    e = hipcub::DeviceRadixSort::SortPairs(p.sort_tmp, bytes, p.keys0, p.keys1, p.vals0, nxt, (int)total, 0,
-                                           end_bit, s);
+    float* dirs_dbg = p.dirs_out ? p.dirs_out + (int64_t)lev * BH * max_slots * D : nullptr;
+    const int64_t nmax = (int64_t)cmax * M;
+    if (nmax <= kLocalCap) {
+      const dim3 grid((unsigned)nslots, (unsigned)BH);
+      if (nmax <= 256)
+        reblock_local_level_kernel<D, 256><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
+      else if (nmax <= 1024)
+        reblock_local_level_kernel<D, 1024><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
+      else
+        reblock_local_level_kernel<D, kLocalCap><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots,
+                                                                      dirs_dbg);
+      e = hipGetLastError();
+    } else {
+      // directions of this level: the caller's per-level copy, else the workspace
+      float* dirs = dirs_dbg ? dirs_dbg : p.dirs;
+      reblock_direction_kernel<D><<<dim3((unsigned)nslots, (unsigned)BH), 256, 0, s>>>(p.features, cur, N, M, lev,
+                                                                                        max_slots, dirs);
+      reblock_key_kernel<D><<<dim3((unsigned)((total + 15) / 16)), 256, 0, s>>>(p.features, cur, dirs, N, M, lev,
+                                                                               max_slots, total, p.keys0, p.vals0);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      size_t bytes = p.sort_bytes;
+      e = hipcub::DeviceRadixSort::SortPairs(p.sort_tmp, bytes, p.keys0, p.keys1, p.vals0, nxt, (int)total, 0,
+                                             end_bit, s);
+    }
     if (e != hipSuccess) return e;
     if (p.levels) {
       e = hipMemcpyAsync(p.levels + (int64_t)(lev + 1) * total, nxt, total * 4, hipMemcpyDeviceToDevice, s);

@@ -388,8 +388,9 @@ bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_byte
  *   M_Q = Q^T Q / N (uncentred, fp32), L = chol(M_Q + lam I) with
  *   lam = ridge * tr(M_Q) / D (ridge when the trace is 0; a pivot that fp32
  *   rounding pushes below lam is clamped to lam);
- *   u_j = z_j / |z_j|, z_j = k_j^T L (0 for a zero key): cos(u_i, u_j) is the
- *   cosine of keys i and j's score profiles over all queries;
+ *   u_j = z_j / |z_j|, z_j = k_j^T L (0 for a zero key), rounded to fp16:
+ *   cos(u_i, u_j) is the cosine of keys i and j's score profiles over all
+ *   queries;
  *   an equal-capacity binary tree of leaves of M tokens: a node of n tokens
  *   spans c = ceil(n/M) leaves, its first child takes floor(c/2)*M of them;
  *   at each split the node's tokens (in their current order, the root in
@@ -405,7 +406,8 @@ bsa_status spark_summaries(const spark_summary_args* a, void* ws, size_t ws_byte
  *   M          16, 32 or 64; J = ceil(N / M) <= 65536; B*H <= 65535
  *   ridge      > 0 (1e-4 is the documented default)
  *   moment, factor  optional fp32 [B*H, D, D] outputs (factor lower-triangular)
- *   features        optional fp32 [B*H, N, D] output (else in the workspace)
+ *   features        optional fp32 [B*H, N, D] output: the unit features as
+ *                   the splits use them (stored in fp16 in the workspace)
  *   levels          optional int32 [nlevels, B*H, N]: the token order after
  *                   every level (level 0 = token order), for checking
  *   dirs            optional fp32 [nlevels - 1, B*H, S, D], S = 2^(nlevels-2):

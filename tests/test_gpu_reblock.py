@@ -19,17 +19,18 @@ pytestmark = pytest.mark.gpu
 bsa = pytest.importorskip("block_sparse_attention_02_amd")
 DEV = torch.device("cuda:0")
 
-# The device's split directions are checked for validity rather than equality:
-# 32 nearly isotropic landmarks have close leading eigenvalues, so fp32 and
-# float64 power iterations may end on different, equally principal axes (the
-# oracle's check_splits).  SPLIT_EPS: tolerated inversion of two consecutive
-# tokens along the device's own direction with the oracle's features (unit
-# vectors within FEATURE_TOL of the device's, plus fp32 dot-product rounding);
-# SPLIT_TAU: tolerated relative shortfall of the direction's Rayleigh quotient
-# against the oracle's direction on the same landmarks.
-SPLIT_EPS = 1e-5
+# Both sides store the unit features in fp16 and split on the stored values;
+# the device's fp32 and the oracle's float64 features can still round to
+# neighbouring fp16 values (a component moves by at most 2^-11 of a unit
+# vector: FEATURE_TOL), so a projection onto a unit direction may differ by up
+# to 4.9e-4 and two consecutive tokens may appear inverted by up to SPLIT_EPS.  The device's split directions are checked for validity rather than
+# equality: 32 nearly isotropic landmarks have close leading eigenvalues, so
+# two runs may end on different, equally principal axes (the oracle's
+# check_splits); SPLIT_TAU is the tolerated relative shortfall of the
+# direction's Rayleigh quotient against the oracle's on the same landmarks.
+SPLIT_EPS = 1e-3
 SPLIT_TAU = 1e-3
-FEATURE_TOL = 2e-5
+FEATURE_TOL = 5e-4
 
 CFGS = {
     "video_2k_d128": (scaled("video", grid=(8, 16, 16), h=2), 64),

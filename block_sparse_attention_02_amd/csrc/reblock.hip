@@ -108,8 +108,10 @@ __global__ __launch_bounds__(256) void moment_partial_kernel(const __bf16* __res
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
   for (int base = t0; base < t1; base += TOK) {
+    // consecutive lanes take consecutive tokens of one 8-channel chunk, so the
+    // 2-byte transposed writes of a wave land on consecutive addresses
     for (int e = threadIdx.x; e < TOK * D / 8; e += 256) {
-      const int r = e / (D / 8), cc = e % (D / 8);
+      const int r = e % TOK, cc = e / TOK;
       const int tok = base + r;
       bf16x8 v = {};
       if (tok < t1) v = *reinterpret_cast<const bf16x8*>(src + (int64_t)tok * sN + cc * 8);
@@ -197,11 +199,11 @@ __global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __rest
 // ---- key features: u = z / |z|, z_d = sum_e k_e L[e][d] ----------------------------
 // On the matrix cores: K is exact in bf16 and L is split into bf16 hi + lo
 // (two products; the dropped remainder is below 2^-17 of L), staged
-// transposed in LDS once per workgroup.  Wave w takes 4 tiles of 32 tokens;
+// transposed in LDS once per workgroup.  Wave w takes 16 tiles of 32 tokens;
 // a tile is D/32 products of 32 x 32 outputs per 16-channel step.  Stored in
 // fp16 (unit vectors: |u_d| <= 1), which is what every later decision reads;
 // `u32` (optional) receives the same values in fp32.
-constexpr int kFeatTiles = 4;  // 32-token tiles per wave
+constexpr int kFeatTiles = 16;  // 32-token tiles per wave
 
 template <int D>
 __global__ __launch_bounds__(256) void key_feature_kernel(const __bf16* __restrict__ k, int64_t sB, int64_t sN,
@@ -377,6 +379,19 @@ __device__ __forceinline__ float project16(const _Float16* __restrict__ ur, cons
   return acc;
 }
 
+// Projection u . v of one member by one thread (the whole fp16 row; v in LDS).
+template <int D>
+__device__ __forceinline__ float project_row(const _Float16* __restrict__ ur, const float* v) {
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const half8 h = *reinterpret_cast<const half8*>(ur + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[8 * c + e], acc);
+  }
+  return acc;
+}
+
 // ---- one level, large nodes: split directions ----------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void reblock_direction_kernel(const _Float16* __restrict__ u,
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __rest
   if (c > 1)
     fk = float_key(project16<D>(u + ((int64_t)bh * N + tok) * D, dirs + ((int64_t)bh * max_slots + slot) * D, l16));
   if (l16 == 0) {
-    keys[g] = ((uint64_t)bh << 48) | ((uint64_t)slot << 32) | fk;
+    keys[g] = ((uint64_t)bh << (32 + level)) | ((uint64_t)slot << 32) | fk;
     vals[g] = tok;
   }
 }
@@ -446,11 +461,10 @@ __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16
     for (int d = threadIdx.x; d < D; d += 256) dirs_out[((int64_t)bh * max_slots + slot) * D + d] = v[d];
   int P = 1;
   while (P < n) P <<= 1;
-  const int l16 = threadIdx.x % 16;
-  for (int i = threadIdx.x / 16; i < P; i += 16) {  // 16 members per pass, 16 lanes each
+  for (int i = threadIdx.x; i < P; i += 256) {  // one member per thread
     uint64_t key = ~0ull;
-    if (i < n) key = ((uint64_t)float_key(project16<D>(ub + (int64_t)ord[i] * D, v, l16)) << 32) | (uint32_t)i;
-    if (l16 == 0) keys[i] = key;
+    if (i < n) key = ((uint64_t)float_key(project_row<D>(ub + (int64_t)ord[i] * D, v)) << 32) | (uint32_t)i;
+    keys[i] = key;
   }
   __syncthreads();
   for (int kk = 2; kk <= P; kk <<= 1)
@@ -482,17 +496,178 @@ __global__ void reblock_tables_kernel(const int32_t* __restrict__ order, int N, 
   if (bh == 0 && p % M == 0) block_len[p / M] = min(M, N - p);
 }
 
+// ---- one level, nodes of at most 256 tokens: one wave per node, 4 nodes per workgroup --------
+// The same steps as the block-level kernel with wave-level synchronisation; the
+// landmark Gram matrix runs on the matrix cores (centred landmarks split into
+// bf16 hi + lo, three products, fp32-accurate).
+constexpr int kWaveCap = 256;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D>
+struct WaveNode {
+  float X[kLandmarks][D + 4];
+  float G[kLandmarks][kLandmarks + 1];
+  float v[D];
+  float a[kLandmarks];
+  int32_t ord[kWaveCap];
+  uint64_t keys[kWaveCap];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void reblock_wave_level_kernel(const _Float16* __restrict__ u,
+                                                                 const int32_t* __restrict__ cur,
+                                                                 int32_t* __restrict__ nxt, int N, int M, int level,
+                                                                 int nslots, int max_slots, float* __restrict__ dirs_out) {
+  __shared__ WaveNode<D> wn[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int slot = blockIdx.x * 4 + w, bh = blockIdx.y;
+  if (slot >= nslots) return;  // whole wave
+  int start, n, c;
+  slot_range(N, M, level, slot, &start, &n, &c);
+  if (n == 0) return;
+  const int32_t* __restrict__ src = cur + (int64_t)bh * N + start;
+  int32_t* __restrict__ dst = nxt + (int64_t)bh * N + start;
+  if (c <= 1) {
+    for (int i = lane; i < n; i += 64) dst[i] = src[i];
+    return;
+  }
+  WaveNode<D>& sh = wn[w];
+  const _Float16* __restrict__ ub = u + (int64_t)bh * N * D;
+  for (int i = lane; i < n; i += 64) sh.ord[i] = src[i];
+  wave_sync();
+  // landmarks, centred
+  for (int e = lane; e < kLandmarks * (D / 8); e += 64) {
+    const int s = e / (D / 8), cc = e % (D / 8);
+    const int tok = sh.ord[(int)(((int64_t)(2 * s + 1) * n) / (2 * kLandmarks))];
+    const half8 h = *reinterpret_cast<const half8*>(ub + (int64_t)tok * D + 8 * cc);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) sh.X[s][8 * cc + x] = (float)h[x];
+  }
+  wave_sync();
+  for (int d = lane; d < D; d += 64) {
+    float m = 0.f;
+    for (int s = 0; s < kLandmarks; ++s) m += sh.X[s][d];
+    m /= (float)kLandmarks;
+    for (int s = 0; s < kLandmarks; ++s) sh.X[s][d] -= m;
+  }
+  wave_sync();
+  // G = X X^T on the matrix cores: lane l holds row l%32, channels 16 ks + 8 (l/32) + 0..7,
+  // which is the A fragment of rows and the B fragment of columns alike
+  f32x16 g;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) g[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const float xv = sh.X[lane & 31][16 * ks + 8 * (lane >> 5) + x];
+      hi[x] = (__bf16)xv;
+      lo[x] = (__bf16)(xv - (float)hi[x]);
+    }
+    g = mfma32(lo, hi, g);
+    g = mfma32(hi, lo, g);
+    g = mfma32(hi, hi, g);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sh.G[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = g[r];
+  wave_sync();
+  // power iteration from the ramp (lane s < 32 holds a_s)
+  float a = (lane < kLandmarks) ? ((float)lane - 0.5f * (kLandmarks - 1)) * rsqrtf(2728.f) : 0.f;
+  for (int it = 0; it < kPowerIters; ++it) {
+    float wv = 0.f;
+    for (int t = 0; t < kLandmarks; ++t) {
+      const float at = __shfl(a, t, 64);
+      if (lane < kLandmarks) wv = fmaf(sh.G[lane][t], at, wv);
+    }
+    float n2 = wv * wv;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
+    if (n2 == 0.f) {
+      a = wv;
+      break;
+    }
+    a = wv / sqrtf(n2);
+  }
+  if (lane < kLandmarks) sh.a[lane] = a;
+  wave_sync();
+  // v = X^T a; norm and the sign of the largest entry (lowest index on ties)
+  constexpr int PL = D / 64;  // channels per lane
+  float vd[PL];
+  float n2 = 0.f, best = -1.f;
+  int bi = 0;
+#pragma unroll
+  for (int x = 0; x < PL; ++x) {
+    const int d = lane + 64 * x;
+    float acc = 0.f;
+    for (int s = 0; s < kLandmarks; ++s) acc = fmaf(sh.X[s][d], sh.a[s], acc);
+    vd[x] = acc;
+    n2 = fmaf(acc, acc, n2);
+    if (fabsf(acc) > best) best = fabsf(acc), bi = d;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n2 += __shfl_xor(n2, o, 64);
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ob > best || (ob == best && oi < bi)) best = ob, bi = oi;
+  }
+  float sgn = 1.f;
+#pragma unroll
+  for (int x = 0; x < PL; ++x)
+    if (lane + 64 * x == bi) sgn = (vd[x] < 0.f) ? -1.f : 1.f;
+  sgn = __shfl(sgn, bi % 64, 64);
+  const float scale = (n2 > 0.f) ? sgn / sqrtf(n2) : sgn;
+#pragma unroll
+  for (int x = 0; x < PL; ++x) {
+    sh.v[lane + 64 * x] = vd[x] * scale;
+    if (dirs_out) dirs_out[((int64_t)bh * max_slots + slot) * D + lane + 64 * x] = vd[x] * scale;
+  }
+  wave_sync();
+  // projections (one member per lane), then a stable bitonic sort of (key, position)
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = lane; i < P; i += 64) {
+    uint64_t key = ~0ull;
+    if (i < n) key = ((uint64_t)float_key(project_row<D>(ub + (int64_t)sh.ord[i] * D, sh.v)) << 32) | (uint32_t)i;
+    sh.keys[i] = key;
+  }
+  wave_sync();
+  for (int kk = 2; kk <= P; kk <<= 1)
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = lane; i < P; i += 64) {
+        const int ij = i ^ j;
+        if (ij > i) {
+          const uint64_t x = sh.keys[i], y = sh.keys[ij];
+          if ((x > y) == ((i & kk) == 0)) sh.keys[i] = y, sh.keys[ij] = x;
+        }
+      }
+      wave_sync();
+    }
+  for (int i = lane; i < n; i += 64) dst[i] = sh.ord[(int)(sh.keys[i] & 0xffffffffu)];
+}
+
 // ---- host orchestration --------------------------------------------------------------------
-static int sort_end_bit(int BH) {
+// Sort keys: head | slot (level bits) | projection key (32 bits).
+static int sort_end_bit(int BH, int level) {
   int bh_bits = 0;
   while ((1 << bh_bits) < BH) ++bh_bits;
-  return 48 + bh_bits;
+  return 32 + level + bh_bits;
 }
 
 size_t reblock_sort_bytes(int64_t total, int BH) {
-  size_t bytes = 0;
-  hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, (const uint64_t*)nullptr, (uint64_t*)nullptr,
-                                     (const int32_t*)nullptr, (int32_t*)nullptr, (int)total, 0, sort_end_bit(BH));
+  size_t bytes = 0, b;
+  for (int level = 0; level <= 16; ++level) {  // the largest over the levels a sort may run at
+    b = 0;
+    hipcub::DeviceRadixSort::SortPairs(nullptr, b, (const uint64_t*)nullptr, (uint64_t*)nullptr,
+                                       (const int32_t*)nullptr, (int32_t*)nullptr, (int)total, 0,
+                                       sort_end_bit(BH, level));
+    bytes = b > bytes ? b : bytes;
+  }
   return bytes;
 }
 
@@ -518,7 +693,6 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
   }
   int32_t* cur = p.order0;
   int32_t* nxt = p.order1;
-  const int end_bit = sort_end_bit(BH);
   const int nlev = reblock_levels(N, M);
   const int max_slots = 1 << (nlev > 1 ? nlev - 2 : 0);
   int cmax = (N + M - 1) / M;  // most leaves of a node at the current level
@@ -528,8 +702,9 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
     const int64_t nmax = (int64_t)cmax * M;
     if (nmax <= kLocalCap) {
       const dim3 grid((unsigned)nslots, (unsigned)BH);
-      if (nmax <= 256)
-        reblock_local_level_kernel<D, 256><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
+      if (nmax <= kWaveCap)
+        reblock_wave_level_kernel<D><<<dim3((unsigned)((nslots + 3) / 4), (unsigned)BH), 256, 0, s>>>(
+            p.features, cur, nxt, N, M, lev, nslots, max_slots, dirs_dbg);
       else if (nmax <= 1024)
         reblock_local_level_kernel<D, 1024><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
       else
@@ -547,7 +722,7 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
       if (e != hipSuccess) return e;
       size_t bytes = p.sort_bytes;
       e = hipcub::DeviceRadixSort::SortPairs(p.sort_tmp, bytes, p.keys0, p.keys1, p.vals0, nxt, (int)total, 0,
-                                             end_bit, s);
+                                             sort_end_bit(BH, lev), s);
     }
     if (e != hipSuccess) return e;
     if (p.levels) {

@@ -381,9 +381,12 @@ def bench_coarse(args):
 
     ca = L.CoarseArgs(v=P(v), d=bsa.api._desc(v), dt=L.BSA_BF16, perm=P(perm), block_len=P(block_len), J=J, M=M,
                       E=P(E), vbar=P(vbar), C=P(C))
+    n_cws = ctypes.c_size_t()
+    L.check(lib.vsa_coarse_ws(ctypes.byref(ca), ctypes.byref(n_cws)))
+    cws = torch.empty(n_cws.value, dtype=torch.uint8, device=dev)
 
     def coarse():
-        L.check(lib.vsa_coarse(ctypes.byref(ca), None, 0, s_ptr))
+        L.check(lib.vsa_coarse(ctypes.byref(ca), P(cws), cws.numel(), s_ptr))
 
     qa = bsa.api._qouter_args(q, k, v, out, 1.0 / D ** 0.5, L.BSA_SEL_BLOCK, None)
     qa.perm, qa.block_len, qa.J, qa.M = P(perm), P(block_len), J, M

@@ -436,7 +436,9 @@ bsa_status vsa_coarse_ws(const vsa_coarse_args* a, size_t* bytes) {
   if (!bytes) return fail(BSA_ERR_ARG, "vsa_coarse_ws: null output");
   bsa_status st = check_coarse(a);
   if (st != BSA_OK) return st;
-  *bytes = a->vbar ? 0 : round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  const size_t BH = (size_t)a->d.B * a->d.H;
+  *bytes = (a->vbar ? 0 : round_up(BH * a->J * a->d.D * sizeof(float))) +
+           round_up(2 * BH * a->d.D * bsa::coarse_jpad(a->J) * sizeof(__bf16));
   return ok();
 }
 
@@ -446,8 +448,11 @@ bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void*
   if (st != BSA_OK) return st;
   if (need && (!ws || ws_bytes < need))
     return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace of %zu bytes required", need);
-  if (need && !aligned16(ws)) return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace must be 16-byte aligned");
+  if (!aligned16(ws)) return fail(BSA_ERR_WORKSPACE, "vsa_coarse: workspace must be 16-byte aligned");
+  const size_t BH = (size_t)a->d.B * a->d.H;
+  const size_t vbar_ws = a->vbar ? 0 : round_up(BH * a->J * a->d.D * sizeof(float));
   float* vbar = a->vbar ? a->vbar : static_cast<float*>(ws);
+  __bf16* vt = reinterpret_cast<__bf16*>(static_cast<char*>(ws) + vbar_ws);
   const int vec = 16 / elem_bytes(a->dt);
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
                       aligned16(a->v);
@@ -457,7 +462,7 @@ bsa_status vsa_coarse(const vsa_coarse_args* a, void* ws, size_t ws_bytes, void*
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s, 1);
   if (e != hipSuccess) return hip_status(e, "pool launch");
-  bsa::CoarseParams cp{a->E, vbar, a->C, (int)(a->d.B * a->d.H), a->J, (int)a->d.D};
+  bsa::CoarseParams cp{a->E, vbar, a->C, (int)(a->d.B * a->d.H), a->J, (int)a->d.D, vt};
   return hip_status(bsa::launch_coarse(cp, s), "coarse launch");
 }
 

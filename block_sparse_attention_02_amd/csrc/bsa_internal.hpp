@@ -34,7 +34,9 @@ struct CoarseParams {
   const float* vbar;  // [BH, J, D]
   float* C;           // [BH, J, D]
   int BH, J, D;
+  __bf16* vt;         // [2, BH, D, coarse_jpad(J)]: V_bar transposed, bf16 hi then lo parts, zero padded
 };
+__host__ __device__ inline int coarse_jpad(int J) { return (J + 63) / 64 * 64; }
 hipError_t launch_coarse(const CoarseParams& p, hipStream_t s);
 
 struct RouteParams {

@@ -321,8 +321,11 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
  *   vbar     optional fp32 [B, H, J, D] contiguous output (NULL: workspace)
  *   C        fp32 [B, H, J, D] contiguous output
  * Supported: D in {64, 128}, B*H <= 65535; C, vbar and the workspace 16-byte
- * aligned.  The softmax weights and the sums are fp32.  The workspace holds
- * vbar when it is not an output: vsa_coarse_ws() bytes.
+ * aligned.  The softmax weights and the sums are fp32; the products weight x
+ * vbar take both factors as a bf16 pair hi + lo (hi*hi + hi*lo + lo*hi, within
+ * 3 * 2^-18 of each product).  The workspace (always needed: vsa_coarse_ws()
+ * bytes, caller-owned, contents undefined after the call) holds vbar when it
+ * is not an output and the transposed bf16 hi/lo copy of vbar.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* v;

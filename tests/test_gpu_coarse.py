@@ -36,13 +36,16 @@ def _oracle_scores(Q, K, tab):
 
 
 def _c_bound(E, vbar, V, J):
-    """fp32 error bound of C: the block means (<= 64 rounded adds of values
+    """Error bound of C: the block means (<= 64 rounded fp32 adds of values
     below max|V|), the weights (argument E - m and exp2 rounding, about
-    2|E - m| + 2 ulp relative) and the J-term weighted sum, with a factor 4
-    of margin."""
+    2|E - m| + 2 ulp relative), the J-term fp32 weighted sum, and the products:
+    weights and block means each split into bf16 hi + lo and multiplied as
+    hi*hi + hi*lo + lo*hi, which drops lo*lo and the two lo roundings (each at
+    most 2^-18 of the product, so 3 * 2^-18 relative); a factor 4 of margin."""
     spread = float((E.max(axis=-1) - E.min(axis=-1)).max())
     vmax = float(np.abs(vbar).max())
-    return 4 * EPS32 * ((J + 2 * spread + 4) * vmax + 64 * float(np.abs(V).max())) + 1e-7
+    fp32 = EPS32 * ((J + 2 * spread + 4) * vmax + 64 * float(np.abs(V).max()))
+    return 4 * (fp32 + 3 * 2.0 ** -18 * vmax) + 1e-7
 
 
 COARSE_CFGS = {

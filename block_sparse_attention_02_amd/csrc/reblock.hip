@@ -84,54 +84,87 @@ int reblock_levels(int N, int M) {
 
 // ---- second moment ---------------------------------------------------------------------
 // Partial Q^T Q over a 2048-token chunk on the matrix cores: bf16 products are
-// exact in fp32, accumulation in fp32.  The chunk is staged transposed
-// (QT[d][t]) so that one 16-byte read gives a lane its 8 consecutive tokens of
-// one channel, which is both the A fragment (rows d1) and, for C = Q^T Q, the
-// B fragment (columns d2) of a 32 x 32 x 16 product.
+// exact in fp32, accumulation in fp32.  Tokens are staged row-major (coalesced
+// 16-byte loads, 16-byte chunks XOR-swizzled per row, two buffers) and read
+// with the transposing LDS read, which gives a lane 8 consecutive tokens of one
+// channel: both the A fragment (rows d1) and, for C = Q^T Q, the B fragment
+// (columns d2) of a 32 x 32 x 16 product.  The next step's loads are in flight
+// during the products.
+
+// Physical 16-byte chunk of logical chunk c in staged row r: the transposing
+// read takes 4 consecutive rows x 32 bytes per 16-lane group, so rows r % 4 get
+// disjoint chunk sets.
+template <int CPR>
+__device__ __forceinline__ int tr_swz(int r, int c) {
+  if constexpr (CPR >= 16)
+    return c ^ ((0xCA60 >> (4 * (r & 3))) & 15);  // XOR 0, 6, 10, 12 for r % 4 = 0..3
+  else
+    return c ^ (2 * (r & 3));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void moment_partial_kernel(const __bf16* __restrict__ q, int64_t sB, int64_t sN,
                                                              int64_t sH, int H, int N, float* __restrict__ part) {
   constexpr int DT = D / 32;       // 32-channel tiles
+  constexpr int CPR = D / 8;       // 16-byte chunks per token row
   constexpr int TOK = 64;          // tokens staged per step
-  constexpr int TPAD = TOK + 8;    // padded row of the transposed stage
+  constexpr int LD = TOK * CPR / 256;  // 16-byte loads per thread per step
   constexpr int TILES = DT * DT;   // output tiles, spread over the 4 waves
   constexpr int TPWV = (TILES + 3) / 4;
-  __shared__ __align__(16) __bf16 QT[D][TPAD];
+  __shared__ __align__(16) __bf16 Qs[2][TOK * D];
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / H, h = bh % H;
   const int t0 = c * kMomentChunk, t1 = min(N, t0 + kMomentChunk);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __bf16* __restrict__ src = q + b * sB + h * sH;
   f32x16 acc[TPWV];
 #pragma unroll
   for (int x = 0; x < TPWV; ++x)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
-  for (int base = t0; base < t1; base += TOK) {
-    // consecutive lanes take consecutive tokens of one 8-channel chunk, so the
-    // 2-byte transposed writes of a wave land on consecutive addresses
-    for (int e = threadIdx.x; e < TOK * D / 8; e += 256) {
-      const int r = e % TOK, cc = e / TOK;
-      const int tok = base + r;
-      bf16x8 v = {};
-      if (tok < t1) v = *reinterpret_cast<const bf16x8*>(src + (int64_t)tok * sN + cc * 8);
+  bf16x8 v[LD];
+  auto load = [&](int base) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x) QT[cc * 8 + x][r] = v[x];
+    for (int u = 0; u < LD; ++u) {
+      const int e = threadIdx.x + 256 * u, r = e / CPR, cc = e % CPR;
+      v[u] = bf16x8{};
+      if (base + r < t1) v[u] = *reinterpret_cast<const bf16x8*>(src + (int64_t)(base + r) * sN + cc * 8);
     }
-    __syncthreads();
+  };
+  // lane's share of the transposing reads: 16-lane group g16, lane jl in it
+  const int g16 = lane >> 4, jl = lane & 15, h2 = lane >> 5;
+  load(t0);
+  int buf = 0;
+  for (int base = t0; base < t1; base += TOK, buf ^= 1) {
+    __bf16* Qb = Qs[buf];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int e = threadIdx.x + 256 * u, r = e / CPR, cc = e % CPR;
+      *reinterpret_cast<bf16x8*>(Qb + r * D + tr_swz<CPR>(r, cc) * 8) = v[u];
+    }
+    __syncthreads();  // this buffer was last read two steps ago, before the previous barrier
+    if (base + TOK < t1) load(base + TOK);
 #pragma unroll
     for (int ks = 0; ks < TOK / 16; ++ks) {
-      bf16x8 f[DT];
+      // fragment of channel tile i over tokens 16ks .. 16ks+15 (runtime i: an
+      // address, never an index into a register array)
+      auto frag = [&](int i) {
+        const int d = 32 * i + 16 * (g16 & 1) + 4 * (jl & 3);
+        const int cc = d >> 3, off = d & 7;
+        const int r0 = 16 * ks + 4 * h2 + (jl >> 2), r1 = r0 + 8;
+        const bf16x4 lo = lds_read_tr16(Qb + r0 * D + tr_swz<CPR>(r0, cc) * 8 + off);
+        const bf16x4 hi = lds_read_tr16(Qb + r1 * D + tr_swz<CPR>(r1, cc) * 8 + off);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      if constexpr (TPWV == DT) {  // wave w owns tiles (w, 0 .. DT-1)
+        const bf16x8 fa = frag(w);
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
-        f[i] = *reinterpret_cast<const bf16x8*>(&QT[32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int x = 0; x < TPWV; ++x) {
-        const int tile = w * TPWV + x;
-        if (tile < TILES) acc[x] = mfma32(f[tile / DT], f[tile % DT], acc[x]);
+        for (int x = 0; x < DT; ++x) acc[x] = mfma32(fa, frag(x), acc[x]);
+      } else {  // one tile per wave: (w / DT, w % DT)
+        static_assert(TPWV == 1 && TILES == 4, "tile split");
+        acc[0] = mfma32(frag(w / DT), frag(w % DT), acc[0]);
       }
     }
-    __syncthreads();
   }
   float* __restrict__ dst = part + ((int64_t)c * BH + bh) * D * D;
 #pragma unroll
@@ -197,76 +230,133 @@ __global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __rest
 }
 
 // ---- key features: u = z / |z|, z_d = sum_e k_e L[e][d] ----------------------------
-// On the matrix cores: K is exact in bf16 and L is split into bf16 hi + lo
-// (two products; the dropped remainder is below 2^-17 of L), staged
-// transposed in LDS once per workgroup.  Wave w takes 16 tiles of 32 tokens;
-// a tile is D/32 products of 32 x 32 outputs per 16-channel step.  Stored in
-// fp16 (unit vectors: |u_d| <= 1), which is what every later decision reads;
-// `u32` (optional) receives the same values in fp32.
-constexpr int kFeatTiles = 16;  // 32-token tiles per wave
+// On the matrix cores as Z^T = L^T K^T: wave w owns the 32 channels
+// 32w .. 32w+31 and keeps its L^T fragments in registers, with L split into
+// bf16 hi + lo (two products; the dropped remainder is below 2^-17 of L); K is
+// exact in bf16.  Tiles of 32 tokens are staged once per workgroup in LDS
+// (coalesced 16-byte loads, 16-byte chunks XOR-swizzled per row, two buffers,
+// three tiles' loads in flight in registers) and read as the B fragments.  In
+// the output layout lane l holds token l%32, so a token's squared norm is a
+// per-lane sum, one swap between the wave halves and one exchange of the
+// waves' partials through LDS; the normalised tile goes back through LDS and
+// out as whole rows (16-byte stores).  Stored in fp16 (unit vectors:
+// |u_d| <= 1), which is what every later decision reads; `u32` (optional)
+// receives the same values in fp32.
+constexpr int kFeatTokens = 1024;  // tokens per workgroup
 
 template <int D>
 __global__ __launch_bounds__(256) void key_feature_kernel(const __bf16* __restrict__ k, int64_t sB, int64_t sN,
                                                           int64_t sH, int H, int N, const float* __restrict__ factor,
                                                           _Float16* __restrict__ u, float* __restrict__ u32) {
-  constexpr int DT = D / 32, KS = D / 16, LP = D + 8;
-  __shared__ __align__(16) __bf16 LThi[D * LP];
-  __shared__ __align__(16) __bf16 LTlo[D * LP];
+  constexpr int DT = D / 32, KS = D / 16, CPR = D / 8;
+  constexpr int TT = 32;                // tokens per tile
+  constexpr int LDT = TT * CPR / 256;   // 16-byte loads per thread per tile
+  static_assert(LDT >= 1 && DT <= 4, "tile shape");
+  __shared__ __align__(16) __bf16 Ks[2][TT * D];
+  __shared__ __align__(16) _Float16 Os[TT * D];  // normalised tile, rows swizzled like Ks
+  __shared__ float Nsq[2][4][TT];
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float* __restrict__ Lg = factor + (int64_t)bh * D * D;
-  for (int idx = threadIdx.x; idx < D * D; idx += 256) {
-    const int e = idx / D, d = idx % D;
-    const float x = Lg[idx];
-    const __bf16 hi = (__bf16)x;
-    LThi[d * LP + e] = hi;
-    LTlo[d * LP + e] = (__bf16)(x - (float)hi);
-  }
-  __syncthreads();
-  const __bf16* __restrict__ src = k + b * sB + h * sH;
-  for (int tt = 0; tt < kFeatTiles; ++tt) {
-    const int t0 = ((blockIdx.x * 4 + w) * kFeatTiles + tt) * 32;
-    if (t0 >= N) break;  // whole wave
-    f32x16 acc[DT];
+  const int lane = threadIdx.x & 63, h2 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool active = w < DT;  // D = 64: waves 2 and 3 only stage
+  const int tb = blockIdx.x * kFeatTokens, te = min(N, tb + kFeatTokens);
+  // A fragments: lane l holds L[16ks + 8(l/32) + e][32w + l%32], e = 0..7
+  bf16x8 lhi[KS], llo[KS];
+  if (active) {
+    const float* __restrict__ Lg = factor + (int64_t)bh * D * D + 32 * w + (lane & 31);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-    const __bf16* __restrict__ krow = src + (int64_t)min(t0 + (lane & 31), N - 1) * sN + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int off = (32 * dt + (lane & 31)) * LP + 16 * ks + 8 * (lane >> 5);
-        acc[dt] = mfma32(a, *reinterpret_cast<const bf16x8*>(&LThi[off]), acc[dt]);
-        acc[dt] = mfma32(a, *reinterpret_cast<const bf16x8*>(&LTlo[off]), acc[dt]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = Lg[(16 * ks + 8 * h2 + e) * D];
+        const __bf16 hi = (__bf16)x;
+        lhi[ks][e] = hi;
+        llo[ks][e] = (__bf16)(x - (float)hi);
       }
-    }
-    // token row of register r: 8*(r/4) + 4*(lane/32) + r%4; its D values sit in
-    // the 32 lanes of this half-wave across the DT tiles
-    float inv[16];
+  }
+  const __bf16* __restrict__ src = k + b * sB + h * sH;
+  // three register sets: the loads of tile i + 3 are issued when tile i has
+  // been written to LDS, so three tiles are in flight per workgroup
+  bf16x8 v0[LDT], v1[LDT], v2[LDT];
+  auto load = [&](bf16x8* v, int t0) {
+    if (t0 >= te) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int q = 0; q < LDT; ++q) {
+      const int e = threadIdx.x + 256 * q, r = e / CPR, c = e % CPR;
+      v[q] = bf16x8{};
+      if (t0 + r < te) v[q] = *reinterpret_cast<const bf16x8*>(src + (int64_t)(t0 + r) * sN + 8 * c);
+    }
+  };
+  auto swz = [](int r, int c) { return c ^ (r & (CPR - 1)); };
+  // one tile: stage from v, refill v with tile t0 + 3 TT, products, norm, store
+  auto tile = [&](bf16x8* v, int t0, int buf) {
+    __bf16* Kb = Ks[buf];
+#pragma unroll
+    for (int q = 0; q < LDT; ++q) {
+      const int e = threadIdx.x + 256 * q, r = e / CPR, c = e % CPR;
+      *reinterpret_cast<bf16x8*>(Kb + r * D + swz(r, c) * 8) = v[q];
+    }
+    __syncthreads();  // tile visible; this buffer and Nsq[buf] were last read two tiles ago, Os one tile ago
+    load(v, t0 + 3 * TT);
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if (active) {
+      const int row = lane & 31;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kb + row * D + swz(row, 2 * ks + h2) * 8);
+        acc = mfma32(lhi[ks], kf, acc);
+        acc = mfma32(llo[ks], kf, acc);
+      }
+      // register 4j + i holds channel 32w + 8j + 4(l/32) + i of token l%32
       float sq = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) sq = fmaf(acc[dt][r], acc[dt][r], sq);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      inv[r] = (sq > 0.f) ? 1.f / sqrtf(sq) : 0.f;
+      for (int r = 0; r < 16; ++r) sq = fmaf(acc[r], acc[r], sq);
+      sq += xor32(sq);
+      if (h2 == 0) Nsq[buf][w][row] = sq;
     }
+    __syncthreads();
+    if (active) {
+      const int row = lane & 31, tok = t0 + row;
+      float tot = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = t0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (tok >= N) continue;
-      const int64_t row = ((int64_t)bh * N + tok) * D + (lane & 31);
+      for (int x = 0; x < DT; ++x) tot += Nsq[buf][x][row];
+      const float inv = (tot > 0.f) ? 1.f / sqrtf(tot) : 0.f;
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const _Float16 hv = (_Float16)(acc[dt][r] * inv[r]);
-        u[row + 32 * dt] = hv;
-        if (u32) u32[row + 32 * dt] = (float)hv;
+      for (int j = 0; j < 4; ++j) {
+        f16x4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(acc[4 * j + i] * inv);
+        // channels 32w + 8j + 4h2 .. +3: half h2 of logical chunk 4w + j
+        *reinterpret_cast<f16x4*>(Os + row * D + swz(row, 4 * w + j) * 8 + 4 * h2) = hv;
+        if (u32 && tok < te) {
+          const f32x4 fv = {(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+          *reinterpret_cast<f32x4*>(u32 + ((int64_t)bh * N + tok) * D + 32 * w + 8 * j + 4 * h2) = fv;
+        }
       }
     }
+    __syncthreads();
+    // whole rows out: 16-byte stores, consecutive lanes on consecutive chunks
+#pragma unroll
+    for (int q = 0; q < LDT; ++q) {
+      const int e = threadIdx.x + 256 * q, r = e / CPR, c = e % CPR;
+      if (t0 + r < te)
+        *reinterpret_cast<bf16x8*>(u + ((int64_t)bh * N + t0 + r) * D + 8 * c) =
+            *reinterpret_cast<const bf16x8*>(Os + r * D + swz(r, c) * 8);
+    }
+  };
+  load(v0, tb);
+  load(v1, tb + TT);
+  load(v2, tb + 2 * TT);
+  // tile i uses LDS buffer i & 1 (every bound is uniform over the workgroup)
+  for (int i = 0, t0 = tb; t0 < te; i += 3, t0 += 3 * TT) {
+    tile(v0, t0, i & 1);
+    if (t0 + TT >= te) break;
+    tile(v1, t0 + TT, (i + 1) & 1);
+    if (t0 + 2 * TT >= te) break;
+    tile(v2, t0 + 2 * TT, i & 1);
   }
 }
 
@@ -681,8 +771,7 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
   moment_reduce_kernel<<<dim3((unsigned)((D * D + 255) / 256), (unsigned)BH), 256, 0, s>>>(p.part, nc, D * D, N,
                                                                                          p.moment);
   moment_factor_kernel<D><<<dim3((unsigned)BH), 1024, 0, s>>>(p.moment, p.ridge, p.factor);
-  const int ftok = 4 * kFeatTiles * 32;  // tokens per feature workgroup
-  key_feature_kernel<D><<<dim3((unsigned)((N + ftok - 1) / ftok), (unsigned)BH), 256, 0, s>>>(
+  key_feature_kernel<D><<<dim3((unsigned)((N + kFeatTokens - 1) / kFeatTokens), (unsigned)BH), 256, 0, s>>>(
       reinterpret_cast<const __bf16*>(p.k), p.sB, p.sN, p.sH, p.H, N, p.factor, p.features, p.features32);
   iota_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(p.order0, N, total);
   hipError_t e = hipGetLastError();

@@ -360,92 +360,143 @@ __global__ __launch_bounds__(256) void key_feature_kernel(const __bf16* __restri
   }
 }
 
+// ---- principal axis of the centred landmarks (one wave) ----------------------------------
+// X: 32 centred landmark rows in LDS, row stride ldx floats.  The Gram matrix
+// G = X X^T runs on the matrix cores (X split into bf16 hi + lo, three
+// products, fp32-accurate): lane l holds row l%32, channels 16ks + 8(l/32) + 0..7,
+// the A fragment of rows and the B fragment of columns alike.  G is symmetric,
+// so the output layout gives lanes l and l+32 the two halves of row l%32; after
+// one swap every lane holds its whole row in registers and each of the 16 power
+// iterations from the ramp is 32 broadcast-FMAs and a 32-term broadcast sum.
+// Returns a_s in lanes s and s + 32.
+template <int D>
+__device__ __forceinline__ float landmark_axis(const float* X, int ldx, int lane) {
+  static_assert(kLandmarks == 32, "one 32 x 32 Gram tile");
+  const int h2 = lane >> 5, s = lane & 31;
+  f32x16 g;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) g[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const float xv = X[s * ldx + 16 * ks + 8 * h2 + x];
+      hi[x] = (__bf16)xv;
+      lo[x] = (__bf16)(xv - (float)hi[x]);
+    }
+    g = mfma32(lo, hi, g);
+    g = mfma32(hi, lo, g);
+    g = mfma32(hi, hi, g);
+  }
+  // g[4j + i] = G[8j + 4 h2 + i][s] = G[s][8j + 4 h2 + i]
+  float row[kLandmarks];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float other = xor32(g[r]);
+    const int j = r >> 2, i = r & 3;
+    row[8 * j + i] = h2 ? other : g[r];
+    row[8 * j + 4 + i] = h2 ? g[r] : other;
+  }
+  auto bcast = [](float x, int t) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), t));
+  };
+  // ramp start s - 15.5, normalised: |ramp|^2 = sum (s - 15.5)^2 = 2728 for 32 landmarks
+  float a = ((float)s - 0.5f * (kLandmarks - 1)) * rsqrtf(2728.f);
+  for (int it = 0; it < kPowerIters; ++it) {
+    float wv = 0.f;
+#pragma unroll
+    for (int t = 0; t < kLandmarks; ++t) wv = fmaf(row[t], bcast(a, t), wv);
+    const float sq = wv * wv;
+    float n2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < kLandmarks; ++t) n2 += bcast(sq, t);
+    if (n2 == 0.f) {  // uniform: the landmarks coincide
+      a = wv;
+      break;
+    }
+    a = wv / sqrtf(n2);
+  }
+  return a;
+}
+
+// One wave: centre the 32 landmark rows of X (LDS, row stride ldx), find their
+// principal axis a (landmark_axis; a_sh receives it), form v = X^T a, normalise
+// it and give its largest-magnitude entry (lowest index on ties) a positive
+// sign.  v (LDS, D floats) receives the unit direction.
+template <int D>
+__device__ __forceinline__ void wave_direction(float* X, int ldx, float* a_sh, float* v, int lane) {
+  constexpr int PL = D / 64;  // channels per lane
+#pragma unroll
+  for (int x = 0; x < PL; ++x) {
+    const int d = lane + 64 * x;
+    float col[kLandmarks];
+    float m = 0.f;
+#pragma unroll
+    for (int s = 0; s < kLandmarks; ++s) col[s] = X[s * ldx + d], m += col[s];
+    m /= (float)kLandmarks;
+#pragma unroll
+    for (int s = 0; s < kLandmarks; ++s) X[s * ldx + d] = col[s] - m;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const float a = landmark_axis<D>(X, ldx, lane);
+  if (lane < kLandmarks) a_sh[lane] = a;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  float vd[PL];
+  float n2 = 0.f, best = -1.f;
+  int bi = 0;
+#pragma unroll
+  for (int x = 0; x < PL; ++x) {
+    const int d = lane + 64 * x;
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < kLandmarks; ++s) acc = fmaf(X[s * ldx + d], a_sh[s], acc);
+    vd[x] = acc;
+    n2 = fmaf(acc, acc, n2);
+    if (fabsf(acc) > best) best = fabsf(acc), bi = d;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n2 += __shfl_xor(n2, o, 64);
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ob > best || (ob == best && oi < bi)) best = ob, bi = oi;
+  }
+  float sgn = 1.f;
+#pragma unroll
+  for (int x = 0; x < PL; ++x)
+    if (lane + 64 * x == bi) sgn = (vd[x] < 0.f) ? -1.f : 1.f;
+  sgn = __shfl(sgn, bi % 64, 64);
+  const float scale = (n2 > 0.f) ? sgn / sqrtf(n2) : sgn;
+#pragma unroll
+  for (int x = 0; x < PL; ++x) v[lane + 64 * x] = vd[x] * scale;
+}
+
 // ---- split direction of one node (all 256 threads of the workgroup) -----------------------
 template <int D>
 struct DirScratch {
   float X[kLandmarks][D + 1];
-  float G[kLandmarks][kLandmarks + 1];
   float a[kLandmarks];
-  float red_v[256];
-  int red_i[256];
-  float sgn;
 };
 
 // ord: the node's tokens in their current order (global or LDS); ub: the
-// head's features.  Leaves the unit direction in v (LDS, D floats).
+// head's features.  Leaves the unit direction in v (LDS, D floats).  The
+// landmark rows are gathered by the whole workgroup (16-byte loads), the rest
+// runs in wave 0.
 template <int D>
 __device__ void node_direction(const _Float16* __restrict__ ub, const int32_t* ord, int n, DirScratch<D>& sh,
                                float* v) {
-  for (int e = threadIdx.x; e < kLandmarks * D; e += 256) {
-    const int s = e / D, d = e % D;
+  for (int e = threadIdx.x; e < kLandmarks * (D / 8); e += blockDim.x) {
+    const int s = e / (D / 8), cc = e % (D / 8);
     const int tok = ord[(int)(((int64_t)(2 * s + 1) * n) / (2 * kLandmarks))];
-    sh.X[s][d] = (float)ub[(int64_t)tok * D + d];
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float m = 0.f;
-    for (int s = 0; s < kLandmarks; ++s) m += sh.X[s][d];
-    m /= (float)kLandmarks;
-    for (int s = 0; s < kLandmarks; ++s) sh.X[s][d] -= m;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kLandmarks * kLandmarks; e += 256) {
-    const int s = e / kLandmarks, t = e % kLandmarks;
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(sh.X[s][d], sh.X[t][d], acc);
-    sh.G[s][t] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {  // power iteration, one wave, lane s < 32 holds a_s
-    const int lane = threadIdx.x;
-    // ramp start s - 15.5, normalised: |ramp|^2 = sum (s - 15.5)^2 = 2728 for 32 landmarks
-    float a = (lane < kLandmarks) ? ((float)lane - 0.5f * (kLandmarks - 1)) * rsqrtf(2728.f) : 0.f;
-    for (int it = 0; it < kPowerIters; ++it) {
-      float w = 0.f;
-      for (int t = 0; t < kLandmarks; ++t) {
-        const float at = __shfl(a, t, 64);
-        if (lane < kLandmarks) w = fmaf(sh.G[lane][t], at, w);
-      }
-      float n2 = w * w;
+    const half8 h = *reinterpret_cast<const half8*>(ub + (int64_t)tok * D + 8 * cc);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
-      if (n2 == 0.f) {  // uniform: the landmarks coincide
-        a = w;
-        break;
-      }
-      a = w / sqrtf(n2);
-    }
-    if (lane < kLandmarks) sh.a[lane] = a;
+    for (int x = 0; x < 8; ++x) sh.X[s][8 * cc + x] = (float)h[x];
   }
   __syncthreads();
-  float vd = 0.f;
-  const int d = threadIdx.x;
-  if (d < D)
-    for (int s = 0; s < kLandmarks; ++s) vd = fmaf(sh.X[s][d], sh.a[s], vd);
-  sh.red_v[threadIdx.x] = vd * vd;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) sh.red_v[threadIdx.x] += sh.red_v[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float nrm = sqrtf(sh.red_v[0]);
-  __syncthreads();
-  // largest |v_d|, lowest d on ties
-  sh.red_v[threadIdx.x] = (d < D) ? fabsf(vd) : -1.f;
-  sh.red_i[threadIdx.x] = d;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const float x = sh.red_v[threadIdx.x + o];
-      const int xi = sh.red_i[threadIdx.x + o];
-      if (x > sh.red_v[threadIdx.x] || (x == sh.red_v[threadIdx.x] && xi < sh.red_i[threadIdx.x]))
-        sh.red_v[threadIdx.x] = x, sh.red_i[threadIdx.x] = xi;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == sh.red_i[0]) sh.sgn = (vd < 0.f) ? -1.f : 1.f;
-  __syncthreads();
-  if (d < D) v[d] = vd * ((nrm > 0.f) ? sh.sgn / nrm : sh.sgn);
+  if (threadIdx.x < 64) wave_direction<D>(&sh.X[0][0], D + 1, sh.a, v, threadIdx.x);
   __syncthreads();
 }
 
@@ -469,7 +520,8 @@ __device__ __forceinline__ float project16(const _Float16* __restrict__ ur, cons
   return acc;
 }
 
-// Projection u . v of one member by one thread (the whole fp16 row; v in LDS).
+// Projection u . v of one member by one lane (the whole fp16 row; v in LDS):
+// within one wave every lane's row loads are in flight together.
 template <int D>
 __device__ __forceinline__ float project_row(const _Float16* __restrict__ ur, const float* v) {
   float acc = 0.f;
@@ -480,6 +532,46 @@ __device__ __forceinline__ float project_row(const _Float16* __restrict__ ur, co
     for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[8 * c + e], acc);
   }
   return acc;
+}
+
+// Projections u . v of 16 members by one 16-lane group: lane j reads 16 bytes
+// of every member row (whole rows per group, coalesced) and keeps 16 partial
+// sums; a butterfly reduce-scatter (8 + 4 + 2 + 1 independent exchanges)
+// leaves member `base + j`'s projection in lane j.  ord: the node's tokens;
+// members at or beyond n read member 0's row (their results are unused).
+template <int D>
+__device__ __forceinline__ float project_batch16(const _Float16* __restrict__ ub, const int32_t* ord, int base, int n,
+                                                 const float* v, int l16) {
+  constexpr int PER = D / 16;  // channels per lane
+  float part[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int i = base + m;
+    const _Float16* __restrict__ ur = ub + (int64_t)ord[(i < n) ? i : 0] * D + l16 * PER;
+    float acc = 0.f;
+    if constexpr (PER == 8) {
+      const half8 h = *reinterpret_cast<const half8*>(ur);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[l16 * 8 + e], acc);
+    } else {
+      const half4 h = *reinterpret_cast<const half4*>(ur);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf((float)h[e], v[l16 * 4 + e], acc);
+    }
+    part[m] = acc;
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    // lanes with bit o clear keep values [0, o), the others [o, 2o)
+    const bool hi = (l16 & o) != 0;
+#pragma unroll
+    for (int m = 0; m < o; ++m) {
+      const float send = hi ? part[m] : part[m + o];
+      const float keep = hi ? part[m + o] : part[m];
+      part[m] = keep + __shfl_xor(send, o, 16);
+    }
+  }
+  return part[0];
 }
 
 // ---- one level, large nodes: split directions ----------------------------------------------
@@ -520,8 +612,9 @@ __global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __rest
   }
 }
 
-// ---- one level, nodes of at most kLocalCap tokens: direction, projections and a
-// stable bitonic sort of (projection key, position) in LDS, one workgroup per node.
+// ---- one level, nodes of at most kLocalCap tokens: direction, projections (16
+// members per 16-lane group) and a stable block radix sort of the projection keys with
+// the positions as values (the order of (key, position)), one workgroup per node.
 constexpr int kLocalCap = 4096;
 
 template <int D, int CAP>
@@ -529,6 +622,11 @@ __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16
                                                                   const int32_t* __restrict__ cur,
                                                                   int32_t* __restrict__ nxt, int N, int M, int level,
                                                                   int max_slots, float* __restrict__ dirs_out) {
+  constexpr int IPT = CAP / 256;
+  using Sorter = hipcub::BlockRadixSort<uint32_t, 256, IPT, int32_t>;
+  constexpr size_t kScratch = sizeof(typename Sorter::TempStorage) > sizeof(DirScratch<D>)
+                                  ? sizeof(typename Sorter::TempStorage)
+                                  : sizeof(DirScratch<D>);
   const int slot = blockIdx.x, bh = blockIdx.y;
   int start, n, c;
   slot_range(N, M, level, slot, &start, &n, &c);
@@ -540,35 +638,35 @@ __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16
     return;
   }
   __shared__ int32_t ord[CAP];
-  __shared__ uint64_t keys[CAP];
-  __shared__ DirScratch<D> sh;
+  __shared__ uint32_t pkey[CAP];
+  __shared__ __align__(16) unsigned char scratch[kScratch];  // direction scratch, then the sort's
   __shared__ float v[D];
   for (int i = threadIdx.x; i < n; i += 256) ord[i] = src[i];
   __syncthreads();
   const _Float16* __restrict__ ub = u + (int64_t)bh * N * D;
-  node_direction<D>(ub, ord, n, sh, v);
+  node_direction<D>(ub, ord, n, *reinterpret_cast<DirScratch<D>*>(scratch), v);
   if (dirs_out)
     for (int d = threadIdx.x; d < D; d += 256) dirs_out[((int64_t)bh * max_slots + slot) * D + d] = v[d];
-  int P = 1;
-  while (P < n) P <<= 1;
-  for (int i = threadIdx.x; i < P; i += 256) {  // one member per thread
-    uint64_t key = ~0ull;
-    if (i < n) key = ((uint64_t)float_key(project_row<D>(ub + (int64_t)ord[i] * D, v)) << 32) | (uint32_t)i;
-    keys[i] = key;
+  const int l16 = threadIdx.x & 15;
+  for (int base = 16 * (threadIdx.x >> 4); base < n; base += 256) {  // uniform within each 16-lane group
+    const float pr = project_batch16<D>(ub, ord, base, n, v, l16);
+    if (base + l16 < n) pkey[base + l16] = float_key(pr);
   }
   __syncthreads();
-  for (int kk = 2; kk <= P; kk <<= 1)
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += 256) {
-        const int ij = i ^ j;
-        if (ij > i) {
-          const uint64_t a = keys[i], b = keys[ij];
-          if ((a > b) == ((i & kk) == 0)) keys[i] = b, keys[ij] = a;
-        }
-      }
-      __syncthreads();
-    }
-  for (int i = threadIdx.x; i < n; i += 256) dst[i] = ord[(int)(keys[i] & 0xffffffffu)];
+  uint32_t kk[IPT];
+  int32_t vv[IPT];
+#pragma unroll
+  for (int x = 0; x < IPT; ++x) {
+    const int i = threadIdx.x * IPT + x;  // blocked arrangement
+    kk[x] = (i < n) ? pkey[i] : 0xffffffffu;  // padding sorts last (positions above every member)
+    vv[x] = i;
+  }
+  Sorter(*reinterpret_cast<typename Sorter::TempStorage*>(scratch)).Sort(kk, vv);
+#pragma unroll
+  for (int x = 0; x < IPT; ++x) {
+    const int i = threadIdx.x * IPT + x;
+    if (i < n) dst[i] = ord[vv[x]];
+  }
 }
 
 __global__ void iota_kernel(int32_t* __restrict__ order, int N, int64_t total) {
@@ -586,11 +684,12 @@ __global__ void reblock_tables_kernel(const int32_t* __restrict__ order, int N, 
   if (bh == 0 && p % M == 0) block_len[p / M] = min(M, N - p);
 }
 
-// ---- one level, nodes of at most 256 tokens: one wave per node, 4 nodes per workgroup --------
+// ---- one level, nodes of at most 256 tokens: one wave per node, two nodes per workgroup -----
 // The same steps as the block-level kernel with wave-level synchronisation; the
 // landmark Gram matrix runs on the matrix cores (centred landmarks split into
 // bf16 hi + lo, three products, fp32-accurate).
 constexpr int kWaveCap = 256;
+constexpr int kWaveNodes = 2;  // nodes (waves) per workgroup
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -600,7 +699,6 @@ __device__ __forceinline__ void wave_sync() {
 template <int D>
 struct WaveNode {
   float X[kLandmarks][D + 4];
-  float G[kLandmarks][kLandmarks + 1];
   float v[D];
   float a[kLandmarks];
   int32_t ord[kWaveCap];
@@ -608,13 +706,13 @@ struct WaveNode {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void reblock_wave_level_kernel(const _Float16* __restrict__ u,
+__global__ __launch_bounds__(128) void reblock_wave_level_kernel(const _Float16* __restrict__ u,
                                                                  const int32_t* __restrict__ cur,
                                                                  int32_t* __restrict__ nxt, int N, int M, int level,
                                                                  int nslots, int max_slots, float* __restrict__ dirs_out) {
-  __shared__ WaveNode<D> wn[4];
+  __shared__ WaveNode<D> wn[kWaveNodes];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int slot = blockIdx.x * 4 + w, bh = blockIdx.y;
+  const int slot = blockIdx.x * kWaveNodes + w, bh = blockIdx.y;
   if (slot >= nslots) return;  // whole wave
   int start, n, c;
   slot_range(N, M, level, slot, &start, &n, &c);
@@ -629,7 +727,7 @@ __global__ __launch_bounds__(256) void reblock_wave_level_kernel(const _Float16*
   const _Float16* __restrict__ ub = u + (int64_t)bh * N * D;
   for (int i = lane; i < n; i += 64) sh.ord[i] = src[i];
   wave_sync();
-  // landmarks, centred
+  // landmarks
   for (int e = lane; e < kLandmarks * (D / 8); e += 64) {
     const int s = e / (D / 8), cc = e % (D / 8);
     const int tok = sh.ord[(int)(((int64_t)(2 * s + 1) * n) / (2 * kLandmarks))];
@@ -638,85 +736,9 @@ __global__ __launch_bounds__(256) void reblock_wave_level_kernel(const _Float16*
     for (int x = 0; x < 8; ++x) sh.X[s][8 * cc + x] = (float)h[x];
   }
   wave_sync();
-  for (int d = lane; d < D; d += 64) {
-    float m = 0.f;
-    for (int s = 0; s < kLandmarks; ++s) m += sh.X[s][d];
-    m /= (float)kLandmarks;
-    for (int s = 0; s < kLandmarks; ++s) sh.X[s][d] -= m;
-  }
-  wave_sync();
-  // G = X X^T on the matrix cores: lane l holds row l%32, channels 16 ks + 8 (l/32) + 0..7,
-  // which is the A fragment of rows and the B fragment of columns alike
-  f32x16 g;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) g[r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    bf16x8 hi, lo;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const float xv = sh.X[lane & 31][16 * ks + 8 * (lane >> 5) + x];
-      hi[x] = (__bf16)xv;
-      lo[x] = (__bf16)(xv - (float)hi[x]);
-    }
-    g = mfma32(lo, hi, g);
-    g = mfma32(hi, lo, g);
-    g = mfma32(hi, hi, g);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sh.G[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = g[r];
-  wave_sync();
-  // power iteration from the ramp (lane s < 32 holds a_s)
-  float a = (lane < kLandmarks) ? ((float)lane - 0.5f * (kLandmarks - 1)) * rsqrtf(2728.f) : 0.f;
-  for (int it = 0; it < kPowerIters; ++it) {
-    float wv = 0.f;
-    for (int t = 0; t < kLandmarks; ++t) {
-      const float at = __shfl(a, t, 64);
-      if (lane < kLandmarks) wv = fmaf(sh.G[lane][t], at, wv);
-    }
-    float n2 = wv * wv;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
-    if (n2 == 0.f) {
-      a = wv;
-      break;
-    }
-    a = wv / sqrtf(n2);
-  }
-  if (lane < kLandmarks) sh.a[lane] = a;
-  wave_sync();
-  // v = X^T a; norm and the sign of the largest entry (lowest index on ties)
-  constexpr int PL = D / 64;  // channels per lane
-  float vd[PL];
-  float n2 = 0.f, best = -1.f;
-  int bi = 0;
-#pragma unroll
-  for (int x = 0; x < PL; ++x) {
-    const int d = lane + 64 * x;
-    float acc = 0.f;
-    for (int s = 0; s < kLandmarks; ++s) acc = fmaf(sh.X[s][d], sh.a[s], acc);
-    vd[x] = acc;
-    n2 = fmaf(acc, acc, n2);
-    if (fabsf(acc) > best) best = fabsf(acc), bi = d;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    n2 += __shfl_xor(n2, o, 64);
-    const float ob = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ob > best || (ob == best && oi < bi)) best = ob, bi = oi;
-  }
-  float sgn = 1.f;
-#pragma unroll
-  for (int x = 0; x < PL; ++x)
-    if (lane + 64 * x == bi) sgn = (vd[x] < 0.f) ? -1.f : 1.f;
-  sgn = __shfl(sgn, bi % 64, 64);
-  const float scale = (n2 > 0.f) ? sgn / sqrtf(n2) : sgn;
-#pragma unroll
-  for (int x = 0; x < PL; ++x) {
-    sh.v[lane + 64 * x] = vd[x] * scale;
-    if (dirs_out) dirs_out[((int64_t)bh * max_slots + slot) * D + lane + 64 * x] = vd[x] * scale;
-  }
+  wave_direction<D>(&sh.X[0][0], D + 4, sh.a, sh.v, lane);
+  if (dirs_out)
+    for (int d = lane; d < D; d += 64) dirs_out[((int64_t)bh * max_slots + slot) * D + d] = sh.v[d];
   wave_sync();
   // projections (one member per lane), then a stable bitonic sort of (key, position)
   int P = 1;
@@ -792,7 +814,8 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
     if (nmax <= kLocalCap) {
       const dim3 grid((unsigned)nslots, (unsigned)BH);
       if (nmax <= kWaveCap)
-        reblock_wave_level_kernel<D><<<dim3((unsigned)((nslots + 3) / 4), (unsigned)BH), 256, 0, s>>>(
+        reblock_wave_level_kernel<D><<<dim3((unsigned)((nslots + kWaveNodes - 1) / kWaveNodes), (unsigned)BH),
+                                       64 * kWaveNodes, 0, s>>>(
             p.features, cur, nxt, N, M, lev, nslots, max_slots, dirs_dbg);
       else if (nmax <= 1024)
         reblock_local_level_kernel<D, 1024><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);

@@ -446,7 +446,7 @@ def bench_coarse(args):
         "roofline": {"kernel": "vsa4_kernel with the coarse epilogue (bsa_forward_qouter, block mode)",
                      "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _profiled_traffic("vsa4_kernel_coarse.md",
+                     "traffic": _profiled_traffic("coarse_kernel_video.md",
                                                   ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp"))},
     }
     ctx = dict(cfg=cfg, x=x, gate=gate)

@@ -500,26 +500,6 @@ __device__ void node_direction(const _Float16* __restrict__ ub, const int32_t* o
   __syncthreads();
 }
 
-// Projection u . v of one member, 16 lanes (8 fp16 channels each for D = 128,
-// 4 for D = 64); every lane of the 16 ends with the sum.
-template <int D>
-__device__ __forceinline__ float project16(const _Float16* __restrict__ ur, const float* v, int l16) {
-  constexpr int PER = D / 16;
-  float acc = 0.f;
-  if constexpr (PER == 8) {
-    const half8 h = *reinterpret_cast<const half8*>(ur + l16 * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[l16 * 8 + e], acc);
-  } else {
-    const half4 h = *reinterpret_cast<const half4*>(ur + l16 * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf((float)h[e], v[l16 * 4 + e], acc);
-  }
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
-  return acc;
-}
-
 // Projection u . v of one member by one lane (the whole fp16 row; v in LDS):
 // within one wave every lane's row loads are in flight together.
 template <int D>
@@ -534,44 +514,57 @@ __device__ __forceinline__ float project_row(const _Float16* __restrict__ ur, co
   return acc;
 }
 
-// Projections u . v of 16 members by one 16-lane group: lane j reads 16 bytes
-// of every member row (whole rows per group, coalesced) and keeps 16 partial
-// sums; a butterfly reduce-scatter (8 + 4 + 2 + 1 independent exchanges)
-// leaves member `base + j`'s projection in lane j.  ord: the node's tokens;
-// members at or beyond n read member 0's row (their results are unused).
+// Projections u . v of 16·NB members by one 16-lane group: lane j reads 16
+// bytes of every member row (whole rows per group, coalesced; all NB·16 row
+// loads in flight together) and keeps one partial sum per member; per batch
+// of 16 a butterfly reduce-scatter (8 + 4 + 2 + 1 independent exchanges)
+// leaves member `base + 16b + j`'s projection in lane j of out[b].  ord: the
+// node's tokens; members at or beyond n read member 0's row (results unused).
+template <int D, int NB>
+__device__ __forceinline__ void project_batches(const _Float16* __restrict__ ub, const int32_t* ord, int base, int n,
+                                                const float* v, int l16, float* out) {
+  constexpr int PER = D / 16;  // channels per lane
+  using HV = typename std::conditional<PER == 8, half8, half4>::type;
+  HV h[NB * 16];
+#pragma unroll
+  for (int m = 0; m < NB * 16; ++m) {
+    const int i = base + m;
+    h[m] = *reinterpret_cast<const HV*>(ub + (int64_t)ord[(i < n) ? i : 0] * D + l16 * PER);
+  }
+  float vr[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) vr[e] = v[l16 * PER + e];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float part[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc = fmaf((float)h[16 * b + m][e], vr[e], acc);
+      part[m] = acc;
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      // lanes with bit o clear keep values [0, o), the others [o, 2o)
+      const bool hi = (l16 & o) != 0;
+#pragma unroll
+      for (int m = 0; m < o; ++m) {
+        const float send = hi ? part[m] : part[m + o];
+        const float keep = hi ? part[m + o] : part[m];
+        part[m] = keep + __shfl_xor(send, o, 16);
+      }
+    }
+    out[b] = part[0];
+  }
+}
+
 template <int D>
 __device__ __forceinline__ float project_batch16(const _Float16* __restrict__ ub, const int32_t* ord, int base, int n,
                                                  const float* v, int l16) {
-  constexpr int PER = D / 16;  // channels per lane
-  float part[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int i = base + m;
-    const _Float16* __restrict__ ur = ub + (int64_t)ord[(i < n) ? i : 0] * D + l16 * PER;
-    float acc = 0.f;
-    if constexpr (PER == 8) {
-      const half8 h = *reinterpret_cast<const half8*>(ur);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)h[e], v[l16 * 8 + e], acc);
-    } else {
-      const half4 h = *reinterpret_cast<const half4*>(ur);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = fmaf((float)h[e], v[l16 * 4 + e], acc);
-    }
-    part[m] = acc;
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    // lanes with bit o clear keep values [0, o), the others [o, 2o)
-    const bool hi = (l16 & o) != 0;
-#pragma unroll
-    for (int m = 0; m < o; ++m) {
-      const float send = hi ? part[m] : part[m + o];
-      const float keep = hi ? part[m + o] : part[m];
-      part[m] = keep + __shfl_xor(send, o, 16);
-    }
-  }
-  return part[0];
+  float r;
+  project_batches<D, 1>(ub, ord, base, n, v, l16, &r);
+  return r;
 }
 
 // ---- one level, large nodes: split directions ----------------------------------------------
@@ -589,33 +582,38 @@ __global__ __launch_bounds__(256) void reblock_direction_kernel(const _Float16* 
   for (int d = threadIdx.x; d < D; d += 256) dirs[((int64_t)bh * max_slots + slot) * D + d] = v[d];
 }
 
-// ---- one level, large nodes: projection keys (16 lanes per position) ------------------------
+// ---- one level, large nodes: projection keys (16 positions per 16-lane group) --------------
+// Node ranges start at multiples of M (16, 32 or 64), so the 16 aligned
+// positions of a batch belong to one node and share its direction.
 template <int D>
 __global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __restrict__ u,
                                                           const int32_t* __restrict__ order,
                                                           const float* __restrict__ dirs, int N, int M, int level,
-                                                          int max_slots, int64_t total, uint64_t* __restrict__ keys,
+                                                          int max_slots, uint64_t* __restrict__ keys,
                                                           int32_t* __restrict__ vals) {
-  const int64_t g = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int bh = blockIdx.y;
+  const int pos0 = (blockIdx.x * 16 + (int)threadIdx.x / 16) * 16;
   const int l16 = threadIdx.x % 16;
-  if (g >= total) return;  // the 16 lanes of a position leave together
-  const int bh = (int)(g / N), pos = (int)(g % N);
+  if (pos0 >= N) return;  // the 16 lanes of a batch leave together
+  const int cnt = min(16, N - pos0);
   int c;
-  const int slot = slot_of(N, M, level, pos, &c);
-  const int tok = order[g];
+  const int slot = slot_of(N, M, level, pos0, &c);
+  const int32_t* __restrict__ ord = order + (int64_t)bh * N + pos0;
   uint32_t fk = 0u;
   if (c > 1)
-    fk = float_key(project16<D>(u + ((int64_t)bh * N + tok) * D, dirs + ((int64_t)bh * max_slots + slot) * D, l16));
-  if (l16 == 0) {
+    fk = float_key(project_batch16<D>(u + (int64_t)bh * N * D, ord, 0, cnt,
+                                      dirs + ((int64_t)bh * max_slots + slot) * D, l16));
+  if (l16 < cnt) {
+    const int64_t g = (int64_t)bh * N + pos0 + l16;
     keys[g] = ((uint64_t)bh << (32 + level)) | ((uint64_t)slot << 32) | fk;
-    vals[g] = tok;
+    vals[g] = ord[l16];
   }
 }
 
 // ---- one level, nodes of at most kLocalCap tokens: direction, projections (16
-// members per 16-lane group) and a stable block radix sort of the projection keys with
+// members per 16-lane group at a time) and a stable block radix sort of the projection keys with
 // the positions as values (the order of (key, position)), one workgroup per node.
-constexpr int kLocalCap = 4096;
+constexpr int kLocalCap = 8192;  // capacities 1024, 4096, 8192 (the largest: one workgroup per CU)
 
 template <int D, int CAP>
 __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16* __restrict__ u,
@@ -819,6 +817,8 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
             p.features, cur, nxt, N, M, lev, nslots, max_slots, dirs_dbg);
       else if (nmax <= 1024)
         reblock_local_level_kernel<D, 1024><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
+      else if (nmax <= 4096)
+        reblock_local_level_kernel<D, 4096><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots, dirs_dbg);
       else
         reblock_local_level_kernel<D, kLocalCap><<<grid, 256, 0, s>>>(p.features, cur, nxt, N, M, lev, max_slots,
                                                                       dirs_dbg);
@@ -828,8 +828,9 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
       float* dirs = dirs_dbg ? dirs_dbg : p.dirs;
       reblock_direction_kernel<D><<<dim3((unsigned)nslots, (unsigned)BH), 256, 0, s>>>(p.features, cur, N, M, lev,
                                                                                         max_slots, dirs);
-      reblock_key_kernel<D><<<dim3((unsigned)((total + 15) / 16)), 256, 0, s>>>(p.features, cur, dirs, N, M, lev,
-                                                                               max_slots, total, p.keys0, p.vals0);
+      const int nbatch = (N + 15) / 16;  // 16 positions per 16-lane group, 16 groups per workgroup
+      reblock_key_kernel<D><<<dim3((unsigned)((nbatch + 15) / 16), (unsigned)BH), 256, 0, s>>>(
+          p.features, cur, dirs, N, M, lev, max_slots, p.keys0, p.vals0);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       size_t bytes = p.sort_bytes;

@@ -36,6 +36,7 @@ CFGS = {
     "video_2k_d128": (scaled("video", grid=(8, 16, 16), h=2), 64),
     "ragged_d64": (scaled("video", grid=(7, 9, 13), h=2, D=64), 64),      # 819 tokens: a 51-token last leaf
     "m32": (scaled("video", grid=(6, 12, 20), h=2), 32),
+    "root_7400_d64": (scaled("video", grid=(8, 25, 37), h=1, D=64), 64),  # a root above 4096 tokens: the 8192-capacity level
 }
 
 

@@ -189,8 +189,9 @@ __global__ void moment_reduce_kernel(const float* __restrict__ part, int nc, int
   moment[(int64_t)bh * DD + e] = sum / (float)N;
 }
 
-// Ridge and Cholesky (right-looking, column by column, in LDS).  A pivot that
-// rounding drives below the ridge is clamped to it.
+// Ridge and Cholesky (right-looking, column by column, in LDS; two barriers per
+// column, no index division).  A pivot that rounding drives below the ridge is
+// clamped to it.
 template <int D>
 __global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __restrict__ moment, float ridge,
                                                              float* __restrict__ factor) {
@@ -210,16 +211,18 @@ __global__ __launch_bounds__(1024) void moment_factor_kernel(const float* __rest
   const float lam = lam_sh;
   for (int d = threadIdx.x; d < D; d += 1024) A[d][d] += lam;
   __syncthreads();
+  // threads as 32 x 32 (row phase, column phase) over the trailing triangle
+  const int ti = threadIdx.x >> 5, tk = threadIdx.x & 31;
   for (int j = 0; j < D; ++j) {
-    if (threadIdx.x == 0) A[j][j] = sqrtf(fmaxf(A[j][j], lam));
+    if (threadIdx.x < 64) {  // wave 0: pivot, then the column below it
+      const float djj = sqrtf(fmaxf(A[j][j], lam));
+      for (int i = j + 1 + threadIdx.x; i < D; i += 64) A[i][j] /= djj;
+      if (threadIdx.x == 0) A[j][j] = djj;
+    }
     __syncthreads();
-    const float djj = A[j][j];
-    for (int i = j + 1 + threadIdx.x; i < D; i += 1024) A[i][j] /= djj;
-    __syncthreads();
-    const int m = D - j - 1;
-    for (int e = threadIdx.x; e < m * m; e += 1024) {
-      const int i = j + 1 + e / m, k = j + 1 + e % m;
-      if (k <= i) A[i][k] = fmaf(-A[i][j], A[k][j], A[i][k]);
+    for (int i = j + 1 + ti; i < D; i += 32) {
+      const float aij = A[i][j];
+      for (int k = j + 1 + tk; k <= i; k += 32) A[i][k] = fmaf(-aij, A[k][j], A[i][k]);
     }
     __syncthreads();
   }

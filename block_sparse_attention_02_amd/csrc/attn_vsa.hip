@@ -723,6 +723,22 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
       r[k] = (uint32_t)min(64 * tau + 16 * w + TM::LPT * (lane / TM::CPR) + k, p.J - 1) * (uint32_t)(D * 2);
   };
 
+  // byte offsets (from the LDS base) of this lane's V transposing reads per
+  // buffer and 32-channel tile: r0 = 32g + 4h2 + (jl >> 2) (the 16-key step u
+  // and the second row group add constants)
+  uint32_t vtr[2][DT];
+  {
+    const int g16 = lane >> 4, jl = lane & 15;
+    const int r0 = 32 * g + 4 * h2 + (jl >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
+      const int c = d >> 3, off = d & 7;
+      const uint32_t e = (uint32_t)((r0 * D + v_swz<CPR>(r0, c) * 8 + off) * 2);
+      vtr[0][dt] = kv_lds + (uint32_t)(2 * TILE) + e;
+      vtr[1][dt] = kv_lds + (uint32_t)(4 * TILE + 2 * TILE) + e;
+    }
+  }
   uint32_t koff[LPT], voff[LPT];
 #pragma unroll
   for (int k = 0; k < LPT; ++k) {
@@ -902,19 +918,19 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 
     // ---- O^T (D x 32 queries) += V_g^T P^T ----
     {
-      const int g16 = lane >> 4, jl = lane & 15;
+      uint32_t vbase[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vbase[dt] = cur ? vtr[1][dt] : vtr[0][dt];
       constexpr int NP = 2 * DT;
       bf16x8 va[NP];
 #pragma unroll
       for (int x = 0; x < NP + PF; ++x) {
         if (x < NP) {
           const int u = x / DT, dt = x % DT;
-          const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
-          const int c = d >> 3, off = d & 7;
-          const int r0 = 32 * g + 16 * u + 4 * h2 + (jl >> 2);
-          const int r1 = r0 + 8;
-          const bf16x4 lo = lds_read_tr16(Vc + r0 * D + v_swz<CPR>(r0, c) * 8 + off);
-          const bf16x4 hi = lds_read_tr16(Vc + r1 * D + v_swz<CPR>(r1, c) * 8 + off);
+          // rows r0 + 16u and r0 + 16u + 8 keep r0's swizzle (same row % 4)
+          const uint32_t a = vbase[dt] + (uint32_t)(16 * u * D * 2);
+          const bf16x4 lo = lds_read_tr16_at(a);
+          const bf16x4 hi = lds_read_tr16_at(a + (uint32_t)(8 * D * 2));
           va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }

@@ -44,6 +44,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(BSA_LDS(s16x4, p));
   return __builtin_bit_cast(bf16x4, v);
 }
+// The same read at a byte offset from the start of LDS.
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(uint32_t byte_off) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)byte_off);
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 // Asynchronous 16-byte global -> LDS copy.  Every lane supplies its own global
 // address; the wave writes 64 consecutive 16-byte slots starting at `lds`

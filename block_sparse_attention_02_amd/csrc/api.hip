@@ -369,6 +369,13 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block capacity M must be 16, 32 or 64");
     if ((int64_t)a->dq.B * a->dq.H * a->J >= (int64_t)1 << 31)
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks");
+    if (a->dt == BSA_BF16) {  // the kernels address one (batch, head) K/V slice with 32-bit offsets
+      const int64_t slice = (a->dkv.N - 1) * a->dkv.sN * 2 + a->dkv.D * 2;
+      if (slice >= (int64_t)1 << 32 || a->dkv.N >= (int64_t)1 << 24 || a->dkv.sN * 2 >= (int64_t)1 << 24)
+        return fail(BSA_ERR_UNSUPPORTED,
+                    "bsa_forward_qouter: block mode needs N < 2^24, a token stride below 2^24 bytes and one "
+                    "(batch, head) K/V slice below 4 GiB");
+    }
     if (a->k_sum || a->v_sum || a->b_sum) {
       if (!a->k_sum || !a->v_sum || !a->b_sum)
         return fail(BSA_ERR_ARG, "bsa_forward_qouter: k_sum, v_sum and b_sum go together");

@@ -139,7 +139,8 @@ __device__ __forceinline__ void stage_ids(i32x4 prs, int j, int M, uint32_t ids_
       : "memory");
 }
 
-// Byte offsets (within the slice) of the LPT tile rows this lane copies.  Copy
+// Byte offsets (within the slice) of the LPT tile rows this lane copies (token
+// ids and the row stride are below 2^24, so a 24-bit multiply is exact).  Copy
 // k of wave w fills LDS row 32w + RPI*k + sub (sub = lane / CPR) with key
 // 32w + LPT*sub + k of the block, so a lane's keys are LPT consecutive entries
 // of the id buffer.  Padding ids (-1) read token 0; their keys are masked.
@@ -151,7 +152,7 @@ __device__ __forceinline__ void tile_rows(uint32_t* rowoff, const int* ids, int 
   for (int q = 0; q < TM::LPT / 4; ++q) {
     const i32x4 v = *reinterpret_cast<const i32x4*>(src + 4 * q);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rowoff[4 * q + e] = (uint32_t)max(v[e], 0) * row_bytes;
+    for (int e = 0; e < 4; ++e) rowoff[4 * q + e] = __umul24((uint32_t)max(v[e], 0), row_bytes);
   }
 }
 
@@ -637,12 +638,12 @@ __device__ __forceinline__ void tile_rows4(uint32_t* rowoff, const int* ids, int
   if constexpr (TM::LPT == 4) {
     const i32x4 v = *reinterpret_cast<const i32x4*>(src);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rowoff[e] = (uint32_t)max(v[e], 0) * row_bytes;
+    for (int e = 0; e < 4; ++e) rowoff[e] = __umul24((uint32_t)max(v[e], 0), row_bytes);
   } else {
     typedef int i32x2 __attribute__((ext_vector_type(2)));
     const i32x2 v = *reinterpret_cast<const i32x2*>(src);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) rowoff[e] = (uint32_t)max(v[e], 0) * row_bytes;
+    for (int e = 0; e < 2; ++e) rowoff[e] = __umul24((uint32_t)max(v[e], 0), row_bytes);
   }
 }
 

@@ -258,7 +258,10 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
  * products, fp32 accumulation and softmax, bf16 output); dt = F32 (block mode
  * only) is computed entirely in fp32 on the vector ALUs and meant for small
  * problems.  VSA block capacity M in {16, 32, 64}; NSA (bf16 only) block size
- * BS in {32, 64, 128}, S <= 64.
+ * BS in {32, 64, 128}, S <= 64.  Block mode in bf16 addresses one (batch,
+ * head) K/V slice with 32-bit byte offsets: it needs N < 2^24, a token stride
+ * (dkv.sN) below 2^23 elements and (N - 1) * dkv.sN + D below 2^31 elements;
+ * anything larger returns BSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* q;

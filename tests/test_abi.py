@@ -123,6 +123,25 @@ def test_qouter_shape_checks():
     assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_SHAPE         # stride % 8
 
 
+def test_qouter_32bit_slice_limits():
+    """Block mode addresses one (batch, head) K/V slice with 32-bit offsets: a
+    slice of 4 GiB or more, N >= 2^24 or a token stride of 2^24 bytes is
+    rejected on the host (no launch)."""
+    lib = L.load()
+    H, D = 24, 128
+    big = 1 << 20  # 2^20 tokens x 24 heads x 128 x 2 bytes = 6 GiB slice span
+    d = L.TDesc(1, big, H, D, big * H * D, H * D, D)
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    d = L.TDesc(1, 1 << 24, 1, 64, (1 << 24) * 64, 64, 64)  # 2 GiB slice, but N = 2^24
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    d = L.TDesc(1, 64, 1, 128, 64 * (1 << 23), 1 << 23, 128)  # token stride 2^24 bytes
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    # a 384 MiB slice span passes, and the call stops at the summaries check that follows
+    ok = L.TDesc(1, 1 << 16, H, D, (1 << 16) * H * D, H * D, D)
+    a = _qouter_args(dq=ok, dkv=ok, dout=ok, k_sum=ctypes.c_void_p(256))
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_ARG
+
+
 H3_CASES = [
     ([130, (2, 16, 16), 60, 200, (4, 16, 16)], (2, 8, 8)),   # the page's metadata example
     ([5, (3, 5, 6), 9, (2, 3, 3), 1, (5, 4, 2)], (2, 2, 2)),

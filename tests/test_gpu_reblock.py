@@ -37,6 +37,7 @@ CFGS = {
     "ragged_d64": (scaled("video", grid=(7, 9, 13), h=2, D=64), 64),      # 819 tokens: a 51-token last leaf
     "m32": (scaled("video", grid=(6, 12, 20), h=2), 32),
     "root_7400_d64": (scaled("video", grid=(8, 25, 37), h=1, D=64), 64),  # a root above 4096 tokens: the 8192-capacity level
+    "m16_d64": (scaled("video", grid=(5, 8, 13), h=2, D=64), 16),         # 520 tokens in 33 leaves of 16 (the last short)
 }
 
 

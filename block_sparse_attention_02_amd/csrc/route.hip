@@ -58,23 +58,28 @@ hipError_t launch_tile_index(int T, int H, int W, int bT, int bH, int bW, int J,
 // loads of an iteration are all in flight together.
 // ============================================================================
 template <typename T, int VW, int CPT>
-__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p, int nsplit) {
   constexpr int UT = (CPT <= 2) ? 8 : 4;  // tokens per iteration
   using Vec = typename std::conditional<VW == 1, T, u32x4>::type;
-  const T* __restrict__ x = reinterpret_cast<const T*>(blockIdx.z ? p.k : p.q);
-  float* __restrict__ out = blockIdx.z ? p.kbar : p.qbar;
+  // blockIdx.z = tensor * nsplit + part: part takes a contiguous share of the
+  // (head, chunk) range, so small grids still fill the chip
+  const int tsel = blockIdx.z / nsplit, part = blockIdx.z % nsplit;
+  const T* __restrict__ x = reinterpret_cast<const T*>(tsel ? p.k : p.q);
+  float* __restrict__ out = tsel ? p.kbar : p.qbar;
   const int i = blockIdx.x, b = blockIdx.y;
   const int n = p.block_len[i];
   const int cpr = p.D / VW;  // vector chunks per head row
   const int nch = p.H * cpr;
+  const int cw = (nch + nsplit - 1) / nsplit;
+  const int cbeg = part * cw, cend = min(nch, cbeg + cw);
   const T* __restrict__ xb = x + (int64_t)b * p.sB;
-  for (int c0 = 0; c0 < nch; c0 += 256 * CPT) {
+  for (int c0 = cbeg; c0 < cend; c0 += 256 * CPT) {
     float acc[CPT][VW];
     int64_t off[CPT];
     const int32_t* members[CPT];  // the block's members in this chunk's head (per-head tables)
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = min(c0 + (int)threadIdx.x + 256 * u, nch - 1);
+      const int c = min(c0 + (int)threadIdx.x + 256 * u, cend - 1);
       off[u] = (int64_t)(c / cpr) * p.sH + (int64_t)(c % cpr) * VW;
       members[u] = p.perm + ((int64_t)b * p.H + c / cpr) * p.perm_bh_stride + (int64_t)i * p.M;
 #pragma unroll
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = c0 + threadIdx.x + 256 * u;
-      if (c < nch) {
+      if (c < cend) {
         const int hh = c / cpr, dc = c % cpr;
         float* dst = out + (((int64_t)b * p.H + hh) * p.J + i) * p.D + dc * VW;
 #pragma unroll
@@ -122,16 +127,18 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 template <typename T, int VW>
 static hipError_t launch_pool_t(const PoolParams& p, int ntensors, hipStream_t s) {
   const int nch = p.H * (p.D / VW);
-  const int cpt = (nch + 255) / 256;
-  dim3 grid(p.J, p.B, ntensors);
+  // below ~4096 workgroups each block's (head, chunk) range is shared by two
+  const int nsplit = ((int64_t)p.J * p.B * ntensors < 4096 && nch > 256) ? 2 : 1;
+  const int cpt = ((nch + nsplit - 1) / nsplit + 255) / 256;
+  dim3 grid(p.J, p.B, ntensors * nsplit);
   if (cpt <= 1)
-    pool_kernel<T, VW, 1><<<grid, 256, 0, s>>>(p);
+    pool_kernel<T, VW, 1><<<grid, 256, 0, s>>>(p, nsplit);
   else if (cpt <= 2)
-    pool_kernel<T, VW, 2><<<grid, 256, 0, s>>>(p);
+    pool_kernel<T, VW, 2><<<grid, 256, 0, s>>>(p, nsplit);
   else if (cpt <= 3)
-    pool_kernel<T, VW, 3><<<grid, 256, 0, s>>>(p);
+    pool_kernel<T, VW, 3><<<grid, 256, 0, s>>>(p, nsplit);
   else
-    pool_kernel<T, VW, 4><<<grid, 256, 0, s>>>(p);
+    pool_kernel<T, VW, 4><<<grid, 256, 0, s>>>(p, nsplit);
   return hipGetLastError();
 }
 

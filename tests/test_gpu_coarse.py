@@ -54,6 +54,7 @@ COARSE_CFGS = {
     "two_col_steps": scaled("video", grid=(8, 24, 28), h=2, R=6),   # J = 84: 64 + a ragged 20
     "ragged_blocks": scaled("video", grid=(6, 22, 30), h=2, R=9),   # partial blocks on every axis
     "d64_odd": scaled("video", grid=(9, 12, 20), h=3, D=64, R=5),
+    "odd_two_chunks": scaled("video", grid=(12, 20, 28), h=2, R=7),  # J = 105: unaligned rows, 64 + 41 columns
 }
 
 

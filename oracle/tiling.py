@@ -6,7 +6,7 @@ ceilings, true lengths of edge blocks), section 3 (pack: members of a block
 become contiguous; outputs go back through the inverse map; padding outputs
 are dropped) and section 2.2 (the keep budget R_r).
 
-Readings where the page is silent (listed in the design doc as well):
+Readings where the page is silent:
 * members inside a block are listed with t slowest and x fastest, the same
   flattening the page uses for whole tokens; the block id has its x-block index
   fastest (blocks A, B, C, D = top-left, top-right, bottom-left, bottom-right);

@@ -947,7 +947,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention shards by heads with no exchange, "
-              "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+              "so one MI355X runs one shard's kernels at their real shape; use --gpus 1", file=sys.stderr)
         return 2
     if args.copy_calibration:
         import torch

@@ -238,3 +238,16 @@ def test_video_full_size_sampled():
     got = to64(out[:, :, heads])
     mask = ~np.isnan(ref)
     assert_attn_close(got[mask], ref[mask], "video full size, sampled blocks with the coarse branch")
+
+
+def test_coarse_is_deterministic():
+    """Two launches on the same scores give the same C bit for bit."""
+    cfg = COARSE_CFGS["odd_two_chunks"]
+    geom, tab, x = _setup(cfg)
+    J = geom.J
+    Q, K = to64(x["q"]), to64(x["k"])
+    E = torch.from_numpy(_oracle_scores(Q, K, tab).astype(np.float32)).to(DEV).contiguous()
+    C1 = bsa.coarse_attention(x["v"], geom.perm, geom.block_len, J, geom.M, E)
+    C2 = bsa.coarse_attention(x["v"], geom.perm, geom.block_len, J, geom.M, E)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)

@@ -140,3 +140,14 @@ def test_reblock_video_full_size():
     assert torch.equal(srt, torch.arange(N, device=DEV).expand(H, N))
     for hh in (0, 13):
         _check_head(x, 64, hh, levels, dirs, features, moment, factor, "video full size")
+
+
+def test_reblock_is_deterministic():
+    """Two runs on the same inputs give the same tables bit for bit (no
+    floating-point atomics: fixed reduction orders, stable sorts)."""
+    cfg, M = CFGS["root_7400_d64"]
+    x = vsa_inputs(cfg, device=DEV)
+    p1, l1 = bsa.spark_reblock(x["q"], x["k"], M=M)
+    p2, l2 = bsa.spark_reblock(x["q"], x["k"], M=M)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(l1, l2)

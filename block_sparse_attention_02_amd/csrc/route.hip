@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p, int nsplit) {
 template <typename T, int VW>
 static hipError_t launch_pool_t(const PoolParams& p, int ntensors, hipStream_t s) {
   const int nch = p.H * (p.D / VW);
-  // below ~4096 workgroups each block's (head, chunk) range is shared by two
-  const int nsplit = ((int64_t)p.J * p.B * ntensors < 4096 && nch > 256) ? 2 : 1;
+  // below 8192 workgroups each block's (head, chunk) range is shared by two
+  const int nsplit = ((int64_t)p.J * p.B * ntensors < 8192 && nch > 256) ? 2 : 1;
   const int cpt = ((nch + nsplit - 1) / nsplit + 255) / 256;
   dim3 grid(p.J, p.B, ntensors * nsplit);
   if (cpt <= 1)

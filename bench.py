@@ -121,8 +121,10 @@ def bench_video(args):
     qa.q2k_idx, qa.q2k_num, qa.kmax = bsa.api._ptr(q2k_idx), bsa.api._ptr(q2k_num), R
     qa.item_order = bsa.api._ptr(order)
 
+    qws = bsa.qouter_workspace(dev)
+
     def attend():
-        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), bsa.api._ptr(qws), qws.numel(), s_ptr))
 
     ev = {n: [_events() for _ in range(args.steps)] for n in ("tile", "route", "attn")}
 
@@ -240,8 +242,10 @@ def bench_reweight(args):
     qa.item_order = P(order)
     qa.k_sum, qa.v_sum, qa.b_sum = P(k_sum), P(v_sum), P(b_sum)
 
+    qws = bsa.qouter_workspace(dev)
+
     def attend():
-        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), bsa.api._ptr(qws), qws.numel(), s_ptr))
 
     stages = (("tile", tile), ("route", route), ("summaries", summarise), ("attn", attend))
     ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
@@ -394,8 +398,10 @@ def bench_coarse(args):
     qa.item_order = P(order)
     qa.coarse, qa.gate = P(C), P(gate)
 
+    qws = bsa.qouter_workspace(dev)
+
     def attend():
-        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), bsa.api._ptr(qws), qws.numel(), s_ptr))
 
     stages = (("tile", tile), ("route", route), ("coarse", coarse), ("attn", attend))
     ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
@@ -545,8 +551,10 @@ def bench_h3(args):
     qa.q2k_idx, qa.q2k_num, qa.kmax = Pp(q2k_idx), Pp(q2k_num), J
     qa.item_order = Pp(order)
 
+    qws = bsa.qouter_workspace(dev)
+
     def attend():
-        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), bsa.api._ptr(qws), qws.numel(), s_ptr))
 
     stages = (("tile", tile), ("route", route), ("attn", attend))
     ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}
@@ -699,8 +707,10 @@ def bench_reblock(args):
     qa.item_order = P(order)
     qa.perm_bh_stride = J * M
 
+    qws = bsa.qouter_workspace(dev)
+
     def attend():
-        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), s_ptr))
+        L.check(lib.bsa_forward_qouter(ctypes.byref(qa), bsa.api._ptr(qws), qws.numel(), s_ptr))
 
     stages = (("reblock", reblock), ("route", route), ("attn", attend))
     ev = {n: [_events() for _ in range(args.steps)] for n, _ in stages}

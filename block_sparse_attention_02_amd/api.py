@@ -17,7 +17,15 @@ __all__ = [
     "tile_dims", "tile_index", "keep_budget", "pool_route_topk", "route_workspace_bytes",
     "attention_vsa", "attention_nsa", "coarse_attention", "spark_summaries", "H3Geometry",
     "h3_pool_route_topk", "h3_forward", "spark_reblock", "reblock_forward", "kvouter", "combine", "VsaGeometry", "vsa_forward",
+    "qouter_workspace", "check",
 ]
+
+
+def check(device=None):
+    """bsa_check on the current stream of ``device``: synchronises, then raises
+    BsaError (BSA_ERR_INDEX) if a kernel met a block id that names no block."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    L.check(_lib().bsa_check(_stream(dev)))
 
 
 def _lib():
@@ -152,6 +160,32 @@ def _qouter_args(q, k, v, out, scale, mode, lse):
                         dout=_desc(out), dt=_dtype(q), scale=scale, mode=mode, lse=_ptr(lse))
 
 
+def _forward_qouter(a, device, workspace):
+    """bsa_forward_qouter with the caller's workspace (allocated when None or
+    too small; the library itself never allocates)."""
+    lib = _lib()
+    n = ctypes.c_size_t()
+    L.check(lib.bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)))
+    if n.value and (workspace is None or workspace.numel() < n.value):
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=device)
+    L.check(lib.bsa_forward_qouter(ctypes.byref(a), _ptr(workspace if n.value else None), n.value,
+                                   _stream(device)))
+
+
+def qouter_workspace(device="cuda"):
+    """A workspace for attention_vsa / attention_nsa that can be reused by
+    every call ordered on one stream (its size does not depend on shapes)."""
+    a = L.QOuterArgs()
+    n = ctypes.c_size_t()
+    # the size only depends on the mode and dtype: query a bf16 block-mode call
+    ph = ctypes.c_void_p(256)
+    a.q = a.k = a.v = a.out = a.perm = a.block_len = a.q2k_idx = a.q2k_num = ph
+    a.dq = a.dkv = a.dout = L.TDesc(1, 64, 1, 64, 64 * 64, 64, 64)
+    a.dt, a.scale, a.mode, a.J, a.M, a.kmax = L.BSA_BF16, 1.0, L.BSA_SEL_BLOCK, 1, 64, 1
+    L.check(_lib().bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)))
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=device)
+
+
 def coarse_attention(v, perm, block_len, J, M, E, need_vbar=False, out=None):
     """Coarse pooled-V branch: C [B, H, J, D] fp32 = softmax(E) V_bar, with
     V_bar the per-block means of v [B, N, H, D] (bf16 or float32) and E the
@@ -207,14 +241,16 @@ def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, nee
 
 
 def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
-                  item_order=None, summaries=None, coarse=None, perm_bh_stride=0):
+                  item_order=None, summaries=None, coarse=None, perm_bh_stride=0, workspace=None):
     """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
     ``item_order``: optional processing order (from pool_route_topk).
     ``summaries``: optional (k_sum, v_sum, b_sum) from spark_summaries; every
     block a query block does not keep then enters through its virtual token.
     ``coarse``: optional (C, gate) -- C fp32 [B,H,J,D] from coarse_attention,
     gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added.
-    ``perm_bh_stride``: per-(b, h) tables in ``perm`` (as in pool_route_topk)."""
+    ``perm_bh_stride``: per-(b, h) tables in ``perm`` (as in pool_route_topk).
+    ``workspace``: optional uint8 device tensor from qouter_workspace (calls
+    that share one must be ordered on one stream)."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -246,7 +282,7 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
                 or gate.numel() != H * D or not (C.is_contiguous() and gate.is_contiguous())):
             raise ValueError("coarse must be a contiguous float32 C [B,H,J,D] and gate [H,D]")
         a.coarse, a.gate = _ptr(C), _ptr(gate)
-    L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
+    _forward_qouter(a, q.device, workspace)
     return (out, lse) if need_lse else out
 
 
@@ -263,7 +299,7 @@ def attention_nsa(q, k, v, block_indices, block_counts, block_size, causal=True,
     a = _qouter_args(q, k, v, out, scale, L.BSA_SEL_TOKEN, lse)
     a.blk_idx, a.blk_cnt = _ptr(block_indices), _ptr(block_counts)
     a.S, a.BS, a.causal = block_indices.shape[-1], int(block_size), int(bool(causal))
-    L.check(_lib().bsa_forward_qouter(ctypes.byref(a), _stream(q.device)))
+    _forward_qouter(a, q.device, None)
     return (out, lse) if need_lse else out
 
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "bsa.h"
@@ -49,6 +50,33 @@ bsa_status check_desc(const bsa_tdesc& d, const char* name, int vec, bool need_v
 
 int elem_bytes(bsa_dtype dt) { return dt == BSA_F32 ? 4 : 2; }
 
+// Sticky index-error flag, one per device: kernels that meet a block id
+// outside their table skip it and set the flag; bsa_check reads and clears it.
+// Host code reaches each device's copy only through the address that
+// hipGetSymbolAddress returns for that device.
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+uint32_t* g_err_flag[kMaxDevices] = {nullptr};
+
+}  // namespace
+
+static __device__ uint32_t index_error_flag;
+
+namespace {
+
+// The current device's flag (nullptr if the device cannot be queried).
+uint32_t* device_error_flag() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (!g_err_flag[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(index_error_flag)) != hipSuccess) return nullptr;
+    g_err_flag[dev] = static_cast<uint32_t*>(ptr);
+  }
+  return g_err_flag[dev];
+}
+
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -62,7 +90,18 @@ const char* bsa_version(void) { return "libbsa 0.1 (gfx950)"; }
 bsa_status bsa_check(void* stream) {
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "stream synchronize");
-  return hip_status(hipGetLastError(), "asynchronous error");
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_status(e, "asynchronous error");
+  uint32_t* flag = device_error_flag();
+  if (!flag) return fail(BSA_ERR_HIP, "bsa_check: the device's index-error flag is not reachable");
+  uint32_t v = 0;
+  e = hipMemcpy(&v, flag, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(e, "index-error flag read");
+  if (v == 0) return ok();
+  const uint32_t zero = 0;
+  e = hipMemcpy(flag, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e, "index-error flag clear");
+  return fail(BSA_ERR_INDEX, "a kernel met a block id at or beyond the number of blocks; the entry was skipped");
 }
 
 // ---------------------------------------------------------------------------- tiling
@@ -355,11 +394,10 @@ static bsa_status check_attn_common(const bsa_qouter_args* a) {
   return BSA_OK;
 }
 
-bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
+// Every host-side check of a query-outer call (common and per mode).
+static bsa_status check_qouter(const bsa_qouter_args* a) {
   bsa_status st = check_attn_common(a);
   if (st != BSA_OK) return st;
-  const float scale_log2 = a->scale * 1.4426950408889634f;
-  hipStream_t s = (hipStream_t)stream;
   if (a->mode == BSA_SEL_BLOCK) {
     if (a->dq.H != a->dkv.H) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block mode needs Hq == Hkv");
     if (!a->perm || !a->block_len || !a->q2k_idx || !a->q2k_num)
@@ -394,14 +432,7 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
       if (!aligned16(a->coarse) || !aligned16(a->gate))
         return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: coarse and gate must be 16-byte aligned");
     }
-    bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
-                         a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
-                         a->dout.sB, a->dout.sN, a->dout.sH,
-                         a->perm, a->block_len, a->q2k_idx, a->q2k_num,
-                         (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
-                         scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum,
-                         a->coarse, a->gate, a->perm_bh_stride};
-    return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
+    return BSA_OK;
   }
   if (a->mode == BSA_SEL_TOKEN) {
     if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: token mode needs bf16");
@@ -412,15 +443,58 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream) {
     const int64_t G = a->dq.H / a->dkv.H;
     const int64_t items = a->dq.B * a->dq.N * a->dkv.H * ((G + 15) / 16);
     if (items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many tokens");
-    bsa::NsaAttnParams p{a->q, a->k, a->v, a->out,
-                         a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
-                         a->dout.sB, a->dout.sN, a->dout.sH,
-                         a->blk_idx, a->blk_cnt,
-                         (int)a->dq.B, (int)a->dq.H, (int)a->dkv.H, a->S, a->BS, a->causal ? 1 : 0,
-                         (int)a->dq.D, a->dq.N, scale_log2, a->lse};
-    return hip_status(bsa::launch_nsa_attention(p, false, s), "nsa attention launch");
+    return BSA_OK;
   }
   return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
+}
+
+// Workspace of bsa_forward_qouter: the scheduler state of the block-mode
+// persistent grid (bf16); none for the fp32 and token modes.
+static size_t qouter_ws_need(const bsa_qouter_args* a) {
+  return (a->mode == BSA_SEL_BLOCK && a->dt == BSA_BF16) ? bsa::qouter_sched_bytes() : 0;
+}
+
+// Launches a validated call with `sched` as the scheduler state (nullptr when
+// the mode needs none).
+static bsa_status launch_qouter(const bsa_qouter_args* a, void* sched, void* stream) {
+  const float scale_log2 = a->scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->mode == BSA_SEL_BLOCK) {
+    bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
+                         a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
+                         a->dout.sB, a->dout.sN, a->dout.sH,
+                         a->perm, a->block_len, a->q2k_idx, a->q2k_num,
+                         (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
+                         scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum,
+                         a->coarse, a->gate, a->perm_bh_stride, sched, device_error_flag()};
+    return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
+  }
+  bsa::NsaAttnParams p{a->q, a->k, a->v, a->out,
+                       a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,
+                       a->dout.sB, a->dout.sN, a->dout.sH,
+                       a->blk_idx, a->blk_cnt,
+                       (int)a->dq.B, (int)a->dq.H, (int)a->dkv.H, a->S, a->BS, a->causal ? 1 : 0,
+                       (int)a->dq.D, a->dq.N, scale_log2, a->lse, device_error_flag()};
+  return hip_status(bsa::launch_nsa_attention(p, false, s), "nsa attention launch");
+}
+
+bsa_status bsa_qouter_ws(const bsa_qouter_args* a, size_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_ARG, "bsa_qouter_ws: null output");
+  bsa_status st = check_qouter(a);
+  if (st != BSA_OK) return st;
+  *bytes = qouter_ws_need(a);
+  return ok();
+}
+
+bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* ws, size_t ws_bytes, void* stream) {
+  bsa_status st = check_qouter(a);
+  if (st != BSA_OK) return st;
+  const size_t need = qouter_ws_need(a);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "bsa_forward_qouter: workspace of %zu bytes required", need);
+  if (need && (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(BSA_ERR_WORKSPACE, "bsa_forward_qouter: workspace must be 256-byte aligned");
+  return launch_qouter(a, need ? ws : nullptr, stream);
 }
 
 // ------------------------------------------------------------------ coarse branch
@@ -657,7 +731,7 @@ static bsa_status check_kvouter(const bsa_kvouter_args* a, bsa::KvOuterParams* o
                             a->q2k, a->q2k_cnt, (int)a->dq.B, (int)a->dq.H, (int)a->dkv.H, a->k_sel, a->BK,
                             (int)a->dq.D, a->causal ? 1 : 0, a->chunk_cap, a->dq.N,
                             a->scale * 1.4426950408889634f, reinterpret_cast<__bf16*>(a->o_buf), a->lse_buf,
-                            a->nslot};
+                            a->nslot, device_error_flag()};
   return BSA_OK;
 }
 

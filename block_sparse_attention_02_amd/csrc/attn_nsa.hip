@@ -85,6 +85,10 @@ __global__ __launch_bounds__(64) void nsa_attn_kernel(NsaAttnParams p) {
     const int blk = sel[pp];
     if (blk < 0) continue;
     const int64_t k0 = (int64_t)blk * p.BS;
+    if (k0 >= p.N) {  // not a block of the sequence: skipped and reported
+      flag_index_error(p.err);
+      continue;
+    }
     if (k0 > last) continue;  // the whole block is masked
     for (int c0 = 0; c0 < p.BS; c0 += KC) {
       const int64_t base = k0 + c0;

@@ -62,6 +62,17 @@ __device__ __forceinline__ int item_block(const VsaAttnParams& p, int64_t wid) {
   return (i >= 0 && i < p.J) ? i : -1;
 }
 
+// Kept entry `pos` of a query block's list: the block id, or -1 when the
+// entry names no block.  An id at or beyond J is skipped like a negative one;
+// `bad` records it, and the item reports it through the device's index-error
+// flag when it ends.
+template <typename T>
+__device__ __forceinline__ int kept_id(T sel, int pos, int J, bool& bad) {
+  const int j = sel[pos];
+  bad |= j >= J;
+  return j < J ? j : -1;
+}
+
 // Physical 16-byte chunk of logical chunk c in K tile row r: 16 consecutive
 // rows read at the same logical chunk land on 16 distinct bank groups.
 template <int CPR>
@@ -247,14 +258,15 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
   const uint32_t ids_lds = lds_offset(ids);
   uint32_t rows[LPT];
   int nj = 0, njn = 0, jn1 = 0;
+  bool bad = false;  // a kept id at or beyond J was met
   if (num > 0) {
-    const int j0 = sel[0];
+    const int j0 = kept_id(sel, 0, p.J, bad);
     nj = (j0 >= 0) ? blen[j0] : 0;
     stage_ids(prs, max(j0, 0), M, ids_lds, lane);
     wait_vmcnt<0>();
     tile_rows<D, MT>(rows, ids, w, lane, row_bytes);
     stage_tile<D, MT>(krs, ks_lds, rows, koff, w);
-    jn1 = sel[min(1, num - 1)];
+    jn1 = kept_id(sel, min(1, num - 1), p.J, bad);
     stage_ids(prs, max(jn1, 0), M, ids_lds, lane);
     stage_tile<D, MT>(vrs, vs_lds, rows, voff, w);
   }
@@ -304,7 +316,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
     // after next (the last one again near the end, a harmless repeat) and the
     // true length of the next block.
     __builtin_amdgcn_sched_barrier(0);
-    const int jn2 = sel[min(pc + 2, num - 1)];
+    const int jn2 = kept_id(sel, min(pc + 2, num - 1), p.J, bad);
     njn = (jn1 >= 0) ? blen[max(jn1, 0)] : 0;
     __builtin_amdgcn_sched_barrier(0);
 
@@ -401,6 +413,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
     jn1 = jn2;
   }
 
+  if (bad) flag_index_error(p.err);
   // ---- epilogue: O = U / l, written at the tokens' original positions ----
   const float l_tot = l_run + xor32(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
@@ -429,20 +442,18 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
 // narrow window of each head's K/V, which stays in L2 (workgroups are spread
 // over the XCDs round-robin, so each XCD serves every 8th query block of the
 // same stretch and all eight share the same window in the last-level cache).
-// Round counters of the persistent grid (one per round of gridDim.x items,
-// cleared before each launch).
-static __device__ uint32_t g_round_ctr[kMaxRounds];
-
+//
+// All scheduling state lives in the caller's workspace (one SchedState per
+// launch, cleared by clear_sched_kernel on the launch's stream), so launches
+// on different streams never share counters.
+//
 // Progress balancing between the two workgroups that share a CU.  The wave
 // arbiter favours the older workgroup (by ~18 % here), which would leave the
 // younger one behind at every round boundary; instead each workgroup publishes
 // how many tiles it has finished and raises its waves' priority while it
 // trails its partner.  Slots are found from the hardware CU id, registered
 // once per launch.
-constexpr int kCuKeys = 2048;  // 8 XCDs x 8 SEs x 2 SHs x 16 CUs
-static __device__ uint32_t g_cu_slots[kCuKeys];
-static __device__ uint32_t g_cu_progress[kCuKeys * 2];
-
+//
 // Work distribution of the four-wave kernel's persistent grid.  Work items
 // (in processing order) are cut into chunks of kChunk; chunk c belongs to XCD
 // c % kXcds (found from the hardware XCC id), whose workgroups take its items
@@ -453,27 +464,28 @@ static __device__ uint32_t g_cu_progress[kCuKeys * 2];
 // which then stays in that XCD's L2.  Correctness depends only on the
 // per-XCD atomic counters: each item is taken exactly once, whatever the waits
 // do.
+constexpr int kCuKeys = 2048;  // 8 XCDs x 8 SEs x 2 SHs x 16 CUs
 constexpr int kXcds = 8;
 constexpr int kChunk = 64;  // items per chunk; chunk c belongs to XCD c % kXcds
-static __device__ uint32_t g_xq[kXcds];  // items taken from each XCD's chunks
-static __device__ uint32_t g_registered;
-static __device__ uint32_t g_xcd_members[kXcds];
-static __device__ uint32_t g_xcd_exited[kXcds];
-static __device__ uint32_t g_xcd_rounds[kXcds * kMaxRounds];
 
-// Clears the scheduling state before a launch (grid-stride over all tables).
-__global__ void clear_rounds_kernel(int n) {
-  const int tid = blockIdx.x * blockDim.x + threadIdx.x, nt = gridDim.x * blockDim.x;
-  for (int r = tid; r < n; r += nt) g_round_ctr[r] = 0u;
-  for (int r = tid; r < kCuKeys; r += nt) g_cu_slots[r] = 0u;
-  for (int r = tid; r < 2 * kCuKeys; r += nt) g_cu_progress[r] = 0u;
-  for (int r = tid; r < kXcds * kMaxRounds; r += nt) g_xcd_rounds[r] = 0u;
-  if (tid < kXcds) {
-    g_xcd_members[tid] = 0u;
-    g_xcd_exited[tid] = 0u;
-  }
-  if (tid < kXcds) g_xq[tid] = 0u;
-  if (tid == 0) g_registered = 0u;
+struct SchedState {
+  uint32_t xq[kXcds];                      // items taken from each XCD's chunks
+  uint32_t registered;                     // workgroups that joined their cohort
+  uint32_t xcd_members[kXcds];
+  uint32_t xcd_exited[kXcds];
+  uint32_t round_ctr[kMaxRounds];          // two-wave kernel: arrivals per round
+  uint32_t cu_slots[kCuKeys];              // workgroups registered per CU
+  uint32_t cu_progress[kCuKeys * 2];       // finished tiles per (CU, slot)
+  uint32_t xcd_rounds[kXcds * kMaxRounds]; // four-wave kernel: arrivals per (XCD, item)
+};
+
+size_t qouter_sched_bytes() { return (sizeof(SchedState) + 255) & ~(size_t)255; }
+
+// Clears the scheduling state before a launch (grid-stride over every word).
+__global__ void clear_sched_kernel(SchedState* st) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(st);
+  constexpr int n = (int)(sizeof(SchedState) / 4);
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n; r += gridDim.x * blockDim.x) w[r] = 0u;
 }
 
 __device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
@@ -487,17 +499,17 @@ struct Cohort {
 
 // Join this XCD's cohort; waits (bounded) until every workgroup of the grid
 // has joined so the member count is final.
-__device__ __forceinline__ Cohort cohort_register(uint32_t* sh) {
+__device__ __forceinline__ Cohort cohort_register(SchedState* st, uint32_t* sh) {
   if (threadIdx.x == 0) {
     const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1);  // XCC_ID
-    __hip_atomic_fetch_add(&g_xcd_members[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&g_registered, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&st->xcd_members[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&st->registered, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int t = 0; t < 4096; ++t) {
-      if (load_relaxed(&g_registered) >= gridDim.x) break;
+      if (load_relaxed(&st->registered) >= gridDim.x) break;
       __builtin_amdgcn_s_sleep(8);
     }
     sh[0] = xcc;
-    sh[1] = load_relaxed(&g_xcd_members[xcc]);
+    sh[1] = load_relaxed(&st->xcd_members[xcc]);
   }
   __syncthreads();
   Cohort c;
@@ -509,12 +521,12 @@ __device__ __forceinline__ Cohort cohort_register(uint32_t* sh) {
 
 // Arrive after a query block and wait (bounded) for the cohort's other
 // members, counting those that have already run out of work.
-__device__ __forceinline__ void cohort_sync(Cohort& c) {
+__device__ __forceinline__ void cohort_sync(SchedState* st, Cohort& c) {
   if (threadIdx.x == 0 && c.round < kMaxRounds) {
-    uint32_t* ctr = &g_xcd_rounds[c.xcc * kMaxRounds + c.round];
+    uint32_t* ctr = &st->xcd_rounds[c.xcc * kMaxRounds + c.round];
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int t = 0; t < 4096; ++t) {
-      if (load_relaxed(ctr) + load_relaxed(&g_xcd_exited[c.xcc]) >= c.members) break;
+      if (load_relaxed(ctr) + load_relaxed(&st->xcd_exited[c.xcc]) >= c.members) break;
       __builtin_amdgcn_s_sleep(8);
     }
   }
@@ -532,13 +544,13 @@ __device__ __forceinline__ int xcd_item(uint32_t x, uint32_t k, int items) {
 // The next work item for a workgroup of XCD x: from its own chunks in order,
 // then from the other XCDs' chunks; -1 when everything is taken.  Every item
 // is handed out exactly once (one atomic counter per XCD).
-__device__ __forceinline__ int next_item(uint32_t x, int items, uint32_t* sh) {
+__device__ __forceinline__ int next_item(SchedState* st, uint32_t x, int items, uint32_t* sh) {
   if (threadIdx.x == 0) {
     int it = -1;
     for (uint32_t y = 0; y < (uint32_t)kXcds && it < 0; ++y) {
       const uint32_t xx = (x + y) % kXcds;
-      if (xcd_item(xx, load_relaxed(&g_xq[xx]), items) < 0) continue;  // used up already
-      it = xcd_item(xx, __hip_atomic_fetch_add(&g_xq[xx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), items);
+      if (xcd_item(xx, load_relaxed(&st->xq[xx]), items) < 0) continue;  // used up already
+      it = xcd_item(xx, __hip_atomic_fetch_add(&st->xq[xx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), items);
     }
     sh[0] = (uint32_t)it;
   }
@@ -555,13 +567,13 @@ struct Balance {
 };
 
 // Register this workgroup on its CU (call once, by every thread).
-__device__ __forceinline__ Balance balance_register(uint32_t* slot_sh) {
+__device__ __forceinline__ Balance balance_register(SchedState* st, uint32_t* slot_sh) {
   Balance bal;
   if (threadIdx.x == 0) {
     const uint32_t hw = __builtin_amdgcn_s_getreg(4 | (31 << 11));   // HW_ID
     const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & 7u;  // XCC_ID
     const uint32_t key = (((xcc * 8u + ((hw >> 13) & 7u)) * 2u + ((hw >> 12) & 1u)) * 16u + ((hw >> 8) & 15u));
-    const uint32_t slot = __hip_atomic_fetch_add(&g_cu_slots[key], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t slot = __hip_atomic_fetch_add(&st->cu_slots[key], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     slot_sh[0] = key;
     slot_sh[1] = slot;
   }
@@ -569,8 +581,8 @@ __device__ __forceinline__ Balance balance_register(uint32_t* slot_sh) {
   const uint32_t key = __builtin_amdgcn_readfirstlane(slot_sh[0]);
   const uint32_t slot = __builtin_amdgcn_readfirstlane(slot_sh[1]);
   if (slot < 2u && key < (uint32_t)kCuKeys) {
-    bal.mine = &g_cu_progress[key * 2 + slot];
-    bal.partner = &g_cu_progress[key * 2 + (slot ^ 1u)];
+    bal.mine = &st->cu_progress[key * 2 + slot];
+    bal.partner = &st->cu_progress[key * 2 + (slot ^ 1u)];
   }
   return bal;
 }
@@ -579,12 +591,12 @@ __device__ __forceinline__ Balance balance_register(uint32_t* slot_sh) {
 // (bounded) until every workgroup of the grid has arrived.  The wait only
 // affects cache locality, never the result; it gives up after a fixed number
 // of polls.
-__device__ __forceinline__ void round_sync(int sync, int wid, int items, int round) {
+__device__ __forceinline__ void round_sync(SchedState* st, int sync, int wid, int items, int round) {
   if (sync && wid + (int)gridDim.x < items && round < kMaxRounds) {
     if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(&g_round_ctr[round], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&st->round_ctr[round], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int t = 0; t < 4096; ++t) {
-        if (__hip_atomic_load(&g_round_ctr[round], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gridDim.x) break;
+        if (load_relaxed(&st->round_ctr[round]) >= gridDim.x) break;
         __builtin_amdgcn_s_sleep(8);
       }
     }
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(2 * MT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   int round = 0;
   for (int wid = blockIdx.x; wid < items; wid += gridDim.x, ++round) {
     vsa_attn_item<D, MT, LSE>(p, wid, Ks, Vs, Ids);
-    round_sync(sync, wid, items, round);
+    round_sync(reinterpret_cast<SchedState*>(p.sched), sync, wid, items, round);
   }
 }
 
@@ -769,16 +781,17 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const uint32_t ids_lds = lds_offset(ids);
   uint32_t rows[LPT];
   int nj = 0, njn = 0, j1 = 0, j2 = 0;
+  bool bad = false;  // a kept id at or beyond J was met
   if (num > 0) {
-    const int j0 = sel[0];
+    const int j0 = kept_id(sel, 0, p.J, bad);
     nj = (j0 >= 0) ? blen[j0] : 0;
     stage_ids(prs, max(j0, 0), M, ids_lds, lane);
     wait_vmcnt<0>();
     tile_rows4<D>(rows, ids, w, lane, row_bytes);
     stage4<D>(krs, kbuf(0), rows, koff, w);
     stage4<D>(vrs, vbuf(0), rows, voff, w);
-    j1 = sel[min(1, num - 1)];
-    j2 = sel[min(2, num - 1)];
+    j1 = kept_id(sel, min(1, num - 1), p.J, bad);
+    j2 = kept_id(sel, min(2, num - 1), p.J, bad);
     stage_ids(prs, max(j1, 0), M, ids_lds, lane);
   } else if constexpr (SUM) {
     if (T > 0) {  // no kept block: the first tile is summary tile 0
@@ -857,7 +870,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
     // scalar table reads for the coming blocks (no LDS result is awaited
     // until the barrier that opens the next block)
     __builtin_amdgcn_sched_barrier(0);
-    const int j3 = sel[max(0, min(t + 3, num - 1))];
+    const int j3 = kept_id(sel, max(0, min(t + 3, num - 1)), p.J, bad);
     njn = (j1 >= 0) ? blen[max(j1, 0)] : 0;
     __builtin_amdgcn_sched_barrier(0);
 
@@ -947,6 +960,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
     j2 = j3;
   }
 
+  if (bad) flag_index_error(p.err);
   // ---- merge the two key halves of each query row through LDS ----
   // Once every wave is past its last tile and its copies have landed, buffer 1
   // is free (the next query block's first copies go to buffer 0).
@@ -1014,24 +1028,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ uint32_t slot_sh[2];
   __shared__ uint32_t Kept[SUM ? kSumMaskWords : 1];      // kept blocks of the query block (summaries)
   __shared__ __align__(256) float Bsum[SUM ? 2 * 4 * 64 : 1];  // biases of a summary tile, per parity and wave
+  SchedState* st = reinterpret_cast<SchedState*>(p.sched);
   Balance bal;
   Cohort coh;
   if (sync) {
-    bal = balance_register(slot_sh);
-    coh = cohort_register(slot_sh);
+    bal = balance_register(st, slot_sh);
+    coh = cohort_register(st, slot_sh);
   }
-  int wid = sync ? next_item(coh.xcc, items, slot_sh) : (int)blockIdx.x;
+  int wid = sync ? next_item(st, coh.xcc, items, slot_sh) : (int)blockIdx.x;
   while (wid >= 0 && wid < items) {
     vsa4_item<D, LSE, SUM>(p, wid, KV, Ids, Mx, bal, Kept, Bsum);
     if (sync) {
-      cohort_sync(coh);
-      wid = next_item(coh.xcc, items, slot_sh);
+      cohort_sync(st, coh);
+      wid = next_item(st, coh.xcc, items, slot_sh);
     } else {
       wid += gridDim.x;
     }
   }
   if (sync && threadIdx.x == 0)
-    __hip_atomic_fetch_add(&g_xcd_exited[coh.xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&st->xcd_exited[coh.xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -1070,6 +1085,10 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   for (int pp = 0; pp < num; ++pp) {
     const int j = sel[pp];
     if (j < 0) continue;
+    if (j >= p.J) {  // not a block: skipped and reported
+      flag_index_error(p.err);
+      continue;
+    }
     const int nj = p.block_len[j];
     __syncthreads();
     for (int e = threadIdx.x; e < nj * D; e += 128) {
@@ -1125,8 +1144,8 @@ static hipError_t launch_vsa_lse(const VsaAttnParams& p, hipStream_t s) {
   const int64_t resident = resident_groups(vsa_attn_kernel<D, MT, LSE>, 2 * MT, cache);
   const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
   const int64_t rounds = (items + grid - 1) / grid;
-  const int sync = (rounds > 1) ? 1 : 0;
-  if (sync) clear_rounds_kernel<<<1, 256, 0, s>>>((int)std::min<int64_t>(rounds, kMaxRounds));
+  const int sync = (rounds > 1 && p.sched != nullptr) ? 1 : 0;
+  if (sync) clear_sched_kernel<<<64, 256, 0, s>>>(reinterpret_cast<SchedState*>(p.sched));
   vsa_attn_kernel<D, MT, LSE><<<dim3((unsigned)grid), dim3(2 * MT), 0, s>>>(p, (int)items, sync);
   return hipGetLastError();
 }
@@ -1143,8 +1162,8 @@ static hipError_t launch_vsa4(const VsaAttnParams& p, hipStream_t s) {
   const int64_t resident = resident_groups(vsa4_kernel<D, LSE, SUM>, 256, cache);
   const int64_t grid = (resident > 0) ? std::min(items, resident) : items;
   const int64_t rounds = (items + grid - 1) / grid;
-  const int sync = (rounds > 1) ? 1 : 0;
-  if (sync) clear_rounds_kernel<<<32, 256, 0, s>>>(0);
+  const int sync = (rounds > 1 && p.sched != nullptr) ? 1 : 0;
+  if (sync) clear_sched_kernel<<<64, 256, 0, s>>>(reinterpret_cast<SchedState*>(p.sched));
   vsa4_kernel<D, LSE, SUM><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p, (int)items, sync);
   return hipGetLastError();
 }

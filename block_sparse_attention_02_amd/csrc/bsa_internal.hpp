@@ -157,7 +157,11 @@ struct VsaAttnParams {
   const float* coarse;  // [B, H, J, D]
   const float* gate;    // [H, D]
   int64_t perm_bh_stride;  // elements between the perm tables of consecutive (b, h); 0: shared
+  void* sched;             // scheduler state of the persistent grid (qouter_sched_bytes(), 256-byte aligned)
+  uint32_t* err;           // sticky index-error flag of the device (a kept id >= J sets it)
 };
+// Bytes of the persistent-grid scheduler state the block-mode kernels use.
+size_t qouter_sched_bytes();
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
 
 struct NsaAttnParams {
@@ -174,6 +178,7 @@ struct NsaAttnParams {
   int64_t N;
   float scale_log2;
   float* lse;  // optional [B, Hq, N]
+  uint32_t* err;  // sticky index-error flag (a block id past the sequence sets it)
 };
 hipError_t launch_nsa_attention(const NsaAttnParams& p, bool f32_io, hipStream_t s);
 
@@ -192,6 +197,7 @@ struct KvOuterParams {
   __bf16* o_buf;   // [B, ks, N, Hq, D]
   float* lse_buf;  // [B, ks, N, Hq]
   int32_t* nslot;  // [B, N, Hkv]
+  uint32_t* err;   // sticky index-error flag (a block id past the sequence sets it)
 };
 size_t kvouter_ws_bytes(const KvOuterParams& p);
 hipError_t launch_kvouter(const KvOuterParams& p, void* ws, hipStream_t s);
@@ -207,5 +213,13 @@ struct CombineParams {
   float* lse;  // optional [B, Hq, N]
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+// ---- index errors ----------------------------------------------------------------
+// Records that a kernel met a block id outside its table (one lane per wave
+// calls it; the flag only ever goes from 0 to 1 until bsa_check clears it).
+__device__ __forceinline__ void flag_index_error(uint32_t* err) {
+  if (err != nullptr && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace bsa

@@ -16,6 +16,8 @@
 // Slot rule (the page leaves it open): slot s of (query i, KV head r) is the
 // rank of the block among the row's valid selections in increasing block order
 // (ties by position), which also fixes the summation order of the combine.
+#include <algorithm>
+
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -34,12 +36,20 @@ struct KvLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Chunk capacity: the caller's (0: 2 * k * BK), at most the edge bound, so
+// that begin + cap never overflows an int in the scan.
+int64_t kv_chunk_cap(const KvOuterParams& p) {
+  const int64_t emax = std::max<int64_t>(1, (int64_t)p.B * p.N * p.Hkv * p.ks);
+  const int64_t cap = p.chunk_cap > 0 ? p.chunk_cap : 2 * (int64_t)p.ks * p.BK;
+  return std::min(cap, emax);
+}
+
 KvLayout kv_layout(const KvOuterParams& p) {
   KvLayout L{};
   const int64_t NB = (p.N + p.BK - 1) / p.BK;
   L.rows = (int)(p.B * p.Hkv * NB);
   L.emax = (int64_t)p.B * p.N * p.Hkv * p.ks;
-  const int cap = p.chunk_cap > 0 ? p.chunk_cap : 2 * p.ks * p.BK;
+  const int64_t cap = kv_chunk_cap(p);
   L.max_chunks = (int)(L.rows + (L.emax + cap - 1) / cap);
   size_t o = 0;
   L.off_count = o;  o += align256((size_t)L.rows * 4);
@@ -93,6 +103,7 @@ __global__ void kv_count_kernel(KvOuterParams p, int NB, int32_t* __restrict__ c
   int nvalid = 0;
   for (int q = 0; q < cnt; ++q) {
     const int blk = row[q];
+    if (blk >= NB) flag_index_error(p.err);
     if (blk < 0 || blk >= NB) continue;
     ++nvalid;
     if (p.causal && (int64_t)blk * p.BK > i) {
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict
   int s = 0, sc = 0;
   for (int r = r0; r < r1; ++r) {
     s += count[r];
-    sc += (count[r] + cap - 1) / cap;
+    sc += count[r] / cap + (count[r] % cap != 0);  // ceil without overflow for any cap
   }
   part[tid] = s;
   cpart[tid] = sc;
@@ -141,7 +152,8 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict
   for (int r = r0; r < r1; ++r) {
     rowptr[r] = e;
     const int n = count[r];
-    for (int c0 = 0; c0 < n; c0 += cap) chunks[ce++] = make_int4(r, e + c0, e + min(n, c0 + cap), 0);
+    for (int64_t c0 = 0; c0 < n; c0 += cap)
+      chunks[ce++] = make_int4(r, e + (int)c0, e + (int)std::min<int64_t>(n, c0 + cap), 0);
     e += n;
   }
   if (tid == 1023) {
@@ -213,6 +225,7 @@ __global__ __launch_bounds__(1024) void kv_index_kernel(KvOuterParams p, int NB,
   int nvalid = 0;
   for (int q = 0; q < cnt; ++q) {
     const int blk = row[q];
+    if (!SCATTER && blk >= NB) flag_index_error(p.err);
     if (blk < 0 || blk >= NB) continue;
     ++nvalid;
     if (p.causal && (int64_t)blk * p.BK > i) {
@@ -548,7 +561,7 @@ hipError_t launch_kvouter(const KvOuterParams& p, void* wsv, hipStream_t s) {
   int32_t* nchunk = reinterpret_cast<int32_t*>(ws + L.off_nchunk);
   int4* chunks = reinterpret_cast<int4*>(ws + L.off_chunks);
   int2* edges = reinterpret_cast<int2*>(ws + L.off_edges);
-  const int cap = p.chunk_cap > 0 ? p.chunk_cap : 2 * p.ks * p.BK;
+  const int cap = (int)kv_chunk_cap(p);
 
   kv_clear_kernel<<<dim3(min(1024, (L.rows + 255) / 256)), dim3(256), 0, s>>>(count, cursor, L.rows);
   const int64_t threads = (int64_t)p.B * p.N * p.Hkv;

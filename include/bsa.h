@@ -20,9 +20,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   Every array argument is device memory owned by the caller.  The
- *           library keeps no global state and never allocates: calls that need
- *           scratch take a caller-supplied workspace whose size comes from the
- *           matching *_ws query.
+ *           library never allocates: calls that need scratch take a
+ *           caller-supplied workspace whose size comes from the matching *_ws
+ *           query (contents undefined after the call).  Calls that share a
+ *           workspace must be ordered on one stream; calls with their own
+ *           workspaces may run concurrently on different streams.  The only
+ *           state the library keeps is one sticky index-error flag per device
+ *           (see Errors).
  * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
  *           Every call only enqueues work on that stream and returns; results
  *           are ready when the stream is synchronised.
@@ -31,9 +35,13 @@
  *           written and the status says why (bsa_last_error() gives a message
  *           for the calling thread).  Launch failures map to BSA_ERR_HIP.
  *           Index entries < 0, and entries at positions >= their row count,
- *           are skipped and never dereferenced.  Entries >= the number of
- *           blocks are a caller error that the kernels do not check.
- *           Nothing aborts, throws or prints.
+ *           are skipped and never dereferenced ([VSA] section 6.2: -1 entries
+ *           are not addresses; [NSA] "Tilelang优化实现": negative ids are
+ *           skipped).  Entries that name no block (>= the number of blocks J,
+ *           or at or beyond the sequence in token mode and KV-outer) are
+ *           skipped the same way, and the kernel that meets one sets the
+ *           device's index-error flag, which bsa_check() reports as
+ *           BSA_ERR_INDEX (and clears).  Nothing aborts, throws or prints.
  * Tensors.  A bsa_tdesc describes a 4-D view [B, N, H, D] (batch, token,
  *           head, channel) with element strides sB, sN, sH and D contiguous
  *           (stride 1).  Both BSHD ([B,N,H,D] contiguous) and BHSD
@@ -79,7 +87,10 @@ const char* bsa_last_error(void);
 /* Library version string. */
 const char* bsa_version(void);
 
-/* Synchronise `stream` and report any asynchronous HIP error as BSA_ERR_HIP. */
+/* Synchronise `stream` and report any asynchronous HIP error as BSA_ERR_HIP;
+ * then read the current device's index-error flag: if a kernel (of any
+ * stream of this device) met a block id that names no block since the last
+ * check, clear the flag and return BSA_ERR_INDEX. */
 bsa_status bsa_check(void* stream);
 
 /* ----------------------------------------------------------------------------
@@ -262,6 +273,12 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
  * head) K/V slice with 32-bit byte offsets: it needs N < 2^24, a token stride
  * (dkv.sN) below 2^23 elements and (N - 1) * dkv.sN + D below 2^31 elements;
  * anything larger returns BSA_ERR_UNSUPPORTED.
+ *
+ * Workspace: bsa_qouter_ws() bytes (256-byte aligned, caller-owned, contents
+ * undefined after the call; 0 bytes in token mode and for fp32).  Block mode
+ * in bf16 keeps the work counters of its persistent grid there (cleared by a
+ * kernel on `stream` before every launch), so two calls with different
+ * workspaces can run concurrently on different streams.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* q;
@@ -307,7 +324,8 @@ typedef struct {
   int64_t perm_bh_stride;
 } bsa_qouter_args;
 
-bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* stream);
+bsa_status bsa_qouter_ws(const bsa_qouter_args* a, size_t* bytes);
+bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
  * Coarse pooled-V branch ([VSA] section 6.7, with the pooling of section 2.1).
@@ -453,7 +471,9 @@ bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes,
  *   1. reverse index: for every (b, r, kv block) the list of (i, s) selecting it
  *      (count, exclusive scan, scatter);
  *   2. scheduler: each list is cut into chunks of at most chunk_cap query
- *      positions (0: 2 * k_sel * BK), so hot blocks spread over workgroups;
+ *      positions (0: 2 * k_sel * BK; any cap above B * N * Hkv * k_sel, the
+ *      bound on the number of edges, acts as that bound), so hot blocks
+ *      spread over workgroups; results do not depend on the cap;
  *   3. K1: per chunk, the K/V tile of the block is staged once and the gathered
  *      queries (G heads per position) attend to it with a local softmax:
  *        L_s = log sum_{j in J_s} exp S_j,  O_s = sum_{j in J_s} exp(S_j - L_s) v_j,

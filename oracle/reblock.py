@@ -22,10 +22,8 @@ principal directions:
   of M_Q + lam * I, lam = ridge * tr(M_Q) / D (ridge * 1 when the trace is 0;
   the page mentions a ridge in the source without its value, 1e-4 here keeps
   the factor well defined in fp32); a zero key has no score direction and
-  gets the zero feature; the features are stored in fp16 (unit vectors, so
-  |u_d| <= 1) and every split decision reads the stored values -- the HIP
-  path's storage precision, taken on both sides because the splits are
-  integer decisions made from them;
+  gets the zero feature; the features are exact (float64): the section
+  defines them as the normalised rows z_j / |z_j| and nothing rounds them;
 * tree: a node holding n tokens spans c = ceil(n / M) leaves; its first child
   takes floor(c / 2) leaves (floor(c / 2) * M tokens), the second the rest; a
   node with c <= 1 is a leaf.  The ranges depend on N and M only;
@@ -66,17 +64,13 @@ def metric_factor(M, ridge=DEFAULT_RIDGE):
     return np.linalg.cholesky(M + lam * np.eye(D))
 
 
-def key_features(K, Q, ridge=DEFAULT_RIDGE, store=np.float16):
-    """Unit features of the keys under the query-side metric: [B, h, N, D],
-    rounded to `store` (fp16: the values the splits read; None: exact)."""
+def key_features(K, Q, ridge=DEFAULT_RIDGE):
+    """Unit features of the keys under the query-side metric: [B, h, N, D]."""
     L = metric_factor(second_moment(Q), ridge)
     Kt = np.transpose(np.asarray(K, dtype=np.float64), (0, 2, 1, 3))
     z = np.matmul(Kt, L)
     nrm = np.linalg.norm(z, axis=-1, keepdims=True)
-    u = np.where(nrm > 0, z / np.where(nrm > 0, nrm, 1.0), 0.0)
-    if store is not None:
-        u = u.astype(store).astype(np.float64)
-    return u
+    return np.where(nrm > 0, z / np.where(nrm > 0, nrm, 1.0), 0.0)
 
 
 def tree_slots(N, M):

@@ -33,9 +33,43 @@ def assert_attn_close(got, ref, what, mask=None):
     assert mx <= ATOL_MAX and mean <= ATOL_MEAN, "%s: max %.3g mean %.3g" % (what, mx, mean)
 
 
-def topk_mismatch(got_idx, ref_idx, gap):
-    """(non-exempt mismatching rows, exempt rows)."""
-    got = got_idx.cpu().numpy() if isinstance(got_idx, torch.Tensor) else got_idx
-    diff = (got != ref_idx).any(-1)
-    exempt = gap < GAP_EXEMPT
-    return int((diff & ~exempt).sum()), int(exempt.sum())
+def check_topk(got_idx, E, R, ref_idx, gap, cols=None, what="topk"):
+    """Complete check of a TopK selection against float64 scores.
+
+    got_idx: kept ids of every row (first R entries used; ascending), E: the
+    float64 scores [..., J] of the same rows, ref_idx: the oracle's kept ids
+    (ties to the lower index), gap: E_(R) - E_(R+1) per row.  ``cols``
+    (b0, b1) restricts the selection to that column range (one H3 region).
+
+    * every row: R distinct ascending ids inside the column range;
+    * rows with gap >= GAP_EXEMPT: exactly the oracle's ids;
+    * exempt rows (several answers are correct): a valid top-R within the
+      gap -- every kept score >= E_(R) - GAP_EXEMPT and every dropped score
+      <= E_(R+1) + GAP_EXEMPT.
+    Asserts all three and returns the number of exempt rows."""
+    got = got_idx.cpu().numpy() if isinstance(got_idx, torch.Tensor) else np.asarray(got_idx)
+    J = E.shape[-1]
+    b0, b1 = (0, J) if cols is None else cols
+    g = got[..., :R].reshape(-1, R).astype(np.int64)
+    r = np.asarray(ref_idx)[..., :R].reshape(-1, R)
+    e = np.asarray(E, dtype=np.float64).reshape(-1, J)
+    gp = np.asarray(gap, dtype=np.float64).reshape(-1)
+    assert ((g >= b0) & (g < b1)).all(), what + ": id outside the column range"
+    assert (np.diff(g, axis=-1) > 0).all() if R > 1 else True, what + ": ids not strictly increasing"
+    exempt = gp < GAP_EXEMPT
+    bad = int(((g != r).any(-1) & ~exempt).sum())
+    sub = e[:, b0:b1]
+    srt = -np.sort(-sub, axis=-1)
+    e_r = srt[:, R - 1]
+    e_r1 = srt[:, R] if R < b1 - b0 else np.full(len(sub), -np.inf)
+    kept = np.take_along_axis(e, g, axis=-1)
+    dropped = sub.copy()
+    np.put_along_axis(dropped, g - b0, -np.inf, axis=-1)
+    ok = (kept >= e_r[:, None] - GAP_EXEMPT).all(-1) & (dropped.max(-1) <= e_r1 + GAP_EXEMPT)
+    invalid = int((~ok & exempt).sum())
+    print("%s: %d rows, %d exempt near-ties (%d not a valid top-%d), %d mismatches"
+          % (what, len(g), int(exempt.sum()), invalid, R, bad), flush=True)
+    assert bad == 0, "%s: %d rows differ from the oracle" % (what, bad)
+    assert invalid == 0, "%s: %d exempt rows are not a valid top-%d" % (what, invalid, R)
+    assert ok[~exempt].all(), what + ": a non-exempt row fails the validity check"
+    return int(exempt.sum())

@@ -107,20 +107,58 @@ def _qouter_args(**kw):
 ])
 def test_qouter_validation(field, value, status):
     a = _qouter_args(**{field: value})
-    assert L.load().bsa_forward_qouter(ctypes.byref(a), None) == status
+    assert L.load().bsa_forward_qouter(ctypes.byref(a), None, 0, None) == status
+    n = ctypes.c_size_t(7)
+    assert L.load().bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)) == status
+
+
+def test_qouter_workspace():
+    """Block mode in bf16 needs the scheduler workspace (the same size for any
+    shape); token mode and fp32 need none.  A missing, short or misaligned
+    workspace is rejected before anything is enqueued."""
+    lib = L.load()
+    n = ctypes.c_size_t()
+    a = _qouter_args()
+    assert lib.bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    need = n.value
+    assert 0 < need <= 1 << 20 and need % 256 == 0
+    d2 = L.TDesc(2, 4096, 8, 64, 4096 * 8 * 64, 8 * 64, 64)
+    assert lib.bsa_qouter_ws(ctypes.byref(_qouter_args(dq=d2, dkv=d2, dout=d2, J=64)), ctypes.byref(n)) == L.BSA_OK
+    assert n.value == need
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None, 0, None) == L.BSA_ERR_WORKSPACE
+    assert lib.bsa_forward_qouter(ctypes.byref(a), ctypes.c_void_p(256), need - 1, None) == L.BSA_ERR_WORKSPACE
+    assert lib.bsa_forward_qouter(ctypes.byref(a), ctypes.c_void_p(256 + 16), need, None) == L.BSA_ERR_WORKSPACE
+    assert b"workspace" in lib.bsa_last_error()
+    f32 = _qouter_args(dt=L.BSA_F32)
+    assert lib.bsa_qouter_ws(ctypes.byref(f32), ctypes.byref(n)) == L.BSA_OK and n.value == 0
+    tok = _qouter_args(mode=L.BSA_SEL_TOKEN, blk_idx=ctypes.c_void_p(256), S=16, BS=64)
+    assert lib.bsa_qouter_ws(ctypes.byref(tok), ctypes.byref(n)) == L.BSA_OK and n.value == 0
+
+
+def test_check_without_a_device_is_an_error_not_a_crash():
+    """bsa_check reports a missing device through BSA_ERR_HIP (the index-error
+    flag lives on the device and is read only after a successful sync)."""
+    if bsa_gpu_present():
+        pytest.skip("a GPU is present")
+    assert L.load().bsa_check(None) == L.BSA_ERR_HIP
+
+
+def bsa_gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
 
 
 def test_qouter_shape_checks():
     lib = L.load()
     d64 = L.TDesc(1, 64, 2, 96, 64 * 2 * 96, 2 * 96, 96)
     a = _qouter_args(dq=d64, dkv=d64, dout=d64)
-    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_UNSUPPORTED   # D = 96
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None, 0, None) == L.BSA_ERR_UNSUPPORTED   # D = 96
     dkv = L.TDesc(1, 64, 1, 128, 64 * 128, 128, 128)
     a = _qouter_args(dkv=dkv)
-    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_UNSUPPORTED   # VSA needs Hq == Hkv
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None, 0, None) == L.BSA_ERR_UNSUPPORTED   # VSA needs Hq == Hkv
     bad = L.TDesc(1, 64, 2, 128, 64 * 2 * 128, 2 * 128 + 4, 128)
     a = _qouter_args(dq=bad)
-    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_SHAPE         # stride % 8
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None, 0, None) == L.BSA_ERR_SHAPE         # stride % 8
 
 
 def test_qouter_32bit_slice_limits():
@@ -131,15 +169,15 @@ def test_qouter_32bit_slice_limits():
     H, D = 24, 128
     big = 1 << 20  # 2^20 tokens x 24 heads x 128 x 2 bytes = 6 GiB slice span
     d = L.TDesc(1, big, H, D, big * H * D, H * D, D)
-    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None, 0, None) == L.BSA_ERR_UNSUPPORTED
     d = L.TDesc(1, 1 << 24, 1, 64, (1 << 24) * 64, 64, 64)  # 2 GiB slice, but N = 2^24
-    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None, 0, None) == L.BSA_ERR_UNSUPPORTED
     d = L.TDesc(1, 64, 1, 128, 64 * (1 << 23), 1 << 23, 128)  # token stride 2^24 bytes
-    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None) == L.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_forward_qouter(ctypes.byref(_qouter_args(dq=d, dkv=d, dout=d)), None, 0, None) == L.BSA_ERR_UNSUPPORTED
     # a 384 MiB slice span passes, and the call stops at the summaries check that follows
     ok = L.TDesc(1, 1 << 16, H, D, (1 << 16) * H * D, H * D, D)
     a = _qouter_args(dq=ok, dkv=ok, dout=ok, k_sum=ctypes.c_void_p(256))
-    assert lib.bsa_forward_qouter(ctypes.byref(a), None) == L.BSA_ERR_ARG
+    assert lib.bsa_forward_qouter(ctypes.byref(a), None, 0, None) == L.BSA_ERR_ARG
 
 
 H3_CASES = [
@@ -215,3 +253,184 @@ def test_h3_route_validation(spans, budgets, kw, status):
     assert L.load().h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == status
     if status == L.BSA_OK:
         assert n.value == 2 * 10 * 64 * 4
+
+
+def _kv_args(**kw):
+    dq = L.TDesc(1, 256, 8, 128, 256 * 8 * 128, 8 * 128, 128)
+    dkv = L.TDesc(1, 256, 2, 128, 256 * 2 * 128, 2 * 128, 128)
+    ph = ctypes.c_void_p(256)
+    a = L.KvOuterArgs(q=ph, k=ph, v=ph, dq=dq, dkv=dkv, dt=L.BSA_BF16, scale=0.088, causal=1, q2k=ph,
+                      q2k_cnt=None, k_sel=4, BK=128, o_buf=ph, lse_buf=ph, nslot=ph, chunk_cap=0)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q2k", None, L.BSA_ERR_ARG),
+    ("nslot", None, L.BSA_ERR_ARG),
+    ("dt", L.BSA_F32, L.BSA_ERR_UNSUPPORTED),
+    ("BK", 96, L.BSA_ERR_UNSUPPORTED),
+    ("k_sel", 0, L.BSA_ERR_UNSUPPORTED),
+    ("k_sel", 65, L.BSA_ERR_UNSUPPORTED),
+    ("chunk_cap", -1, L.BSA_ERR_ARG),
+    ("scale", float("nan"), L.BSA_ERR_ARG),
+    ("o_buf", ctypes.c_void_p(264), L.BSA_ERR_SHAPE),
+    ("dkv", L.TDesc(1, 256, 3, 128, 256 * 3 * 128, 3 * 128, 128), L.BSA_ERR_SHAPE),   # 8 % 3
+    ("dkv", L.TDesc(1, 255, 2, 128, 255 * 2 * 128, 2 * 128, 128), L.BSA_ERR_SHAPE),   # N differs
+    ("dkv", L.TDesc(1, 256, 2, 96, 256 * 2 * 96, 2 * 96, 96), L.BSA_ERR_UNSUPPORTED),  # D differs / 96
+])
+def test_kvouter_validation(field, value, status):
+    lib = L.load()
+    a = _kv_args(**{field: value})
+    n = ctypes.c_size_t()
+    assert lib.bsa_kvouter_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    assert lib.bsa_forward_kvouter(ctypes.byref(a), None, 0, None) == status
+    assert lib.bsa_last_error()
+
+
+def test_kvouter_workspace_and_chunk_cap_bound():
+    """The workspace holds counts, cursors, row pointers, the chunk list and
+    the edges; a chunk cap above the number of possible edges (up to INT_MAX)
+    acts as that bound, so the chunk list of the scan never overflows."""
+    lib = L.load()
+    n0, n1, n2 = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.bsa_kvouter_ws(ctypes.byref(_kv_args()), ctypes.byref(n0)) == L.BSA_OK
+    emax = 256 * 2 * 4
+    assert lib.bsa_kvouter_ws(ctypes.byref(_kv_args(chunk_cap=emax)), ctypes.byref(n1)) == L.BSA_OK
+    assert lib.bsa_kvouter_ws(ctypes.byref(_kv_args(chunk_cap=2 ** 31 - 1)), ctypes.byref(n2)) == L.BSA_OK
+    assert n1.value == n2.value > 0
+    assert n0.value >= emax * 8   # the (position, slot) edge list alone
+    a = _kv_args()
+    assert lib.bsa_forward_kvouter(ctypes.byref(a), ctypes.c_void_p(256), n0.value - 1, None) == L.BSA_ERR_WORKSPACE
+    assert lib.bsa_forward_kvouter(ctypes.byref(a), ctypes.c_void_p(256 + 128), n0.value,
+                                   None) == L.BSA_ERR_WORKSPACE
+
+
+def _combine_args(**kw):
+    ph = ctypes.c_void_p(256)
+    d = L.TDesc(1, 256, 8, 128, 256 * 8 * 128, 8 * 128, 128)
+    a = L.CombineArgs(o_buf=ph, lse_buf=ph, nslot=ph, k_sel=4, Hkv=2, dout=d, out=ph, lse=None)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("o_buf", None, L.BSA_ERR_ARG),
+    ("out", None, L.BSA_ERR_ARG),
+    ("Hkv", 3, L.BSA_ERR_SHAPE),
+    ("Hkv", 0, L.BSA_ERR_SHAPE),
+    ("k_sel", 0, L.BSA_ERR_UNSUPPORTED),
+    ("out", ctypes.c_void_p(260), L.BSA_ERR_SHAPE),
+    ("dout", L.TDesc(1, 256, 8, 512, 256 * 8 * 512, 8 * 512, 512), L.BSA_ERR_UNSUPPORTED),
+    ("dout", L.TDesc(1, 256, 8, 128, 256 * 8 * 128, 8 * 128 + 4, 128), L.BSA_ERR_SHAPE),
+])
+def test_combine_validation(field, value, status):
+    assert L.load().bsa_combine(ctypes.byref(_combine_args(**{field: value})), None) == status
+
+
+def _coarse_args(**kw):
+    ph = ctypes.c_void_p(256)
+    d = L.TDesc(1, 2048, 2, 128, 2048 * 2 * 128, 2 * 128, 128)
+    a = L.CoarseArgs(v=ph, d=d, dt=L.BSA_BF16, perm=ph, block_len=ph, J=32, M=64, E=ph, vbar=None, C=ph)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("E", None, L.BSA_ERR_ARG),
+    ("C", None, L.BSA_ERR_ARG),
+    ("dt", 5, L.BSA_ERR_ARG),
+    ("J", 0, L.BSA_ERR_SHAPE),
+    ("C", ctypes.c_void_p(264), L.BSA_ERR_SHAPE),
+    ("d", L.TDesc(1, 2048, 2, 96, 2048 * 2 * 96, 2 * 96, 96), L.BSA_ERR_UNSUPPORTED),
+])
+def test_coarse_validation(field, value, status):
+    lib = L.load()
+    a = _coarse_args(**{field: value})
+    n = ctypes.c_size_t()
+    assert lib.vsa_coarse_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    assert lib.vsa_coarse(ctypes.byref(a), None, 0, None) == status
+
+
+def test_coarse_workspace():
+    lib = L.load()
+    n = ctypes.c_size_t()
+    assert lib.vsa_coarse_ws(ctypes.byref(_coarse_args()), ctypes.byref(n)) == L.BSA_OK
+    # vbar (2 x 32 x 128 fp32) + the transposed bf16 hi/lo copy (2 x 2 x 128 x 64)
+    assert n.value == 2 * 32 * 128 * 4 + 2 * 2 * 128 * 64 * 2
+    assert lib.vsa_coarse(ctypes.byref(_coarse_args()), None, 0, None) == L.BSA_ERR_WORKSPACE
+
+
+def _summary_args(**kw):
+    ph = ctypes.c_void_p(256)
+    d = L.TDesc(1, 2048, 2, 128, 2048 * 2 * 128, 2 * 128, 128)
+    a = L.SummaryArgs(q=ph, k=ph, v=ph, d=d, dt=L.BSA_BF16, perm=ph, block_len=ph, J=32, M=64, scale=0.088,
+                      anchor=None, anchor_out=None, k_sum=ph, v_sum=ph, b_sum=ph)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k_sum", None, L.BSA_ERR_ARG),
+    ("q", None, L.BSA_ERR_ARG),          # no anchor and no queries to take it from
+    ("dt", L.BSA_F32, L.BSA_ERR_UNSUPPORTED),
+    ("M", 65, L.BSA_ERR_SHAPE),
+    ("scale", float("inf"), L.BSA_ERR_ARG),
+    ("v", ctypes.c_void_p(264), L.BSA_ERR_SHAPE),
+])
+def test_summaries_validation(field, value, status):
+    lib = L.load()
+    a = _summary_args(**{field: value})
+    n = ctypes.c_size_t()
+    assert lib.spark_summaries_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    assert lib.spark_summaries(ctypes.byref(a), None, 0, None) == status
+
+
+def test_summaries_workspace_only_without_anchor():
+    lib = L.load()
+    n = ctypes.c_size_t()
+    assert lib.spark_summaries_ws(ctypes.byref(_summary_args()), ctypes.byref(n)) == L.BSA_OK and n.value > 0
+    a = _summary_args(anchor=ctypes.c_void_p(256), q=None)
+    assert lib.spark_summaries_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK and n.value == 0
+
+
+def _reblock_args(**kw):
+    ph = ctypes.c_void_p(256)
+    d = L.TDesc(1, 2048, 2, 128, 2048 * 2 * 128, 2 * 128, 128)
+    a = L.ReblockArgs(q=ph, k=ph, d=d, dt=L.BSA_BF16, M=64, ridge=1e-4, perm=ph, block_len=ph)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("perm", None, L.BSA_ERR_ARG),
+    ("dt", L.BSA_F32, L.BSA_ERR_UNSUPPORTED),
+    ("M", 48, L.BSA_ERR_UNSUPPORTED),
+    ("ridge", 0.0, L.BSA_ERR_ARG),
+    ("ridge", float("nan"), L.BSA_ERR_ARG),
+    ("q", ctypes.c_void_p(264), L.BSA_ERR_SHAPE),
+    ("d", L.TDesc(1, 2048, 2, 32, 2048 * 2 * 32, 2 * 32, 32), L.BSA_ERR_UNSUPPORTED),
+])
+def test_reblock_validation(field, value, status):
+    lib = L.load()
+    a = _reblock_args(**{field: value})
+    n = ctypes.c_size_t()
+    assert lib.spark_reblock_ws(ctypes.byref(a), ctypes.byref(n)) == status
+    assert lib.spark_reblock(ctypes.byref(a), None, 0, None) == status
+
+
+def test_reblock_dims_and_workspace():
+    lib = L.load()
+    J, nl = ctypes.c_int(), ctypes.c_int()
+    assert lib.spark_reblock_dims(115200, 64, ctypes.byref(J), ctypes.byref(nl)) == L.BSA_OK
+    assert (J.value, nl.value) == (1800, 12)
+    assert lib.spark_reblock_dims(0, 64, ctypes.byref(J), ctypes.byref(nl)) == L.BSA_ERR_SHAPE
+    n = ctypes.c_size_t()
+    assert lib.spark_reblock_ws(ctypes.byref(_reblock_args()), ctypes.byref(n)) == L.BSA_OK and n.value > 0
+    assert lib.spark_reblock(ctypes.byref(_reblock_args()), ctypes.c_void_p(256), n.value - 1,
+                             None) == L.BSA_ERR_WORKSPACE

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import GAP_EXEMPT, assert_attn_close, to64
+from gpu_util import assert_attn_close, check_topk, to64
 from workloads import h3_inputs, scaled, workload
 
 pytestmark = pytest.mark.gpu
@@ -49,21 +49,29 @@ ROUTE_CFGS = {
 
 
 def _oracle_route(x, cfg, lay, budgets):
+    """The oracle's grouped tables plus its float64 scores E [B, h, J, J]."""
     Q, K = to64(x["q"]), to64(x["k"])
     qbar = oracle.pool_blocks(Q, lay["perm"], lay["block_len"], lay["M"])
     kbar = oracle.pool_blocks(K, lay["perm"], lay["block_len"], lay["M"])
-    return oracle.h3_route(qbar, kbar, lay["num_prefix"], lay["spans"], budgets)
+    ref_idx, ref_num, gap = oracle.h3_route(qbar, kbar, lay["num_prefix"], lay["spans"], budgets)
+    return ref_idx, ref_num, gap, oracle.routing_matrix(qbar, kbar)
 
 
-def _check_tables(idx, num, ref_idx, ref_num, gap, what):
+def _check_tables(idx, num, ref, spans, budgets, num_prefix, what):
+    """Counts and context rows exactly; each region's part of every video row
+    through the complete TopK check (bit-exact outside near-ties, a valid
+    top-R_r within the gap inside them)."""
+    ref_idx, ref_num, gap, E = ref
     got_idx, got_num = idx.cpu().numpy(), num.cpu().numpy()
     assert np.array_equal(got_num, ref_num), what + ": counts differ"
-    exempt = (gap < GAP_EXEMPT).any(-1)
-    bad = ((got_idx != ref_idx).any(-1) & ~exempt).sum()
-    print("%s: %d rows, %d exempt near-ties, %d mismatches" % (what, exempt.size, int(exempt.sum()), int(bad)),
-          flush=True)
-    assert bad == 0
-    # exempt rows are still valid tables: ascending, the prefix, the right count per region
+    P = num_prefix
+    assert np.array_equal(got_idx[:, :, :P], ref_idx[:, :, :P]), what + ": context rows differ"
+    assert (got_idx[:, :, P:, :P] == np.arange(P)).all(), what + ": video rows miss the prefix"
+    off = P
+    for r, ((b0, b1), R) in enumerate(zip(spans, budgets)):
+        check_topk(got_idx[:, :, P:, off:off + R], E[:, :, P:], R, ref_idx[:, :, P:, off:off + R],
+                   gap[:, :, P:, r], cols=(b0, b1), what="%s region %d" % (what, r))
+        off += R
     return got_idx
 
 
@@ -80,8 +88,8 @@ def test_grouped_route_matches_oracle(name):
     Q, K = to64(x["q"]), to64(x["k"])
     rq = oracle.pool_blocks(Q, lay["perm"], lay["block_len"], lay["M"])
     assert (np.abs(to64(qbar) - rq) / np.maximum(1.0, np.abs(rq))).max() <= 1e-5
-    ref_idx, ref_num, gap = _oracle_route(x, cfg, lay, budgets)
-    got = _check_tables(idx, num, ref_idx, ref_num, gap, name)
+    ref = _oracle_route(x, cfg, lay, budgets)
+    got = _check_tables(idx, num, ref, geom.spans, budgets, geom.num_prefix, name)
     P = geom.num_prefix
     for row, n in zip(got.reshape(-1, geom.J), num.cpu().numpy().reshape(-1)):
         kept = row[:n]
@@ -142,8 +150,8 @@ def test_h3_full_size_sampled():
     heads = [0, 7, 15, 23]
     hsel = torch.tensor(heads, device=DEV)
     sub = {k_: v_[:, :, hsel] for k_, v_ in x.items()}
-    ref_idx, ref_num, gap = _oracle_route(sub, cfg, lay, budgets)
-    _check_tables(idx[:, hsel], num[:, hsel], ref_idx, ref_num, gap, "h3 full size")
+    ref = _oracle_route(sub, cfg, lay, budgets)
+    _check_tables(idx[:, hsel], num[:, hsel], ref, geom.spans, budgets, geom.num_prefix, "h3 full size")
     J, P = geom.J, geom.num_prefix
     (r0, r1), (t0, t1) = geom.spans
     rng = np.random.default_rng(7)

@@ -28,15 +28,6 @@ def test_factor_reproduces_the_ridged_moment():
     assert np.max(np.abs(L @ np.swapaxes(L, -1, -2) - (M + 1e-3 * tr / 6 * np.eye(6)))) < 1e-12
 
 
-def test_features_stored_in_fp16():
-    rng = np.random.default_rng(58)
-    Q, K = rng.standard_normal((1, 50, 1, 8)), rng.standard_normal((1, 50, 1, 8))
-    exact = rb.key_features(K, Q, store=None)
-    stored = rb.key_features(K, Q)
-    assert np.array_equal(stored, exact.astype(np.float16).astype(np.float64))
-    assert np.max(np.abs(stored - exact)) <= 2.0 ** -11
-
-
 def test_zero_trace_and_zero_key():
     Q = np.zeros((1, 5, 1, 3))
     L = rb.metric_factor(rb.second_moment(Q), ridge=0.25)
@@ -54,7 +45,7 @@ def test_cosine_identity_with_score_profiles():
     B, N, h, D = 1, 300, 2, 8
     Q = rng.standard_normal((B, N, h, D))
     K = rng.standard_normal((B, N, h, D))
-    U = rb.key_features(K, Q, ridge=0.0, store=None)
+    U = rb.key_features(K, Q, ridge=0.0)
     for hh in range(h):
         S = Q[0, :, hh] @ K[0, :, hh].T          # [queries, keys]: column j = profile of key j
         Sn = S / np.linalg.norm(S, axis=0, keepdims=True)

@@ -179,3 +179,43 @@ def test_mean_summary_differs_from_reweight():
     O, _ = oracle.reweight_attention(Q, K, V, tab["perm"], tab["block_len"], M, idx, num, mk, mv, mb)
     dense = _dense(Q[0, :, 0], K[0, :, 0], V[0, :, 0])
     assert np.max(np.abs(O[0, :, 0] - dense)) > 1e-3
+
+
+def test_seeded_construction_of_section_10(golden):
+    """The page's own check (section 10): with the summaries taken at the
+    query, the mixed softmax reproduces dense attention to rounding; plain
+    mean summaries miss it by the printed 0.240925."""
+    g = golden("spark_seeded_construction.txt")
+    n, dk, dv, blk = (int(g[key][0]) for key in ("tokens", "key_dim", "value_dim", "block"))
+    rng = np.random.default_rng(int(g["seed"][0]))
+    k = rng.normal(size=(n, dk))
+    v = rng.normal(size=(n, dv))
+    a = rng.normal(size=dk)
+    tab = oracle.tile_index(n, 1, 1, blk, 1, 1)
+    J, M = tab["J"], tab["M"]
+    # the value channels are padded with zeros up to the key width (the
+    # oracle keeps one channel count); the padding channels stay zero
+    K = k.reshape(1, n, 1, dk)
+    V = np.zeros((1, n, 1, dk))
+    V[0, :, 0, :dv] = v
+    Q = np.broadcast_to(a, (1, n, 1, dk)).copy()  # every query row is a
+    exact = [int(x) for x in g["exact_blocks"]]
+    idx = np.full((1, 1, J, len(exact)), -1, dtype=np.int64)
+    idx[0, 0, :, :] = exact
+    num = np.full((1, 1, J), len(exact), dtype=np.int64)
+    dense = _dense(a[None], k, v)[0]
+    ks, vs, b, _ = oracle.block_summaries(K, V, tab["perm"], tab["block_len"], M, a.reshape(1, 1, dk))
+    O, _ = oracle.reweight_attention(Q, K, V, tab["perm"], tab["block_len"], M, idx, num, ks, vs, b)
+    err = np.abs(O[0, :, 0, :dv] - dense).max()
+    assert err <= float(g["reweight_assert"][0])
+    assert np.all(O[0, :, 0, dv:] == 0.0)
+    mk = np.zeros_like(ks)
+    mv = np.zeros_like(vs)
+    for j in range(J):
+        toks = tab["perm"][j * M: (j + 1) * M]
+        mk[0, 0, j] = K[0, toks, 0].mean(axis=0)
+        mv[0, 0, j] = V[0, toks, 0].mean(axis=0)
+    mb = np.full((1, 1, J), math.log(M))
+    Om, _ = oracle.reweight_attention(Q, K, V, tab["perm"], tab["block_len"], M, idx, num, mk, mv, mb)
+    err_mean = np.abs(Om[0, :, 0, :dv] - dense).max()
+    assert abs(err_mean - float(g["mean_summary_max_err"][0])) <= 5e-7

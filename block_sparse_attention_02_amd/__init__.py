@@ -26,6 +26,8 @@ from .api import (
     h3_forward,
     spark_reblock,
     reblock_forward,
+    qouter_workspace,
+    check,
 )
 from . import metrics
 
@@ -50,5 +52,7 @@ __all__ = [
     "h3_forward",
     "spark_reblock",
     "reblock_forward",
+    "qouter_workspace",
+    "check",
     "metrics",
 ]

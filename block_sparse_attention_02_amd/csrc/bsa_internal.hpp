@@ -215,10 +215,12 @@ struct CombineParams {
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
 // ---- index errors ----------------------------------------------------------------
-// Records that a kernel met a block id outside its table (one lane per wave
-// calls it; the flag only ever goes from 0 to 1 until bsa_check clears it).
+// Records that a kernel met a block id outside its table: the lowest active
+// lane of the calling wave sets the flag (lanes may call it divergently); the
+// flag only ever goes from 0 to 1 until bsa_check clears it.
 __device__ __forceinline__ void flag_index_error(uint32_t* err) {
-  if (err != nullptr && (threadIdx.x & 63) == 0)
+  const uint64_t active = __builtin_amdgcn_read_exec();
+  if (err != nullptr && (int)(threadIdx.x & 63) == __builtin_ctzll(active))
     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

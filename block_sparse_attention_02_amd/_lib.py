@@ -119,6 +119,7 @@ PROTOTYPES = {
     "vsa_pool_route_topk": (_i32, [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]),
     "bsa_qouter_ws": (_i32, [ctypes.POINTER(QOuterArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "bsa_forward_qouter": (_i32, [ctypes.POINTER(QOuterArgs), _p, ctypes.c_size_t, _p]),
+    "bsa_forward_qouter_static": (_i32, [ctypes.POINTER(QOuterArgs), _p]),
     "h3_tile_dims": (_i32, [ctypes.POINTER(Segment), _i32, _i32, _i32, _i32] + [ctypes.POINTER(_i32)] * 6),
     "h3_tile_index": (_i32, [ctypes.POINTER(Segment), _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
     "h3_pool_route_topk_ws": (_i32, [ctypes.POINTER(H3RouteArgs), ctypes.POINTER(ctypes.c_size_t)]),

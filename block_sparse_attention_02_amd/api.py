@@ -162,8 +162,15 @@ def _qouter_args(q, k, v, out, scale, mode, lse):
 
 def _forward_qouter(a, device, workspace):
     """bsa_forward_qouter with the caller's workspace (allocated when None or
-    too small; the library itself never allocates)."""
+    too small; the library itself never allocates).  ``workspace="static"``
+    calls bsa_forward_qouter_static instead, which needs no workspace (calls
+    that overlap on one device then race; see include/bsa.h)."""
     lib = _lib()
+    if isinstance(workspace, str):
+        if workspace != "static":
+            raise ValueError("workspace must be a tensor, None or 'static'")
+        L.check(lib.bsa_forward_qouter_static(ctypes.byref(a), _stream(device)))
+        return
     n = ctypes.c_size_t()
     L.check(lib.bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)))
     if n.value and (workspace is None or workspace.numel() < n.value):
@@ -250,7 +257,8 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
     gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added.
     ``perm_bh_stride``: per-(b, h) tables in ``perm`` (as in pool_route_topk).
     ``workspace``: optional uint8 device tensor from qouter_workspace (calls
-    that share one must be ordered on one stream)."""
+    that share one must be ordered on one stream), or "static" for the
+    library's no-allocation entry point."""
     _need_cuda(q, k, v, perm, block_len, q2k_idx, q2k_num)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")

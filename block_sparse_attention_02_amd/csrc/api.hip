@@ -497,6 +497,58 @@ bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* ws, size_t ws_byte
   return launch_qouter(a, need ? ws : nullptr, stream);
 }
 
+// ---------------------------------------------- query-outer attention, no allocation
+// Scratch of bsa_forward_qouter_static: the scheduler state that
+// bsa_forward_qouter keeps in the caller's workspace.  One copy per device,
+// held until the process ends; host code reaches a device's copy only through
+// the address hipGetSymbolAddress returns for it (kept in g_scratch_ptr).
+constexpr size_t kQouterScratchBytes = 256 * 1024;
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[kQouterScratchBytes];
+
+namespace {
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// The current device's scratch address, looked up once per device with that
+// device current; nullptr (and the HIP error in *e) if the lookup fails.
+void* device_scratch(hipError_t* e) {
+  int dev = 0;
+  *e = hipGetDevice(&dev);
+  if (*e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*e != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+bsa_status bsa_forward_qouter_static(const bsa_qouter_args* a, void* stream) {
+  bsa_status st = check_qouter(a);
+  if (st != BSA_OK) return st;
+  const size_t need = qouter_ws_need(a);
+  if (need > kQouterScratchBytes)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter_static: %zu bytes of scratch needed, the static limit is %zu",
+                need, kQouterScratchBytes);
+  void* sched = nullptr;
+  if (need) {
+    hipError_t e = hipSuccess;
+    sched = device_scratch(&e);
+    if (!sched) return hip_status(e, "bsa_forward_qouter_static: scratch address");
+  }
+  return launch_qouter(a, sched, stream);
+}
+
 // ------------------------------------------------------------------ coarse branch
 static bsa_status check_coarse(const vsa_coarse_args* a) {
   if (!a) return fail(BSA_ERR_ARG, "vsa_coarse: null args");

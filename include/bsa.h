@@ -327,6 +327,19 @@ typedef struct {
 bsa_status bsa_qouter_ws(const bsa_qouter_args* a, size_t* bytes);
 bsa_status bsa_forward_qouter(const bsa_qouter_args* a, void* ws, size_t ws_bytes, void* stream);
 
+/* bsa_forward_qouter for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, kernels and results, with no workspace argument.  The scratch
+ * it needs (the persistent grid's work counters, the bsa_qouter_ws() bytes)
+ * is a static device array of 256 KiB inside the library, one per device,
+ * held until the process ends; the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Every call on a device shares that device's
+ * array and clears it on `stream` before use, so calls that overlap on one
+ * device race (their work counters mix and outputs may be left unwritten):
+ * order such calls on one stream.  A request whose scratch would exceed the
+ * static array returns BSA_ERR_UNSUPPORTED. */
+bsa_status bsa_forward_qouter_static(const bsa_qouter_args* a, void* stream);
+
 /* ----------------------------------------------------------------------------
  * Coarse pooled-V branch ([VSA] section 6.7, with the pooling of section 2.1).
  *

@@ -1,6 +1,7 @@
 """Build libbsa.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_attention_02_amd.build [--jobs N]
+    python block_sparse_attention_02_amd/build.py [--jobs N]   (runs without importing the package,
+                                                           so a stale library does not stop it)
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` at the
 repository root, then linked into ``block_sparse_attention_02_amd/libbsa.so``.

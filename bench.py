@@ -89,6 +89,8 @@ def _profiled_traffic(profile, sources):
 
 
 ATTN_SOURCES = ("attn_vsa.hip", "bsa_device.hpp", "bsa_internal.hpp")
+# the kernel that serves 64-row blocks without summaries
+ATTN_KERNEL = "vsa_pp_kernel"
 KV_SOURCES = ("kvouter.hip", "bsa_device.hpp", "bsa_internal.hpp")
 
 
@@ -308,8 +310,8 @@ def bench_video(args):
     w = _Vsa()
     ms_step, ms, stats = time_stages((("tile", w.tile), ("route", w.route), ("attn", w.attend)), args, w.stream)
     rb = w.route_bytes()
-    roof = _roofline_mfma("vsa4_kernel (bsa_forward_qouter, block mode)", w.valid_flops(), w.nominal_flops(),
-                          ms["attn"], _profiled_traffic("vsa4_kernel_video.md", ATTN_SOURCES))
+    roof = _roofline_mfma(ATTN_KERNEL + " (bsa_forward_qouter, block mode)", w.valid_flops(), w.nominal_flops(),
+                          ms["attn"], _profiled_traffic(ATTN_KERNEL + "_video.md", ATTN_SOURCES))
     res = _line(args, w.nominal_flops() / (ms_step * 1e-3) / 1e12, ms_step, w.config("video_dit_vsa"), DATA_VIDEO,
                 ms, stats, roof,
                 {"pct_bf16_peak_attn_valid": round(100 * roof["frac"], 2),
@@ -442,7 +444,7 @@ def bench_coarse(args):
     # softmax(E) V_bar of every head (2*J*J*D multiply-adds)
     coarse_flops = 2.0 * B * h * J * J * D
     coarse_bytes = (v.numel() * v.element_size() + B * h * J * D * 4) + (w.E.numel() * 4 + 2 * B * h * J * D * 4)
-    roof = _roofline_mfma("vsa4_kernel with the coarse epilogue (bsa_forward_qouter, block mode)", w.valid_flops(),
+    roof = _roofline_mfma(ATTN_KERNEL + " with the coarse epilogue (bsa_forward_qouter, block mode)", w.valid_flops(),
                           w.nominal_flops(), ms["attn"], _profiled_traffic("coarse_kernel_video.md", ATTN_SOURCES))
     data = "synthetic (seeded N(0,1) + per-cell offsets, seeded N(0, 0.25) gate; no dataset or weights)"
     res = _line(args, (w.nominal_flops() + coarse_flops) / (ms_step * 1e-3) / 1e12, ms_step,
@@ -544,8 +546,8 @@ def bench_h3(args):
     flops = 4.0 * D * M * M * pairs_nominal              # every pair counted as full blocks
     valid_flops = 4.0 * D * bsa.metrics.vsa_valid_pairs(geom.block_len, q2k_idx, q2k_num)
     route_bytes = 2 * q.numel() * q.element_size() + 2 * B * h * J * D * 4 + 4 * pairs_nominal
-    roof = _roofline_mfma("vsa4_kernel over the grouped index table (bsa_forward_qouter, block mode)", valid_flops,
-                          flops, ms["attn"], _profiled_traffic("vsa4_kernel_h3.md", ATTN_SOURCES))
+    roof = _roofline_mfma(ATTN_KERNEL + " over the grouped index table (bsa_forward_qouter, block mode)", valid_flops,
+                          flops, ms["attn"], _profiled_traffic(ATTN_KERNEL + "_h3.md", ATTN_SOURCES))
     config = {"workload": "h3_r2v_multi_region", "B": B, "heads": h,
               "segments": [s_ if isinstance(s_, int) else list(s_) for s_ in cfg["segments"]],
               "block": list(cfg["block"]), "D": D, "J": J, "M": M, "tokens": N, "prefix_blocks": P,
@@ -651,8 +653,8 @@ def bench_reblock(args):
     ms_step, ms, stats = time_stages((("reblock", reblock), ("route", route), ("attn", attend)), args, stream)
     flops = 4.0 * B * h * N * D * R * M
     valid = 4.0 * D * bsa.metrics.vsa_valid_pairs(block_len, q2k_idx, q2k_num)
-    roof = _roofline_mfma("vsa4_kernel over per-head reblocked tables (bsa_forward_qouter, block mode)", valid, flops,
-                          ms["attn"], _profiled_traffic("vsa4_kernel_reblock.md", ATTN_SOURCES))
+    roof = _roofline_mfma(ATTN_KERNEL + " over per-head reblocked tables (bsa_forward_qouter, block mode)", valid, flops,
+                          ms["attn"], _profiled_traffic(ATTN_KERNEL + "_reblock.md", ATTN_SOURCES))
     config = {"workload": "video_dit_vsa_spark_reblock", "B": B, "heads": h, "grid": list(cfg["grid"]),
               "D": D, "J": J, "M": M, "R": R, "tokens": N, "tree_levels": nl.value}
     res = _line(args, flops / (ms_step * 1e-3) / 1e12, ms_step, config, DATA_VIDEO, ms, stats, roof)

@@ -519,17 +519,22 @@ __device__ __forceinline__ Cohort cohort_register(SchedState* st, uint32_t* sh) 
   return c;
 }
 
-// Arrive after a query block and wait (bounded) for the cohort's other
-// members, counting those that have already run out of work.
-__device__ __forceinline__ void cohort_sync(SchedState* st, Cohort& c) {
-  if (threadIdx.x == 0 && c.round < kMaxRounds) {
-    uint32_t* ctr = &st->xcd_rounds[c.xcc * kMaxRounds + c.round];
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int t = 0; t < 4096; ++t) {
-      if (load_relaxed(ctr) + load_relaxed(&st->xcd_exited[c.xcc]) >= c.members) break;
-      __builtin_amdgcn_s_sleep(8);
-    }
+// Arrive at the end of round c.round and wait (bounded) for the cohort's
+// other members, counting those that have already run out of work (called by
+// one lane of the workgroup).
+__device__ __forceinline__ void cohort_arrive_wait(SchedState* st, const Cohort& c) {
+  if (c.round >= kMaxRounds) return;
+  uint32_t* ctr = &st->xcd_rounds[c.xcc * kMaxRounds + c.round];
+  __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int t = 0; t < 4096; ++t) {
+    if (load_relaxed(ctr) + load_relaxed(&st->xcd_exited[c.xcc]) >= c.members) break;
+    __builtin_amdgcn_s_sleep(8);
   }
+}
+
+// Arrive after a query block and wait for the cohort (whole workgroup).
+__device__ __forceinline__ void cohort_sync(SchedState* st, Cohort& c) {
+  if (threadIdx.x == 0) cohort_arrive_wait(st, c);
   ++c.round;
   __syncthreads();
 }
@@ -1051,6 +1056,402 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ============================================================================
+// 64-row blocks, ping-pong schedule.  One 8-wave workgroup per CU works on two
+// query blocks at a time, one per group of four waves; inside a group the
+// waves take the roles of the four-wave kernel (query half hq, key half g).
+// Each step of a group is either a matrix phase M_t (PV of kept block t-1,
+// then S^T = K Q^T of kept block t) or a vector phase S_t (the online softmax
+// of block t, plus the copies of later blocks).  The two groups run half a
+// step apart with one workgroup barrier per phase, so while one group's waves
+// run their softmax the other group's waves -- on the same SIMDs -- keep the
+// matrix cores busy (the SIMD arbiter issues VALU work of one wave during the
+// matrix operations of another).
+//
+// Phases of one query block with T kept blocks:
+//   L0 (S)  take the item, query rows, token ids of blocks 0, 1, 2
+//   L1 (M)  copies of K(0), V(0), K(1)
+//   L2 (S)  (the first copies land)
+//   M_0, S_0, M_1, S_1, ..., M_{T-1}, S_{T-1}, M_T
+//   E0 (S)  key half 1 hands its partial state to key half 0 through LDS
+//   E1 (M)  key half 0 merges, normalises and stores; the next item is taken
+// S_s issues, in this order, the token ids of block s+3 and the copies of
+// K(s+2) and V(s+1) (entries past the list repeat its last block: harmless
+// copies into free buffers).  K(t) lives in Kbuf[t & 1], V(t) in Vbuf[t & 1],
+// the ids of block t in slot t & 3 of the wave's id ring.  Before M_s every
+// batch but the last has landed, before S_s the ids at the head of the last.
+// ============================================================================
+// The next work item of the XCD's chunk queue for one group (called by one
+// lane; -1 when everything is taken).
+__device__ __forceinline__ int pp_next_item(SchedState* st, uint32_t x, int items) {
+  for (uint32_t y = 0; y < (uint32_t)kXcds; ++y) {
+    const uint32_t xx = (x + y) % kXcds;
+    if (xcd_item(xx, load_relaxed(&st->xq[xx]), items) < 0) continue;
+    const int it = xcd_item(xx, __hip_atomic_fetch_add(&st->xq[xx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                            items);
+    if (it >= 0) return it;
+  }
+  return -1;
+}
+
+template <int D, bool LSE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void vsa_pp_kernel(VsaAttnParams p,
+                                                                                              int items) {
+  using TM = Tile4<D>;
+  constexpr int LPT = TM::LPT, CPR = TM::CPR;
+  constexpr int KS = D / 16;    // k-steps of QK^T
+  constexpr int DT = D / 32;    // 32-channel tiles of O
+  constexpr int NP = 2 * DT;    // PV products
+  constexpr int TILE = 64 * D;  // elements of one K or V tile
+  constexpr int M = 64;
+  constexpr int PF = 2;         // operand prefetch distance (products)
+  // per group: Kbuf[0], Kbuf[1], Vbuf[0], Vbuf[1]
+  __shared__ __align__(1024) __bf16 KV[2 * 4 * TILE];
+  __shared__ __align__(256) int Ids[8 * 4 * 64];  // per wave: a ring of 4 token-id slots
+  __shared__ float Mx[2 * 2 * 3 * 64];            // per group and query half: m, l, lx of key half 1
+  __shared__ int item_sh[2];                      // next item of each group
+  __shared__ int done_at[2];                      // barrier count at which each group ran out of items
+  __shared__ uint32_t coh_sh[2];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wv >> 2, ww = wv & 3;
+  const int hq = ww >> 1, g = ww & 1, h2 = lane >> 5;
+  const bool lead = ww == 0 && lane == 0;
+  SchedState* st = reinterpret_cast<SchedState*>(p.sched);
+  const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (15 << 11)) & (kXcds - 1);  // XCC_ID
+
+  __bf16* KVg = KV + grp * 4 * TILE;
+  const uint32_t kv_lds = lds_offset(KVg);
+  auto kbuf = [&](int x) { return kv_lds + (uint32_t)(x * TILE * 2); };
+  auto vbuf = [&](int x) { return kv_lds + (uint32_t)((2 + x) * TILE * 2); };
+  int* ring = Ids + wv * 4 * 64;
+  auto ring_lds = [&](int slot) { return lds_offset(ring + slot * 64); };
+  const int krow = 32 * g + (lane & 31);
+  const int qrow = 32 * hq + (lane & 31);
+  const uint32_t row_bytes = (uint32_t)(p.kv_sN * 2);
+  const uint32_t slice_bytes = (uint32_t)((p.N - 1) * p.kv_sN * 2 + D * 2);
+  const auto blen = as_const(p.block_len);
+
+  // per-lane swizzled chunk offsets of the copies
+  uint32_t koff[LPT], voff[LPT];
+#pragma unroll
+  for (int k = 0; k < LPT; ++k) {
+    const int r = TM::row(k, ww, lane), pc = lane % CPR;
+    koff[k] = (uint32_t)k_swz<CPR>(r, pc) * 16;
+    voff[k] = (uint32_t)v_swz<CPR>(r, pc) * 16;
+  }
+  // byte offset (from Vbuf[0]) of this lane's V transposing reads, per 32-channel tile
+  uint32_t vtr[DT];
+  {
+    const int g16 = lane >> 4, jl = lane & 15;
+    const int r0 = 32 * g + 4 * h2 + (jl >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + 16 * (g16 & 1) + 4 * (jl & 3);
+      const int c = d >> 3, off = d & 7;
+      vtr[dt] = vbuf(0) + (uint32_t)((r0 * D + v_swz<CPR>(r0, c) * 8 + off) * 2);
+    }
+  }
+
+  // Group 0 of every workgroup of an XCD starts its items together with the
+  // others (bounded wait), and group 1 follows its group 0 one phase later, so
+  // the XCD's query blocks walk their sorted block lists in step and share
+  // the head's K/V window in L2.
+  const bool sync = p.sched != nullptr;
+  Cohort coh;
+  if (sync) coh = cohort_register(st, coh_sh);
+  if (threadIdx.x == 0 || threadIdx.x == 256) {
+    item_sh[grp] = p.sched ? pp_next_item(st, xcc, items) : (int)(2 * blockIdx.x + grp);
+    done_at[grp] = 0x7fffffff;
+  }
+  __syncthreads();
+
+  // Every phase opens with one workgroup barrier; both groups pass the same
+  // number of them, group 1 one phase behind group 0, so that the matrix
+  // phases of one group meet the vector phases of the other.
+  int q = 0;
+  auto phase = [&]() {
+    BSA_BARRIER();
+    ++q;
+  };
+  if (grp == 1) phase();
+
+  for (;;) {
+    // ---------------- L0: take the item, load the query rows, stage ids ----------------
+    phase();
+    const int wid = __builtin_amdgcn_readfirstlane(item_sh[grp]);
+    if (wid < 0 || wid >= items) {
+      if (lead) {
+        done_at[grp] = q;
+        if (sync && grp == 0)
+          __hip_atomic_fetch_add(&st->xcd_exited[coh.xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      break;
+    }
+    int i = item_block(p, wid);
+    const bool out_ok = i >= 0;
+    if (!out_ok) i = 0;
+    const int64_t bh = wid / p.J;
+    const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
+    const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
+    const __bf16* qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
+    const i32x4 krs = make_rsrc(reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + hh * p.kv_sH, slice_bytes);
+    const i32x4 vrs = make_rsrc(reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + hh * p.kv_sH, slice_bytes);
+    const i32x4 prs = make_rsrc(perm, (uint32_t)p.J * (uint32_t)M * 4u);
+    const auto sel = as_const(p.q2k_idx) + (bh * p.J + i) * p.kmax;
+    const int T = out_ok ? min(as_const(p.q2k_num)[bh * p.J + i], p.kmax) : 0;
+    const int ni = blen[i];
+    const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
+    bf16x8 qop[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qop[k] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * k + 8 * h2);
+    bool bad = false;
+    int j0 = 0, ja = 0, jb = 0, jc = 0;
+    if (T > 0) {
+      j0 = kept_id(sel, 0, p.J, bad);
+      ja = kept_id(sel, min(1, T - 1), p.J, bad);
+      jb = kept_id(sel, min(2, T - 1), p.J, bad);
+      jc = kept_id(sel, min(3, T - 1), p.J, bad);
+      stage_ids(prs, max(j0, 0), M, ring_lds(0), lane);
+      stage_ids(prs, max(ja, 0), M, ring_lds(1), lane);
+      stage_ids(prs, max(jb, 0), M, ring_lds(2), lane);
+    }
+
+    // ---------------- L1: copies of K(0), V(0), K(1) ----------------
+    wait_vmcnt<0>();  // query rows and ids have landed
+    phase();
+#pragma unroll
+    for (int k = 0; k < KS; ++k) asm volatile("" ::"v"(qop[k]));
+    uint32_t rows_next[LPT];  // rows of the block whose V copy is next
+    int nj = 0;
+    if (T > 0) {
+      uint32_t rows[LPT];
+      nj = (j0 >= 0) ? blen[j0] : 0;
+      tile_rows4<D>(rows, ring + 0 * 64, ww, lane, row_bytes);
+      stage4<D>(krs, kbuf(0), rows, koff, ww);
+      stage4<D>(vrs, vbuf(0), rows, voff, ww);
+      tile_rows4<D>(rows_next, ring + 1 * 64, ww, lane, row_bytes);
+      stage4<D>(krs, kbuf(1), rows_next, koff, ww);
+    }
+
+    // ---------------- L2: the first copies land ----------------
+    phase();
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, lx_run = 0.f;
+    f32x16 sacc;
+    bf16x8 pop[2];
+    // S^T = K(s) Q^T for the key half of this wave
+    auto qk = [&](int s) {
+      const __bf16* Kc = KVg + (s & 1) * TILE;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      bf16x8 ka[KS];
+#pragma unroll
+      for (int x = 0; x < KS + PF; ++x) {
+        if (x < KS) {
+          ka[x] = *reinterpret_cast<const bf16x8*>(Kc + krow * D + k_swz<CPR>(krow, 2 * x + h2) * 8);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        if (x >= PF) {
+          sacc = mfma32(ka[x - PF], qop[x - PF], sacc);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        }
+      }
+    };
+
+    // ---------------- M_0: S^T of block 0 ----------------
+    wait_vmcnt<2 * LPT>();  // K(0) of the prologue batch K(0), V(0), K(1)
+    phase();
+    if (T > 0) qk(0);
+    for (int s = 0; s < T; ++s) {
+      // ---------------- S_s: copies for later blocks, softmax of block s ----------------
+      wait_vmcnt<2 * LPT>();  // the ids at the head of the last batch (own copies only)
+      phase();
+      {
+        // batch: ids(s+3), K(s+2) with the rows of block s+2, V(s+1) with those of s+1
+        stage_ids(prs, max(jc, 0), M, ring_lds((s + 3) & 3), lane);
+        uint32_t rows[LPT];
+        tile_rows4<D>(rows, ring + ((s + 2) & 3) * 64, ww, lane, row_bytes);
+        stage4<D>(krs, kbuf(s & 1), rows, koff, ww);
+        stage4<D>(vrs, vbuf((s + 1) & 1), rows_next, voff, ww);
+#pragma unroll
+        for (int k = 0; k < LPT; ++k) rows_next[k] = rows[k];
+      }
+      // scalar reads for the coming steps: the block after the ids just staged,
+      // and the true length of the next block
+      __builtin_amdgcn_sched_barrier(0);
+      const int jd = kept_id(sel, min(s + 4, T - 1), p.J, bad);
+      const int njn = (ja >= 0) ? blen[max(ja, 0)] : 0;
+      __builtin_amdgcn_sched_barrier(0);
+
+      if (nj < M) {  // edge / short block: mask keys at or beyond its true length
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
+          sacc[r] = (key < nj) ? sacc[r] : -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+      // lazy rescale (as in the four-wave kernel): the reference moves only
+      // when some row's maximum grew by more than 8 in log2 units
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        if constexpr (LSE) lx_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float rs = 0.f, rsx = 0.f;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * hlf + 2 * e;
+          const float a = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -m_use));
+          const float c = fast_exp2(__builtin_fmaf(sacc[r + 1], p.scale_log2, -m_use));
+          pk[e] = pack2_bf16_sum<LSE>(a, c, &rs, &rsx);
+        }
+        pop[hlf] = __builtin_bit_cast(bf16x8, pk);
+      }
+      l_run += rs;
+      if constexpr (LSE) lx_run += rsx;
+      nj = njn;
+      ja = jb;
+      jb = jc;
+      jc = jd;
+
+      // The probabilities must be formed in this phase: left to itself the
+      // compiler sinks the exponentials past the barrier, next to their use.
+      asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(l_run), "v"(lx_run));
+
+      // ---------------- M_{s+1}: PV(s), then S^T of block s+1 ----------------
+      wait_vmcnt<2 * LPT + 1>();  // every batch but the last one
+      phase();
+      {
+        const uint32_t vb = (s & 1) ? (uint32_t)(TILE * 2) : 0u;
+        bf16x8 va[NP];
+#pragma unroll
+        for (int x = 0; x < NP + PF; ++x) {
+          if (x < NP) {
+            const int u = x / DT, dt = x % DT;
+            // rows r0 + 16u and r0 + 16u + 8 keep r0's swizzle (same row % 4)
+            const uint32_t a = vtr[dt] + vb + (uint32_t)(16 * u * D * 2);
+            const bf16x4 lo = lds_read_tr16_at(a);
+            const bf16x4 hi = lds_read_tr16_at(a + (uint32_t)(8 * D * 2));
+            va[x] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          }
+          if (x >= PF) {
+            const int y = x - PF;
+            oacc[y % DT] = mfma32(va[y], pop[y / DT], oacc[y % DT]);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < T) qk(s + 1);
+    }
+
+    // ---------------- E0: key half 1 hands its state to key half 0 ----------------
+    wait_vmcnt<0>();  // the last (repeat) copies have landed in this group's buffers
+    phase();
+    if (bad) flag_index_error(p.err);
+    float* scr = reinterpret_cast<float*>(KVg) + hq * (64 * DT * 16);
+    float* mxs = Mx + (grp * 2 + hq) * 3 * 64;
+    if (g == 1 && out_ok) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 v = {oacc[d][4 * c4], oacc[d][4 * c4 + 1], oacc[d][4 * c4 + 2], oacc[d][4 * c4 + 3]};
+          *reinterpret_cast<f32x4*>(scr + ((d * 4 + c4) * 64 + lane) * 4) = v;
+        }
+      mxs[lane] = m_run;
+      mxs[64 + lane] = l_run;
+      mxs[128 + lane] = lx_run;
+    }
+
+    // ---------------- E1: merge, normalise, store; take the next item ----------------
+    phase();
+    if (g == 0 && out_ok) {
+      const float mb = mxs[lane], lb = mxs[64 + lane], lxb = mxs[128 + lane];
+      const float m = fmaxf(m_run, mb);
+      const float fa = (m == -INFINITY) ? 0.f : fast_exp2(m_run - m);
+      const float fb = (m == -INFINITY) ? 0.f : fast_exp2(mb - m);
+      const float l_part = fa * l_run + fb * lb;
+      const float l_tot = l_part + xor32(l_part);
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      __bf16* __restrict__ og = reinterpret_cast<__bf16*>(p.o) + b * p.o_sB + (int64_t)qtok * p.o_sN + hh * p.o_sH;
+      // one 32-channel tile at a time: merge with key half 1, normalise, store
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(scr + ((d * 4 + c4) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[d][4 * c4 + e] = fa * oacc[d][4 * c4 + e] + fb * v[e];
+        }
+        if (qrow < ni) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int dd = 32 * d + 8 * jj + 4 * h2;
+            const f32x4 cg = coarse_term(p, bh, hh, i, dd);
+            bf16x4 v4 = {(__bf16)fmaf(oacc[d][4 * jj + 0], inv, cg[0]), (__bf16)fmaf(oacc[d][4 * jj + 1], inv, cg[1]),
+                         (__bf16)fmaf(oacc[d][4 * jj + 2], inv, cg[2]), (__bf16)fmaf(oacc[d][4 * jj + 3], inv, cg[3])};
+            *reinterpret_cast<bf16x4*>(og + dd) = v4;
+          }
+        }
+      }
+      if constexpr (LSE) {
+        const float lx_part = fa * lx_run + fb * lxb;
+        const float lx = lx_part + xor32(lx_part);
+        if (qrow < ni && h2 == 0) p.lse[bh * p.N + qtok] = (lx > 0.f) ? (m + __log2f(lx)) * kLn2 : -INFINITY;
+      }
+    }
+    if (lead) item_sh[grp] = p.sched ? pp_next_item(st, xcc, items) : item_sh[grp] + 2 * (int)gridDim.x;
+    if (sync && grp == 0) {
+      if (lead) cohort_arrive_wait(st, coh);
+      ++coh.round;
+    }
+  }
+
+  // Out of items: keep passing barriers until the other group is out too; a
+  // count recorded in a phase is read only after the next barrier.
+  for (;;) {
+    phase();
+    if (done_at[0] < q && done_at[1] < q) break;
+  }
+}
+
+template <int D, bool LSE>
+static hipError_t launch_vsa_pp(const VsaAttnParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.B * p.H * p.J;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    cus = 256;
+  const int64_t grid = std::min<int64_t>((items + 1) / 2, cus);
+  if (p.sched) clear_sched_kernel<<<64, 256, 0, s>>>(reinterpret_cast<SchedState*>(p.sched));
+  vsa_pp_kernel<D, LSE><<<dim3((unsigned)grid), dim3(512), 0, s>>>(p, (int)items);
+  return hipGetLastError();
+}
+
+// ============================================================================
 // float32 inputs: exact fp32 attention on the vector ALUs (teaching-size
 // problems).  One workgroup per query block, two lanes per query row, each lane
 // owning half of the channels; K and V tiles of the kept block are staged in
@@ -1172,7 +1573,7 @@ template <int D>
 static hipError_t launch_vsa_d(const VsaAttnParams& p, hipStream_t s) {
   if (p.M <= 32) return launch_vsa_mt<D, 32>(p, s);
   if (p.k_sum) return p.lse ? launch_vsa4<D, true, true>(p, s) : launch_vsa4<D, false, true>(p, s);
-  return p.lse ? launch_vsa4<D, true, false>(p, s) : launch_vsa4<D, false, false>(p, s);
+  return p.lse ? launch_vsa_pp<D, true>(p, s) : launch_vsa_pp<D, false>(p, s);
 }
 
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s) {

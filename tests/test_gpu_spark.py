@@ -111,8 +111,10 @@ def test_exact_at_anchor_end_to_end():
 
 
 def test_all_blocks_kept_equals_plain_path():
-    """Rows that keep every block add no virtual token: identical to the plain
-    kernel bit for bit."""
+    """Rows that keep every block add no virtual token: the summary path gives
+    the plain path's result.  The two run different kernels (their sums are
+    ordered differently), so both must match dense attention within the
+    attention tolerance and each other within two bf16 rounding steps."""
     cfg = scaled("video", grid=(8, 16, 16), h=2, R=4)
     geom, tab, x = _setup(cfg)
     B, N, h, D = x["q"].shape
@@ -123,7 +125,13 @@ def test_all_blocks_kept_equals_plain_path():
     o1 = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num, summaries=summ)
     o2 = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
+    Q, K, V = to64(x["q"]), to64(x["k"]), to64(x["v"])
+    dense, _ = oracle.vsa_attention(Q, K, V, tab["perm"], tab["block_len"], tab["M"], idx.cpu().numpy(),
+                                    num.cpu().numpy())
+    assert_attn_close(o1, dense, "summaries, every block kept")
+    assert_attn_close(o2, dense, "plain, every block kept")
+    a, b = o1.float(), o2.float()
+    assert bool(((a - b).abs() <= 2.0 ** -6 * b.abs() + 2.0 ** -20).all())
 
 
 def test_summary_argument_errors():

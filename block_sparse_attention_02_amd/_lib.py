@@ -102,6 +102,13 @@ class KvOuterArgs(ctypes.Structure):
                 ("o_buf", _p), ("lse_buf", _p), ("nslot", _p), ("chunk_cap", _i32)]
 
 
+class KvOuterLayout(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("max_edges", ctypes.c_int64), ("max_chunks", ctypes.c_int64),
+                ("chunk_cap", ctypes.c_int64), ("off_count", ctypes.c_size_t), ("off_rowptr", ctypes.c_size_t),
+                ("off_nchunk", ctypes.c_size_t), ("off_chunks", ctypes.c_size_t), ("off_edges", ctypes.c_size_t),
+                ("bytes", ctypes.c_size_t)]
+
+
 class CombineArgs(ctypes.Structure):
     _fields_ = [("o_buf", _p), ("lse_buf", _p), ("nslot", _p), ("k_sel", _i32), ("Hkv", _i32),
                 ("dout", TDesc), ("out", _p), ("lse", _p)]
@@ -133,6 +140,7 @@ PROTOTYPES = {
     "spark_summaries": (_i32, [ctypes.POINTER(SummaryArgs), _p, ctypes.c_size_t, _p]),
     "bsa_kvouter_ws": (_i32, [ctypes.POINTER(KvOuterArgs), ctypes.POINTER(ctypes.c_size_t)]),
     "bsa_forward_kvouter": (_i32, [ctypes.POINTER(KvOuterArgs), _p, ctypes.c_size_t, _p]),
+    "bsa_kvouter_index_layout": (_i32, [ctypes.POINTER(KvOuterArgs), ctypes.POINTER(KvOuterLayout)]),
     "bsa_combine": (_i32, [ctypes.POINTER(CombineArgs), _p]),
 }
 

@@ -319,8 +319,15 @@ def _kv_args(q, k, v, q2k, block_size, causal, q2k_cnt, scale, chunk_cap, o_buf,
 
 
 def kvouter(q, k, v, q2k, block_size, causal=True, q2k_cnt=None, scale=None, chunk_cap=0,
-            workspace=None, bufs=None):
-    """KV-outer K1: returns (o_buf [B,ks,N,Hq,D] bf16, lse_buf [B,ks,N,Hq], nslot [B,N,Hkv])."""
+            workspace=None, bufs=None, index=False):
+    """KV-outer K1: returns (o_buf [B,ks,N,Hq,D] bf16, lse_buf [B,ks,N,Hq], nslot [B,N,Hkv]).
+
+    With ``index=True`` a fourth item holds the reverse index and schedule the
+    call left in its workspace (int32 views into it, valid until the
+    workspace is reused): count [rows], rowptr [rows + 1], nchunk [1],
+    chunks [max_chunks, 4] (the first nchunk are set), edges [max_edges, 2]
+    (the first rowptr[rows] are set), plus rows and chunk_cap.
+    """
     _need_cuda(q, k, v, q2k, q2k_cnt)
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -339,7 +346,24 @@ def kvouter(q, k, v, q2k, block_size, causal=True, q2k_cnt=None, scale=None, chu
     if workspace is None or workspace.numel() < n.value:
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     L.check(_lib().bsa_forward_kvouter(ctypes.byref(a), _ptr(workspace), n.value, _stream(dev)))
-    return o_buf, lse_buf, nslot
+    if not index:
+        return o_buf, lse_buf, nslot
+    lay = L.KvOuterLayout()
+    L.check(_lib().bsa_kvouter_index_layout(ctypes.byref(a), ctypes.byref(lay)))
+
+    def region(off, n_int32):
+        return workspace[off:off + 4 * n_int32].view(torch.int32)
+
+    views = {
+        "rows": lay.rows,
+        "chunk_cap": lay.chunk_cap,
+        "count": region(lay.off_count, lay.rows),
+        "rowptr": region(lay.off_rowptr, lay.rows + 1),
+        "nchunk": region(lay.off_nchunk, 1),
+        "chunks": region(lay.off_chunks, 4 * lay.max_chunks).view(lay.max_chunks, 4),
+        "edges": region(lay.off_edges, 2 * lay.max_edges).view(lay.max_edges, 2),
+    }
+    return o_buf, lse_buf, nslot, views
 
 
 def combine(o_buf, lse_buf, nslot, Hkv, need_lse=False, out=None):

@@ -9,6 +9,11 @@
 #include "bsa.h"
 #include "bsa_internal.hpp"
 
+namespace bsa {
+// Defined beside the KV-outer kernels, which own the workspace layout.
+void kvouter_index_layout(const KvOuterParams& p, bsa_kvouter_layout* out);
+}  // namespace bsa
+
 namespace {
 
 thread_local std::string g_err;
@@ -793,6 +798,15 @@ bsa_status bsa_kvouter_ws(const bsa_kvouter_args* a, size_t* bytes) {
   bsa_status st = check_kvouter(a, &p);
   if (st != BSA_OK) return st;
   *bytes = bsa::kvouter_ws_bytes(p);
+  return ok();
+}
+
+bsa_status bsa_kvouter_index_layout(const bsa_kvouter_args* a, bsa_kvouter_layout* out) {
+  if (!out) return fail(BSA_ERR_ARG, "bsa_kvouter_index_layout: null output");
+  bsa::KvOuterParams p{};
+  bsa_status st = check_kvouter(a, &p);
+  if (st != BSA_OK) return st;
+  bsa::kvouter_index_layout(p, out);
   return ok();
 }
 

@@ -18,6 +18,7 @@
 // (ties by position), which also fixes the summation order of the combine.
 #include <algorithm>
 
+#include "bsa.h"
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -65,6 +66,14 @@ KvLayout kv_layout(const KvOuterParams& p) {
 }  // namespace
 
 size_t kvouter_ws_bytes(const KvOuterParams& p) { return kv_layout(p).total; }
+
+// Offsets of the reverse index and chunk list inside the workspace, for
+// bsa_kvouter_index_layout.
+void kvouter_index_layout(const KvOuterParams& p, bsa_kvouter_layout* out) {
+  const KvLayout L = kv_layout(p);
+  *out = bsa_kvouter_layout{L.rows,      L.emax,       L.max_chunks, kv_chunk_cap(p), L.off_count,
+                            L.off_rowptr, L.off_nchunk, L.off_chunks, L.off_edges,     L.total};
+}
 
 // ----------------------------------------------------------------------------
 __global__ void kv_clear_kernel(int32_t* __restrict__ a, int32_t* __restrict__ b, int n) {

@@ -22,7 +22,8 @@
  * Memory.   Every array argument is device memory owned by the caller.  The
  *           library never allocates: calls that need scratch take a
  *           caller-supplied workspace whose size comes from the matching *_ws
- *           query (contents undefined after the call).  Calls that share a
+ *           query (contents undefined after the call, except the regions
+ *           bsa_kvouter_index_layout describes).  Calls that share a
  *           workspace must be ordered on one stream; calls with their own
  *           workspaces may run concurrently on different streams.  The only
  *           state the library keeps is one sticky index-error flag per device
@@ -523,6 +524,36 @@ typedef struct {
 
 bsa_status bsa_kvouter_ws(const bsa_kvouter_args* a, size_t* bytes);
 bsa_status bsa_forward_kvouter(const bsa_kvouter_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Where bsa_forward_kvouter leaves the reverse index and the schedule of steps
+ * 1 and 2 inside its workspace ([MSA] section 5: the q2k -> k2q CSR; section 7:
+ * the chunk list).  Unlike the rest of the workspace, these regions hold, after
+ * the call and until the workspace is reused, with rows = B * Hkv * NB,
+ * NB = ceil(N / BK), reverse rows in (b, r, block) order:
+ *   count  int32 [rows]        edges per reverse row;
+ *   rowptr int32 [rows + 1]    exclusive prefix sum of count;
+ *   nchunk int32 [1]           number of chunks;
+ *   chunks int32x4 [nchunk]    {row, begin, end, 0}: a run of at most
+ *                              chunk_cap edges of one row, rows in order;
+ *   edges  int32x2 [rowptr[rows]]  {query position i, slot s}, each row's
+ *                              edges between rowptr[row] and rowptr[row + 1]
+ *                              in an unspecified order.
+ * A block entirely after position i (block * BK > i) under the causal rule
+ * keeps its slot but has no edge.  Offsets are in bytes from the workspace
+ * start (each 256-byte aligned); `bytes` equals bsa_kvouter_ws; chunk_cap is
+ * the effective cap (the argument's, or its default, bounded by max_edges).
+ * Same validation and errors as bsa_kvouter_ws.  For inspection and tests of
+ * the schedule; the call reads no device memory. */
+typedef struct {
+  int64_t rows;        /* reverse-index rows B * Hkv * NB */
+  int64_t max_edges;   /* B * N * Hkv * k_sel */
+  int64_t max_chunks;  /* bound on nchunk */
+  int64_t chunk_cap;
+  size_t off_count, off_rowptr, off_nchunk, off_chunks, off_edges;
+  size_t bytes;
+} bsa_kvouter_layout;
+
+bsa_status bsa_kvouter_index_layout(const bsa_kvouter_args* a, bsa_kvouter_layout* out);
 
 typedef struct {
   const void* o_buf;

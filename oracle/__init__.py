@@ -20,7 +20,11 @@ it is written directly from the source pages:
   hierarchical split.
 
 Every function computes the plain definition in float64 with NumPy: no online
-softmax, no blocking, no reverse index.  Each one is pinned by the ``not gpu``
+softmax, no blocking, no reverse index.  The one exception is
+``kv_schedule``: a plain host C++ reference of the KV-outer reverse index and
+scheduler (integer work, built with g++; the tests compare the library's index
+with it exactly and run its brute-force checker under the address and
+undefined-behaviour sanitizers).  Each one is pinned by the ``not gpu``
 tests in ``tests/test_oracle_*.py`` against values printed on the pages,
 closed forms, brute force and library routines.
 """

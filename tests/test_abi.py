@@ -307,6 +307,27 @@ def test_kvouter_workspace_and_chunk_cap_bound():
                                    None) == L.BSA_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("cap,eff", [(0, 2 * 4 * 128), (3, 3), (5000, 256 * 2 * 4), (2 ** 31 - 1, 256 * 2 * 4)])
+def test_kvouter_index_layout(cap, eff):
+    """The reverse index and schedule regions lie inside the workspace, do not
+    overlap, are 256-byte aligned and have the sizes the header states."""
+    lib = L.load()
+    a = _kv_args(chunk_cap=cap)
+    lay, n = L.KvOuterLayout(), ctypes.c_size_t()
+    assert lib.bsa_kvouter_index_layout(ctypes.byref(a), ctypes.byref(lay)) == L.BSA_OK
+    assert lib.bsa_kvouter_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    rows, emax = 1 * 2 * 2, 256 * 2 * 4     # B * Hkv * ceil(256 / 128), B * N * Hkv * k_sel
+    assert (lay.rows, lay.max_edges, lay.chunk_cap, lay.bytes) == (rows, emax, eff, n.value)
+    assert lay.max_chunks == rows + -(-emax // eff)
+    spans = sorted([(lay.off_count, 4 * rows), (lay.off_rowptr, 4 * (rows + 1)), (lay.off_nchunk, 4),
+                    (lay.off_chunks, 16 * lay.max_chunks), (lay.off_edges, 8 * emax)])
+    for (o0, n0), (o1, _) in zip(spans, spans[1:]):
+        assert o0 + n0 <= o1
+    assert all(o % 256 == 0 for o, _ in spans) and spans[-1][0] + spans[-1][1] <= lay.bytes
+    assert lib.bsa_kvouter_index_layout(ctypes.byref(a), None) == L.BSA_ERR_ARG
+    assert lib.bsa_kvouter_index_layout(ctypes.byref(_kv_args(k_sel=0)), ctypes.byref(lay)) == L.BSA_ERR_UNSUPPORTED
+
+
 def _combine_args(**kw):
     ph = ctypes.c_void_p(256)
     d = L.TDesc(1, 256, 8, 128, 256 * 8 * 128, 8 * 128, 128)

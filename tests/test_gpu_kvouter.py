@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import kv_schedule
 from gpu_util import assert_attn_close, to64
 from workloads import msa_inputs, nsa_inputs, scaled, workload
 
@@ -36,6 +37,86 @@ def _check_partials(q, k, v, q2k, BK, causal, cnt, o_buf, lse_buf, nslot, name):
     assert np.abs(got_l[fin] - r_l[fin]).max() <= 1e-3
     assert_attn_close(o_buf, np.nan_to_num(r_o), name + " partials", mask=np.broadcast_to(valid[..., None], r_o.shape))
     return r_o, r_l, r_n
+
+
+def _check_index(ix, q2k, BK, causal, cnt=None):
+    """The reverse index and schedule the library left in its workspace equal
+    the host reference's: counts, row pointers and chunks exactly, each row's
+    edges as a set (their order inside a row is unspecified)."""
+    ref = kv_schedule.reference(q2k.cpu().numpy(), BK, causal=causal,
+                                q2k_cnt=None if cnt is None else cnt.cpu().numpy(), cap=ix["chunk_cap"])
+    assert not ref["flagged"]
+    count, rowptr = ix["count"].cpu().numpy(), ix["rowptr"].cpu().numpy()
+    assert np.array_equal(count, ref["count"]), "counts differ"
+    assert np.array_equal(rowptr, ref["rowptr"]), "row pointers differ"
+    nchunk = int(ix["nchunk"].item())
+    assert nchunk == len(ref["chunks"])
+    assert np.array_equal(ix["chunks"][:nchunk].cpu().numpy(), ref["chunks"]), "chunks differ"
+    edges = ix["edges"][:int(rowptr[-1])].cpu().numpy()
+    rowid = np.repeat(np.arange(len(count)), count)
+    order = np.lexsort((edges[:, 1], edges[:, 0], rowid))
+    assert np.array_equal(edges[order], ref["edges"]), "edges differ"
+    return ref
+
+
+def _random_selection(B, N, Hkv, ks, BK, seed):
+    """Mostly visible blocks in any order, with -1 entries, duplicates and
+    blocks after the query; random counts."""
+    rng = np.random.default_rng(seed)
+    NB = -(-N // BK)
+    cur = (np.arange(N) // BK + 1)[None, :, None, None]
+    sel = np.floor(rng.random((B, N, Hkv, ks)) * cur).astype(np.int32)
+    u = rng.random(sel.shape)
+    sel[u < 0.1] = -1
+    fut = u > 0.9
+    sel[fut] = rng.integers(0, NB, int(fut.sum()))
+    dup = rng.random(sel.shape[:-1]) < 0.2
+    sel[..., 1][dup] = sel[..., 0][dup]
+    cnt = rng.integers(0, ks + 1, (B, N, Hkv)).astype(np.int32)
+    return sel, cnt
+
+
+def _bf16_inputs(B, N, Hq, Hkv, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return tuple(torch.randn(shape, generator=g).to(torch.bfloat16).to(DEV)
+                 for shape in ((B, N, Hq, D), (B, N, Hkv, D), (B, N, Hkv, D)))
+
+
+INDEX_CASES = {
+    # B, N, Hq, Hkv, D, BK, k, causal, cap, counts; oracle partials for small N
+    "dups_causal_counts_cap5": (2, 1000, 4, 2, 64, 64, 8, True, 5, True),
+    "noncausal_cap1": (1, 300, 2, 1, 128, 128, 4, False, 1, False),
+    # Hkv * NB = 8 * 1025 exceeds the 8192 bins of the LDS histogram: the
+    # global count / scatter kernels build the index
+    "global_count_scatter": (1, 65600, 8, 8, 64, 64, 2, True, 0, True),
+}
+
+
+@pytest.mark.parametrize("name", list(INDEX_CASES))
+def test_kvouter_index_matches_reference(name):
+    B, N, Hq, Hkv, D, BK, ks, causal, cap, with_cnt = INDEX_CASES[name]
+    print("case", name, flush=True)
+    q, k, v = _bf16_inputs(B, N, Hq, Hkv, D, seed=11)
+    sel, cnt = _random_selection(B, N, Hkv, ks, BK, seed=12)
+    q2k_d = torch.from_numpy(sel).to(DEV)
+    cnt_d = torch.from_numpy(cnt).to(DEV) if with_cnt else None
+    o_buf, lse_buf, nslot, ix = bsa.kvouter(q, k, v, q2k_d, BK, causal=causal, q2k_cnt=cnt_d, chunk_cap=cap,
+                                            index=True)
+    out = bsa.combine(o_buf, lse_buf, nslot, Hkv)
+    torch.cuda.synchronize()
+    bsa.check(DEV)
+    ref = _check_index(ix, q2k_d, BK, causal, cnt_d)
+    assert np.array_equal(nslot.cpu().numpy(), ref["nslot"])
+    if N <= 1000:
+        _check_partials(q, k, v, q2k_d, BK, causal, cnt_d, o_buf, lse_buf, nslot, name)
+    rng = np.random.default_rng(13)
+    pos = [(int(b), int(i)) for b, i in zip(rng.integers(0, B, 12), rng.integers(0, N, 12))] + [(0, 0), (B - 1, N - 1)]
+    ref_o, _ = oracle.nsa_attention(to64(q), to64(k), to64(v), sel, cnt if with_cnt else None, BK, causal=causal,
+                                    tokens=pos)
+    mask = np.zeros(ref_o.shape, dtype=bool)
+    for b, i in pos:
+        mask[b, i] = True
+    assert_attn_close(out, np.nan_to_num(ref_o), name + " combined (sampled)", mask=mask)
 
 
 CASES = {
@@ -126,9 +207,11 @@ def test_msa_full_size_sampled():
     cfg = workload("msa")
     print("case msa full size", flush=True)
     q, k, v, q2k = msa_inputs(cfg, device=DEV)
-    o_buf, lse_buf, nslot = bsa.kvouter(q, k, v, q2k, 128)
+    o_buf, lse_buf, nslot, ix = bsa.kvouter(q, k, v, q2k, 128, index=True)
     out = bsa.combine(o_buf, lse_buf, nslot, 4)
     torch.cuda.synchronize()
+    ref_ix = _check_index(ix, q2k, 128, True)      # the whole index, exactly
+    assert np.array_equal(nslot.cpu().numpy(), ref_ix["nslot"])
     rng = np.random.default_rng(5)
     pos = [(0, int(i)) for i in rng.integers(0, cfg["N"], 24)] + [(0, 0), (0, 127), (0, 128), (0, cfg["N"] - 1)]
     q64, k64, v64 = to64(q), to64(k), to64(v)

@@ -524,7 +524,8 @@ def bench_h3(args):
     ra = L.H3RouteArgs(q=Pp(q), k=Pp(k), d=bsa.api._desc(q), dt=L.BSA_BF16, perm=Pp(geom.perm),
                        block_len=Pp(geom.block_len), J=J, M=M, num_prefix=P, nregions=nr,
                        spans=ctypes.cast(spans, ctypes.c_void_p), budgets=ctypes.cast(buds, ctypes.c_void_p),
-                       kmax=J, scale=1.0 / D ** 0.5, q2k_idx=Pp(q2k_idx), q2k_num=Pp(q2k_num), item_order=Pp(order))
+                       kmax=J, scale=1.0 / D ** 0.5, q2k_idx=Pp(q2k_idx), q2k_num=Pp(q2k_num), item_order=Pp(order),
+                       no_fill=1)   # the attention reads only the first q2k_num entries of a row
     nws = ctypes.c_size_t()
     L.check(lib.h3_pool_route_topk_ws(ctypes.byref(ra), ctypes.byref(nws)))
     ws = torch.empty(nws.value, dtype=torch.uint8, device=dev)

@@ -75,7 +75,7 @@ class H3RouteArgs(ctypes.Structure):
                 ("perm", _p), ("block_len", _p), ("J", _i32), ("M", _i32),
                 ("num_prefix", _i32), ("nregions", _i32), ("spans", _p), ("budgets", _p),
                 ("kmax", _i32), ("scale", _f32), ("q2k_idx", _p), ("q2k_num", _p),
-                ("qbar", _p), ("kbar", _p), ("item_order", _p)]
+                ("qbar", _p), ("kbar", _p), ("item_order", _p), ("no_fill", _i32)]
 
 
 class ReblockArgs(ctypes.Structure):

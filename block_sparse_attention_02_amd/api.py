@@ -452,10 +452,11 @@ class H3Geometry:
 
 
 def h3_pool_route_topk(q, k, geom, budgets, kmax=None, scale=None, item_order=None, debug=False, out=None,
-                       workspace=None):
+                       workspace=None, fill=True):
     """Grouped routing over an H3 layout: context query blocks keep every
     block, video query blocks keep the prefix plus each region's TopK.
-    Returns (q2k_idx [B,H,J,kmax], q2k_num [B,H,J]) (plus qbar, kbar with debug)."""
+    Returns (q2k_idx [B,H,J,kmax], q2k_num [B,H,J]) (plus qbar, kbar with debug).
+    ``fill=False`` leaves the entries past each row's count unwritten."""
     _need_cuda(q, k)
     B, N, H, D = q.shape
     J = geom.J
@@ -482,7 +483,7 @@ def h3_pool_route_topk(q, k, geom, budgets, kmax=None, scale=None, item_order=No
                       block_len=_ptr(geom.block_len), J=J, M=geom.M, num_prefix=geom.num_prefix, nregions=nr,
                       spans=ctypes.cast(spans, ctypes.c_void_p), budgets=ctypes.cast(buds, ctypes.c_void_p),
                       kmax=kmax, scale=scale, q2k_idx=_ptr(q2k_idx), q2k_num=_ptr(q2k_num), qbar=_ptr(qbar),
-                      kbar=_ptr(kbar), item_order=_ptr(item_order))
+                      kbar=_ptr(kbar), item_order=_ptr(item_order), no_fill=0 if fill else 1)
     lib = _lib()
     n = ctypes.c_size_t()
     L.check(lib.h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)))
@@ -496,10 +497,12 @@ def h3_pool_route_topk(q, k, geom, budgets, kmax=None, scale=None, item_order=No
 
 def h3_forward(q, k, v, geom, budgets, scale=None, need_lse=False, workspace=None):
     """Multi-region routed attention: pool -> grouped route -> exact attention
-    over the union of kept blocks (one softmax).  Returns (out, q2k_idx, q2k_num)."""
+    over the union of kept blocks (one softmax).  Returns (out, q2k_idx, q2k_num);
+    the table's entries past each row's count are not written (no -1 fill)."""
     B, _, H, _ = q.shape
     order = torch.empty((B, H, geom.J), dtype=torch.int32, device=q.device)
-    q2k_idx, q2k_num = h3_pool_route_topk(q, k, geom, budgets, scale=scale, item_order=order, workspace=workspace)
+    q2k_idx, q2k_num = h3_pool_route_topk(q, k, geom, budgets, scale=scale, item_order=order, workspace=workspace,
+                                          fill=False)
     res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
                         need_lse=need_lse, item_order=order)
     if need_lse:

@@ -371,7 +371,7 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
     if (e != hipSuccess) return hip_status(e, "grouped route/topk launch");
     out_off += a->budgets[r];
   }
-  e = bsa::launch_h3_fill(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, P, nsel, s);
+  e = bsa::launch_h3_fill(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, P, nsel, !a->no_fill, s);
   if (e != hipSuccess || !a->item_order) return hip_status(e, "grouped index fill launch");
   return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, a->item_order, s),
                     "item order launch");

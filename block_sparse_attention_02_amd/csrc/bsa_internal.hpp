@@ -102,9 +102,10 @@ struct H3Layout {
 hipError_t launch_h3_tile_index(const H3Layout& L, int J, int32_t* perm, int32_t* block_len, int32_t* inv,
                                 hipStream_t s);
 // Rows < num_prefix: every block; other rows: blocks [0, num_prefix), the
-// region entries already written at [num_prefix, nsel), then -1; q2k_num.
+// region entries already written at [num_prefix, nsel), then -1 when `fill`;
+// q2k_num.
 hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int kmax, int num_prefix, int nsel,
-                          hipStream_t s);
+                          bool fill, hipStream_t s);
 // Processing order of the query blocks of every (b, h): Morton order of the
 // quartile entries of their kept lists ([B*H, J] int32 output).
 hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,

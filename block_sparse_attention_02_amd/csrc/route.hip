@@ -643,9 +643,11 @@ hipError_t launch_h3_tile_index(const H3Layout& L, int J, int32_t* perm, int32_t
 // Grouped routing ("VSA 实现详解" section 5.3, exempt rule): the per-region TopK
 // launches write the region entries of every video row; this kernel writes the
 // rest -- a context row keeps every block, a video row the prefix blocks in
-// front of its region entries -- the -1 fill and the counts.  One wave per row.
+// front of its region entries -- the -1 fill (when `fill`) and the counts.  One
+// wave per row.
 __global__ __launch_bounds__(256) void h3_fill_kernel(int32_t* __restrict__ q2k_idx, int32_t* __restrict__ q2k_num,
-                                                      int64_t rows, int J, int kmax, int num_prefix, int nsel) {
+                                                      int64_t rows, int J, int kmax, int num_prefix, int nsel,
+                                                      int fill) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -653,7 +655,8 @@ __global__ __launch_bounds__(256) void h3_fill_kernel(int32_t* __restrict__ q2k_
   int32_t* out = q2k_idx + row * kmax;
   const bool context = i < num_prefix;
   const int keep = context ? J : nsel;
-  for (int q = lane; q < kmax; q += 64) {
+  const int end = fill ? kmax : (context ? J : num_prefix);
+  for (int q = lane; q < end; q += 64) {
     if (context ? q < J : q < num_prefix)
       out[q] = q;
     else if (q >= keep)
@@ -663,10 +666,10 @@ __global__ __launch_bounds__(256) void h3_fill_kernel(int32_t* __restrict__ q2k_
 }
 
 hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int kmax, int num_prefix, int nsel,
-                          hipStream_t s) {
+                          bool fill, hipStream_t s) {
   const int64_t rows = (int64_t)BH * J;
   h3_fill_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(q2k_idx, q2k_num, rows, J, kmax, num_prefix,
-                                                                       nsel);
+                                                                       nsel, fill ? 1 : 0);
   return hipGetLastError();
 }
 

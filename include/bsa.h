@@ -209,8 +209,13 @@ bsa_status h3_tile_index(const bsa_segment* seg, int nseg, int bT, int bH, int b
  *   query block i >= num_prefix (video): keeps blocks 0..num_prefix-1 and, for
  *     every region r = [spans[2r], spans[2r+1]), the budgets[r] largest
  *     E[i, j] over the region's j (ties: lower j first);
- * written ascending to q2k_idx[b,h,i,:] with -1 fill, count in q2k_num.  The
- * attention over the union is bsa_forward_qouter in block mode.
+ * written ascending to q2k_idx[b,h,i,:] with -1 fill ([VSA] section 5.3: the
+ * table is kmax = J wide, so a video row is mostly fill), count in q2k_num.
+ * With no_fill set, entries at or past a row's count are left as they are
+ * (bsa_forward_qouter and the item order read only the first q2k_num[row]
+ * entries of a row); this saves rewriting the fill, most of the table's
+ * bytes, on every call.  The attention over the union is bsa_forward_qouter
+ * in block mode.
  *   spans, budgets   host arrays [2*nregions], [nregions]: the regions must
  *                    tile [num_prefix, J) in order; 1 <= budgets[r] <= size
  *   kmax             >= J when num_prefix > 0, and >= num_prefix + sum budgets
@@ -236,6 +241,7 @@ typedef struct {
   float* qbar;
   float* kbar;
   int32_t* item_order;
+  int no_fill;  /* 0: -1 fill past each row's count; nonzero: no fill */
 } h3_route_args;
 
 bsa_status h3_pool_route_topk_ws(const h3_route_args* a, size_t* bytes);

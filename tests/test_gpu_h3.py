@@ -134,6 +134,36 @@ def test_forward_matches_oracle(name):
         assert_attn_close(out[0, torch.as_tensor(ctx, device=DEV), hh], dense, "h3 context rows, head %d" % hh)
 
 
+def test_no_fill_leaves_padding_and_changes_nothing_else():
+    """Without the -1 fill the entries past each row's count keep what the
+    table held, the counted entries and the item order equal the filled
+    table's, and the attention over either table is bitwise the same."""
+    cfg = ATTN_CFGS["r2v_m64"]
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=DEV)
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    x = h3_inputs(cfg, device=DEV)
+    B, _, H, _ = x["q"].shape
+    J = geom.J
+    sentinel = 0x7ead
+    tables = {}
+    for fill in (True, False):
+        idx = torch.full((B, H, J, J), sentinel, dtype=torch.int32, device=DEV)
+        num = torch.empty((B, H, J), dtype=torch.int32, device=DEV)
+        order = torch.empty((B, H, J), dtype=torch.int32, device=DEV)
+        bsa.h3_pool_route_topk(x["q"], x["k"], geom, budgets, item_order=order, out=(idx, num), fill=fill)
+        out = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num,
+                                item_order=order)
+        torch.cuda.synchronize()
+        tables[fill] = (idx.cpu().numpy(), num.cpu().numpy(), order.cpu().numpy(), out.clone())
+    (fi, fn, fo, fout), (ni, nn, no, nout) = tables[True], tables[False]
+    assert np.array_equal(fn, nn) and np.array_equal(fo, no)
+    past = np.arange(J)[None, None, None, :] >= fn[..., None]
+    assert past.any()
+    assert (fi[past] == -1).all() and (ni[past] == sentinel).all()
+    assert np.array_equal(fi[~past], ni[~past])
+    assert torch.equal(fout.view(torch.int16), nout.view(torch.int16))
+
+
 def test_h3_full_size_sampled():
     """The H3 workload at full size (146676 tokens, J = 2412, 24 heads) in the
     launch configuration of bench.py: grouped routing of heads 0, 7, 15, 23

@@ -679,7 +679,7 @@ bsa_status spark_reblock_dims(int N, int M, int* J, int* nlevels) {
 
 namespace {
 struct ReblockWs {
-  size_t part, moment, factor, features, dirs, keys, vals, order, sort, total;
+  size_t part, moment, factor, features, dirs, keys, order, total;
 };
 
 ReblockWs reblock_ws_layout(const spark_reblock_args* a) {
@@ -694,10 +694,8 @@ ReblockWs reblock_ws_layout(const spark_reblock_args* a) {
   w.features = round_up((size_t)(BH * N * D * 2));  // fp16 features (the debug output is a copy)
   w.dirs = round_up((size_t)(BH * slots * D * 4));
   w.keys = round_up((size_t)(BH * N * 8));
-  w.vals = round_up((size_t)(BH * N * 4));
   w.order = round_up((size_t)(BH * N * 4));
-  w.sort = round_up(bsa::reblock_sort_bytes(BH * N, (int)BH));
-  w.total = w.part + w.moment + w.factor + w.features + w.dirs + 2 * w.keys + w.vals + 2 * w.order + w.sort;
+  w.total = w.part + w.moment + w.factor + w.features + w.dirs + 2 * w.keys + 2 * w.order;
   return w;
 }
 }  // namespace
@@ -752,11 +750,8 @@ bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes,
   rp.dirs = reinterpret_cast<float*>(take(w.dirs));
   rp.keys0 = reinterpret_cast<uint64_t*>(take(w.keys));
   rp.keys1 = reinterpret_cast<uint64_t*>(take(w.keys));
-  rp.vals0 = reinterpret_cast<int32_t*>(take(w.vals));
   rp.order0 = reinterpret_cast<int32_t*>(take(w.order));
   rp.order1 = reinterpret_cast<int32_t*>(take(w.order));
-  rp.sort_tmp = take(w.sort);
-  rp.sort_bytes = w.sort;
   rp.levels = a->levels, rp.perm = a->perm, rp.block_len = a->block_len;
   rp.dirs_out = a->dirs;
   return hip_status(bsa::launch_reblock(rp, (hipStream_t)stream), "reblock launch");

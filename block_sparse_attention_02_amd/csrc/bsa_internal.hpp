@@ -71,19 +71,15 @@ struct ReblockParams {
   float* features32;  // optional fp32 copy of the same values
   float* dirs;      // [BH, max slots, D]
   float* dirs_out;  // optional [nlevels - 1, BH, max slots, D]: every level's directions
-  uint64_t* keys0;  // [BH*N] each
+  uint64_t* keys0;  // [BH*N] each: sort composites (projection key << 32 | position)
   uint64_t* keys1;
-  int32_t* vals0;
   int32_t* order0;
   int32_t* order1;
-  void* sort_tmp;
-  size_t sort_bytes;
   int32_t* levels;     // optional [nlevels, BH, N]
   int32_t* perm;       // [BH, J*M]
   int32_t* block_len;  // [J]
 };
 int reblock_levels(int N, int M);
-size_t reblock_sort_bytes(int64_t total, int BH);
 hipError_t launch_reblock(const ReblockParams& p, hipStream_t s);
 
 // ---- H3 multi-region layout and grouped routing ------------------------------

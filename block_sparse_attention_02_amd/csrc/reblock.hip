@@ -16,16 +16,19 @@
 // floor((2s+1) n / 64) of the node's current order, their centred Gram
 // matrix, 16 power iterations from the ramp a_s = s - 15.5 (centring puts the
 // all-ones vector in the Gram matrix's null space), v = X^T a normalised,
-// largest entry positive), one projection key per token, and one stable
-// radix sort of (head, node, projection) keys that leaves every node's tokens
-// in projection order -- the first child's tokens first, in place.
+// largest entry positive), one projection key per token, and a stable sort of
+// every node's tokens by their keys -- the first child's tokens first, in
+// place.  Sorts run on unique 64-bit composites (key << 32 | position in the
+// node's current order), so any correct sort of them is the stable order:
+// nodes of at most 8192 tokens are sorted in LDS by one workgroup (stable
+// radix sort), larger ones in 8192-key chunks that merge-path rounds then
+// merge.
 //
 // Design (MI355X): the moment is an fp32 outer-product accumulation over
 // 2048-token chunks (each thread an 8 x 8 tile of the D x D matrix), reduced
 // in a fixed order, ridged and factored by a one-workgroup Cholesky in LDS;
 // the unit features u = z / |z|, z = k^T L, are formed with L resident in LDS.
 // Decisions (projections, sort keys) are taken in fp32.
-#include <hipcub/hipcub.hpp>
 
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
@@ -592,8 +595,7 @@ template <int D>
 __global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __restrict__ u,
                                                           const int32_t* __restrict__ order,
                                                           const float* __restrict__ dirs, int N, int M, int level,
-                                                          int max_slots, uint64_t* __restrict__ keys,
-                                                          int32_t* __restrict__ vals) {
+                                                          int max_slots, uint64_t* __restrict__ keys) {
   const int bh = blockIdx.y;
   const int pos0 = (blockIdx.x * 16 + (int)threadIdx.x / 16) * 16;
   const int l16 = threadIdx.x % 16;
@@ -607,15 +609,102 @@ __global__ __launch_bounds__(256) void reblock_key_kernel(const _Float16* __rest
     fk = float_key(project_batch16<D>(u + (int64_t)bh * N * D, ord, 0, cnt,
                                       dirs + ((int64_t)bh * max_slots + slot) * D, l16));
   if (l16 < cnt) {
-    const int64_t g = (int64_t)bh * N + pos0 + l16;
-    keys[g] = ((uint64_t)bh << (32 + level)) | ((uint64_t)slot << 32) | fk;
-    vals[g] = ord[l16];
+    int start, n, cc;
+    slot_range(N, M, level, slot, &start, &n, &cc);
+    keys[(int64_t)bh * N + pos0 + l16] = ((uint64_t)fk << 32) | (uint32_t)(pos0 + l16 - start);
   }
 }
 
+// ---- sorts -----------------------------------------------------------------------------
+// Stable LSD radix sort of 256 * IPT (key, value) pairs in LDS by 256 threads:
+// four passes of 8-bit digits.  Wave w owns the contiguous range
+// [w * 64 * IPT, (w + 1) * 64 * IPT) of the current order and takes it in
+// rounds of 64 consecutive items, so its lanes meet the items in order.  In a
+// round the lanes holding the same digit find each other with 8 ballots; an
+// item's rank among the wave's items of its digit is the wave's running count
+// of that digit (read before the round's leader adds the round's count) plus
+// the number of its peers in lower lanes.  A scan over (digit, wave) then
+// gives every (wave, digit) its output offset, and the items are scattered.
+// Equal keys keep their order, so sorting (projection key, position) this way
+// gives the same order as sorting the unique 64-bit composites.
+template <int IPT>
+__device__ __forceinline__ void block_radix_sort(uint32_t* keys, uint32_t* vals, uint32_t* hist /* [4 * 256] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int base = w * 64 * IPT;
+  for (int shift = 0; shift < 32; shift += 8) {
+    for (int x = threadIdx.x; x < 4 * 256; x += 256) hist[x] = 0u;
+    __syncthreads();
+    uint32_t k[IPT], v[IPT], pre[IPT];
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      k[r] = keys[base + 64 * r + lane];
+      v[r] = vals[base + 64 * r + lane];
+    }
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      const uint32_t d = (k[r] >> shift) & 255u;
+      uint64_t peers = ~0ull;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(((d >> b) & 1u) != 0u);
+        peers &= ((d >> b) & 1u) ? bal : ~bal;
+      }
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+      uint32_t* h = hist + w * 256 + d;
+      pre[r] = *h + below;  // this wave's LDS operations complete in order
+      if (below == 0u) *h += (uint32_t)__builtin_popcountll(peers);
+    }
+    __syncthreads();
+    {  // offsets: digit-major, then wave
+      const int d = threadIdx.x;
+      const uint32_t c0 = hist[d], c1 = hist[256 + d], c2 = hist[512 + d], c3 = hist[768 + d];
+      const uint32_t tot = c0 + c1 + c2 + c3;
+      // exclusive scan of tot over the 256 digits: within the wave, then across waves
+      uint32_t incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      __shared__ uint32_t wsum[4];
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      uint32_t off = incl - tot;
+      for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+      hist[d] = off;
+      hist[256 + d] = off + c0;
+      hist[512 + d] = off + c0 + c1;
+      hist[768 + d] = off + c0 + c1 + c2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      const uint32_t d = (k[r] >> shift) & 255u;
+      const uint32_t at = hist[w * 256 + d] + pre[r];
+      keys[at] = k[r];
+      vals[at] = v[r];
+    }
+    __syncthreads();
+  }
+}
+
+// Number of A elements among the first d outputs of merging sorted A (la)
+// and B (lb) -- keys are unique.
+__device__ __forceinline__ int merge_path(const uint64_t* a, int la, const uint64_t* b, int lb, int d) {
+  int lo = max(0, d - lb), hi = min(d, la);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < b[d - 1 - mid])
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
 // ---- one level, nodes of at most kLocalCap tokens: direction, projections (16
-// members per 16-lane group at a time) and a stable block radix sort of the projection keys with
-// the positions as values (the order of (key, position)), one workgroup per node.
+// members per 16-lane group at a time) and a stable radix sort of the
+// projection keys with the positions as values, one workgroup per node.
 constexpr int kLocalCap = 8192;  // capacities 1024, 4096, 8192 (the largest: one workgroup per CU)
 
 template <int D, int CAP>
@@ -623,11 +712,6 @@ __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16
                                                                   const int32_t* __restrict__ cur,
                                                                   int32_t* __restrict__ nxt, int N, int M, int level,
                                                                   int max_slots, float* __restrict__ dirs_out) {
-  constexpr int IPT = CAP / 256;
-  using Sorter = hipcub::BlockRadixSort<uint32_t, 256, IPT, int32_t>;
-  constexpr size_t kScratch = sizeof(typename Sorter::TempStorage) > sizeof(DirScratch<D>)
-                                  ? sizeof(typename Sorter::TempStorage)
-                                  : sizeof(DirScratch<D>);
   const int slot = blockIdx.x, bh = blockIdx.y;
   int start, n, c;
   slot_range(N, M, level, slot, &start, &n, &c);
@@ -639,34 +723,129 @@ __global__ __launch_bounds__(256) void reblock_local_level_kernel(const _Float16
     return;
   }
   __shared__ int32_t ord[CAP];
-  __shared__ uint32_t pkey[CAP];
-  __shared__ __align__(16) unsigned char scratch[kScratch];  // direction scratch, then the sort's
+  __shared__ uint32_t keys[CAP];
+  __shared__ uint32_t vals[CAP];
+  __shared__ uint32_t hist[4 * 256];
+  __shared__ DirScratch<D> dsh;
   __shared__ float v[D];
   for (int i = threadIdx.x; i < n; i += 256) ord[i] = src[i];
   __syncthreads();
   const _Float16* __restrict__ ub = u + (int64_t)bh * N * D;
-  node_direction<D>(ub, ord, n, *reinterpret_cast<DirScratch<D>*>(scratch), v);
+  node_direction<D>(ub, ord, n, dsh, v);
   if (dirs_out)
     for (int d = threadIdx.x; d < D; d += 256) dirs_out[((int64_t)bh * max_slots + slot) * D + d] = v[d];
   const int l16 = threadIdx.x & 15;
   for (int base = 16 * (threadIdx.x >> 4); base < n; base += 256) {  // uniform within each 16-lane group
     const float pr = project_batch16<D>(ub, ord, base, n, v, l16);
-    if (base + l16 < n) pkey[base + l16] = float_key(pr);
+    if (base + l16 < n) {
+      keys[base + l16] = float_key(pr);
+      vals[base + l16] = (uint32_t)(base + l16);
+    }
+  }
+  for (int i = n + (int)threadIdx.x; i < CAP; i += 256) {  // padding sorts last (after every member)
+    keys[i] = ~0u;
+    vals[i] = (uint32_t)i;
   }
   __syncthreads();
-  uint32_t kk[IPT];
-  int32_t vv[IPT];
-#pragma unroll
-  for (int x = 0; x < IPT; ++x) {
-    const int i = threadIdx.x * IPT + x;  // blocked arrangement
-    kk[x] = (i < n) ? pkey[i] : 0xffffffffu;  // padding sorts last (positions above every member)
-    vv[x] = i;
+  block_radix_sort<CAP / 256>(keys, vals, hist);
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = ord[vals[i]];
+}
+
+// ---- one level, large nodes: sort every 8192-key chunk of every node in LDS ----------------
+// (radix sort of the high halves with the low halves -- the positions, unique
+// inside a node -- as values; equal keys keep their position order)
+constexpr int kChunkKeys = 8192;
+
+__global__ __launch_bounds__(256) void reblock_chunk_sort_kernel(uint64_t* __restrict__ keys, int N, int M,
+                                                                 int level) {
+  const int slot = blockIdx.y, bh = blockIdx.z;
+  int start, n, c;
+  slot_range(N, M, level, slot, &start, &n, &c);
+  const int c0 = blockIdx.x * kChunkKeys;
+  if (c0 >= n) return;  // whole workgroup
+  const int m = min(kChunkKeys, n - c0);
+  uint64_t* __restrict__ g = keys + (int64_t)bh * N + start + c0;
+  __shared__ uint32_t skey[kChunkKeys];
+  __shared__ uint32_t sval[kChunkKeys];
+  __shared__ uint32_t hist[4 * 256];
+  for (int i = threadIdx.x; i < kChunkKeys; i += 256) {  // composites: key << 32 | position
+    const uint64_t kv = (i < m) ? g[i] : ~0ull;  // padding sorts last
+    skey[i] = (uint32_t)(kv >> 32);
+    sval[i] = (uint32_t)kv;
   }
-  Sorter(*reinterpret_cast<typename Sorter::TempStorage*>(scratch)).Sort(kk, vv);
-#pragma unroll
-  for (int x = 0; x < IPT; ++x) {
-    const int i = threadIdx.x * IPT + x;
-    if (i < n) dst[i] = ord[vv[x]];
+  __syncthreads();
+  block_radix_sort<kChunkKeys / 256>(skey, sval, hist);
+  for (int i = threadIdx.x; i < m; i += 256) g[i] = ((uint64_t)skey[i] << 32) | sval[i];
+}
+
+// ---- one level, large nodes: one merge-path round ------------------------------------------
+// Runs of L sorted keys (the last one of a node may be short) are merged in
+// pairs into runs of 2L.  Each workgroup writes kMergeTile consecutive outputs
+// of one merged pair: it finds where that output range starts and ends in the
+// two runs (merge path), stages both pieces in LDS and each thread merges 8
+// outputs after its own merge-path search.  The last round (`cur` given)
+// writes the tokens themselves: the low half of a composite is the token's
+// position in the node's current order.
+constexpr int kMergeTile = 2048;
+
+__global__ __launch_bounds__(256) void reblock_merge_kernel(const uint64_t* __restrict__ src,
+                                                            uint64_t* __restrict__ dst, int N, int M, int level,
+                                                            int L, const int32_t* __restrict__ cur,
+                                                            int32_t* __restrict__ nxt) {
+  const int slot = blockIdx.y, bh = blockIdx.z;
+  int start, n, c;
+  slot_range(N, M, level, slot, &start, &n, &c);
+  const int t0 = blockIdx.x * kMergeTile;
+  if (t0 >= n) return;  // whole workgroup
+  const int base = t0 / (2 * L) * (2 * L);  // the merged pair's first output (kMergeTile divides 2L)
+  const int la = min(L, n - base), lb = max(0, min(L, n - base - L));
+  const int64_t node = (int64_t)bh * N + start;
+  const uint64_t* __restrict__ A = src + node + base;
+  const uint64_t* __restrict__ B = A + la;
+  const int d0 = t0 - base, d1 = min(d0 + kMergeTile, la + lb);
+  __shared__ int ends[2];
+  __shared__ uint64_t sh[kMergeTile];
+  if (threadIdx.x < 64) {  // wave 0: both ends by a 64-way search (3 rounds of loads for 2^16 keys)
+    const int lane = threadIdx.x;
+    for (int e = 0; e < 2; ++e) {
+      const int d = e ? d1 : d0;
+      int lo = max(0, d - lb), hi = min(d, la);  // the answer lies in [lo, hi]
+      while (lo < hi) {
+        // A[i] < B[d - 1 - i] holds exactly for i below the answer; probe 64 points of [lo, hi)
+        const int span = hi - lo;
+        const int i = lo + (int)(((int64_t)span * lane) >> 6);
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(A[i] < B[d - 1 - i]);
+        const int t = __builtin_popcountll(bal);  // the true probes are the lowest t lanes
+        const int nlo = t > 0 ? lo + (int)(((int64_t)span * (t - 1)) >> 6) + 1 : lo;
+        const int nhi = t < 64 ? lo + (int)(((int64_t)span * t) >> 6) : hi;
+        lo = nlo;
+        hi = nhi;
+      }
+      if (lane == 0) ends[e] = lo;
+    }
+  }
+  __syncthreads();
+  const int i0 = ends[0], i1 = ends[1], j0 = d0 - i0, j1 = d1 - i1;
+  const int na = i1 - i0, nb = j1 - j0;
+  for (int x = threadIdx.x; x < na + nb; x += 256) sh[x] = (x < na) ? A[i0 + x] : B[j0 + x - na];
+  __syncthreads();
+  __shared__ uint64_t ob[kMergeTile];  // the merged tile, stored coalesced below
+  const int dl = 8 * (int)threadIdx.x;
+  if (dl < na + nb) {
+    int ia = merge_path(sh, na, sh + na, nb, dl), ib = dl - ia;
+    const int cnt = min(8, na + nb - dl);
+    for (int q = 0; q < cnt; ++q) {
+      const bool take_a = ib >= nb || (ia < na && sh[ia] < sh[na + ib]);
+      ob[dl + q] = take_a ? sh[ia++] : sh[na + ib++];
+    }
+  }
+  __syncthreads();
+  const int64_t o0 = node + base + d0;
+  for (int x = threadIdx.x; x < na + nb; x += 256) {
+    if (cur)
+      nxt[o0 + x] = cur[node + (int)(uint32_t)ob[x]];
+    else
+      dst[o0 + x] = ob[x];
   }
 }
 
@@ -765,29 +944,11 @@ __global__ __launch_bounds__(128) void reblock_wave_level_kernel(const _Float16*
 }
 
 // ---- host orchestration --------------------------------------------------------------------
-// Sort keys: head | slot (level bits) | projection key (32 bits).
-static int sort_end_bit(int BH, int level) {
-  int bh_bits = 0;
-  while ((1 << bh_bits) < BH) ++bh_bits;
-  return 32 + level + bh_bits;
-}
-
-size_t reblock_sort_bytes(int64_t total, int BH) {
-  size_t bytes = 0, b;
-  for (int level = 0; level <= 16; ++level) {  // the largest over the levels a sort may run at
-    b = 0;
-    hipcub::DeviceRadixSort::SortPairs(nullptr, b, (const uint64_t*)nullptr, (uint64_t*)nullptr,
-                                       (const int32_t*)nullptr, (int32_t*)nullptr, (int)total, 0,
-                                       sort_end_bit(BH, level));
-    bytes = b > bytes ? b : bytes;
-  }
-  return bytes;
-}
-
 template <int D>
 static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
   const int BH = p.B * p.H, N = p.N, M = p.M;
   const int64_t total = (int64_t)BH * N;
+  static_assert((2 * kChunkKeys) % kMergeTile == 0, "a merge tile never straddles two merged pairs");
   const int nc = (N + kMomentChunk - 1) / kMomentChunk;
   moment_partial_kernel<D><<<dim3((unsigned)nc, (unsigned)BH), 256, 0, s>>>(
       reinterpret_cast<const __bf16*>(p.q), p.sB, p.sN, p.sH, p.H, N, p.part);
@@ -833,12 +994,23 @@ static hipError_t reblock_d(const ReblockParams& p, hipStream_t s) {
                                                                                         max_slots, dirs);
       const int nbatch = (N + 15) / 16;  // 16 positions per 16-lane group, 16 groups per workgroup
       reblock_key_kernel<D><<<dim3((unsigned)((nbatch + 15) / 16), (unsigned)BH), 256, 0, s>>>(
-          p.features, cur, dirs, N, M, lev, max_slots, p.keys0, p.vals0);
+          p.features, cur, dirs, N, M, lev, max_slots, p.keys0);
+      reblock_chunk_sort_kernel<<<dim3((unsigned)((nmax + kChunkKeys - 1) / kChunkKeys), (unsigned)nslots,
+                                       (unsigned)BH), 256, 0, s>>>(p.keys0, N, M, lev);
+      // merge rounds: runs of 8192, 16384, ... keys until one run holds the
+      // largest node; the last round writes the next order itself
+      uint64_t* ka = p.keys0;
+      uint64_t* kb = p.keys1;
+      const dim3 mgrid((unsigned)((nmax + kMergeTile - 1) / kMergeTile), (unsigned)nslots, (unsigned)BH);
+      for (int64_t L = kChunkKeys; L < nmax; L *= 2) {
+        const bool last = 2 * L >= nmax;
+        reblock_merge_kernel<<<mgrid, 256, 0, s>>>(ka, kb, N, M, lev, (int)L, last ? cur : nullptr,
+                                                   last ? nxt : nullptr);
+        uint64_t* t = ka;
+        ka = kb;
+        kb = t;
+      }
       e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      size_t bytes = p.sort_bytes;
-      e = hipcub::DeviceRadixSort::SortPairs(p.sort_tmp, bytes, p.keys0, p.keys1, p.vals0, nxt, (int)total, 0,
-                                             sort_end_bit(BH, lev), s);
     }
     if (e != hipSuccess) return e;
     if (p.levels) {

@@ -537,6 +537,7 @@ def bench_h3(args):
     qa.perm, qa.block_len, qa.J, qa.M = Pp(geom.perm), Pp(geom.block_len), J, M
     qa.q2k_idx, qa.q2k_num, qa.kmax = Pp(q2k_idx), Pp(q2k_num), J
     qa.item_order = Pp(order)
+    qa.order_long = P  # the context query blocks (every block kept) start first
     qws = bsa.qouter_workspace(dev)
 
     def attend():

@@ -60,7 +60,7 @@ class QOuterArgs(ctypes.Structure):
                 ("blk_idx", _p), ("blk_cnt", _p), ("S", _i32), ("BS", _i32), ("causal", _i32),
                 ("lse", _p), ("item_order", _p),
                 ("k_sum", _p), ("v_sum", _p), ("b_sum", _p),
-                ("coarse", _p), ("gate", _p), ("perm_bh_stride", _i64)]
+                ("coarse", _p), ("gate", _p), ("perm_bh_stride", _i64), ("order_long", _i32)]
 
 
 class Segment(ctypes.Structure):

@@ -248,7 +248,7 @@ def spark_summaries(q, k, v, perm, block_len, J, M, scale=None, anchor=None, nee
 
 
 def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, need_lse=False, out=None,
-                  item_order=None, summaries=None, coarse=None, perm_bh_stride=0, workspace=None):
+                  item_order=None, summaries=None, coarse=None, perm_bh_stride=0, workspace=None, order_long=0):
     """Block-selected exact attention (VSA mode).  q, k, v: [B, N, H, D].
     ``item_order``: optional processing order (from pool_route_topk).
     ``summaries``: optional (k_sum, v_sum, b_sum) from spark_summaries; every
@@ -256,6 +256,8 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
     ``coarse``: optional (C, gate) -- C fp32 [B,H,J,D] from coarse_attention,
     gate fp32 [H, D]; each token of block i then gets gate * C[:, :, i] added.
     ``perm_bh_stride``: per-(b, h) tables in ``perm`` (as in pool_route_topk).
+    ``order_long``: the first order_long positions of every (b, h)'s order
+    run first, across all (b, h) (long kept lists first; results unchanged).
     ``workspace``: optional uint8 device tensor from qouter_workspace (calls
     that share one must be ordered on one stream), or "static" for the
     library's no-allocation entry point."""
@@ -270,6 +272,7 @@ def attention_vsa(q, k, v, perm, block_len, J, M, q2k_idx, q2k_num, scale=None, 
     a.perm, a.block_len, a.J, a.M = _ptr(perm), _ptr(block_len), J, M
     a.q2k_idx, a.q2k_num, a.kmax = _ptr(q2k_idx), _ptr(q2k_num), q2k_idx.shape[-1]
     a.perm_bh_stride = int(perm_bh_stride)
+    a.order_long = int(order_long)
     if item_order is not None:
         _need_cuda(item_order)
         if item_order.dtype != torch.int32 or item_order.numel() != B * H * J or not item_order.is_contiguous():
@@ -504,7 +507,7 @@ def h3_forward(q, k, v, geom, budgets, scale=None, need_lse=False, workspace=Non
     q2k_idx, q2k_num = h3_pool_route_topk(q, k, geom, budgets, scale=scale, item_order=order, workspace=workspace,
                                           fill=False)
     res = attention_vsa(q, k, v, geom.perm, geom.block_len, geom.J, geom.M, q2k_idx, q2k_num, scale=scale,
-                        need_lse=need_lse, item_order=order)
+                        need_lse=need_lse, item_order=order, order_long=geom.num_prefix)
     if need_lse:
         return res[0], q2k_idx, q2k_num, res[1]
     return res, q2k_idx, q2k_num

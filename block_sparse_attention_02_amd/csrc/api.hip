@@ -198,7 +198,7 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
                       a->q2k_idx, a->q2k_num, a->E, 0, a->J, 0, a->J, 0, 1};
   e = bsa::launch_route_topk(rp, s);
   if (e != hipSuccess || !a->item_order) return hip_status(e, "route/topk launch");
-  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, (int)(a->d.B * a->d.H), a->J, a->kmax,
+  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, (int)(a->d.B * a->d.H), a->J, a->kmax, 0,
                                            a->item_order, s),
                     "item order launch");
 }
@@ -373,7 +373,7 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
   }
   e = bsa::launch_h3_fill(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, P, nsel, !a->no_fill, s);
   if (e != hipSuccess || !a->item_order) return hip_status(e, "grouped index fill launch");
-  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, a->item_order, s),
+  return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, B * H, J, a->kmax, P, a->item_order, s),
                     "item order launch");
 }
 
@@ -430,6 +430,8 @@ static bsa_status check_qouter(const bsa_qouter_args* a) {
     }
     if (a->perm_bh_stride < 0 || (a->perm_bh_stride > 0 && a->perm_bh_stride < (int64_t)a->J * a->M))
       return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: perm_bh_stride must be 0 or >= J*M");
+    if (a->order_long < 0 || a->order_long > a->J)
+      return fail(BSA_ERR_ARG, "bsa_forward_qouter: order_long must lie in [0, J]");
     if (a->perm_bh_stride && a->k_sum)
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: summaries need one shared perm table");
     if (a->coarse || a->gate) {
@@ -471,7 +473,7 @@ static bsa_status launch_qouter(const bsa_qouter_args* a, void* sched, void* str
                          a->perm, a->block_len, a->q2k_idx, a->q2k_num,
                          (int)a->dq.B, (int)a->dq.H, a->J, a->M, a->kmax, (int)a->dq.D, a->dq.N,
                          scale_log2, a->lse, a->item_order, a->k_sum, a->v_sum, a->b_sum,
-                         a->coarse, a->gate, a->perm_bh_stride, sched, device_error_flag()};
+                         a->coarse, a->gate, a->perm_bh_stride, sched, device_error_flag(), a->order_long};
     return hip_status(bsa::launch_vsa_attention(p, a->dt == BSA_F32, s), "vsa attention launch");
   }
   bsa::NsaAttnParams p{a->q, a->k, a->v, a->out,

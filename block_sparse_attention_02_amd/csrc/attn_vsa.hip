@@ -53,12 +53,24 @@ __device__ __forceinline__ f32x4 coarse_term(const VsaAttnParams& p, int64_t bh,
 // ordered separately with wait_vmcnt<>().
 #define BSA_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// Query block of work item wid = (b*H + h)*J + slot: the slot itself, or the
-// slot's entry of the caller's processing order (-1 when that entry is not a
-// block index).
-__device__ __forceinline__ int item_block(const VsaAttnParams& p, int64_t wid) {
-  if (!p.order) return (int)(wid % p.J);
-  const int i = as_const(p.order)[wid];
+__device__ __forceinline__ int item_of(const VsaAttnParams& p, int64_t wid, int64_t* bh) {
+  // Work item wid -> (b * H + h, query block).  The first order_long
+  // positions of every (b, h)'s order come first, across all (b, h) (the
+  // longest items start first); then the rest, (b, h) by (b, h).  -1: the
+  // order names no block.
+  const int nl = p.order_long;
+  const int64_t nlong = (int64_t)p.B * p.H * nl;
+  int64_t pos;
+  if (wid < nlong || nl == p.J) {
+    *bh = wid / nl;
+    pos = wid % nl;
+  } else {
+    const int64_t w2 = wid - nlong;
+    *bh = w2 / (p.J - nl);
+    pos = nl + w2 % (p.J - nl);
+  }
+  if (!p.order) return (int)pos;
+  const int i = as_const(p.order)[*bh * p.J + pos];
   return (i >= 0 && i < p.J) ? i : -1;
 }
 
@@ -200,9 +212,9 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5;  // which half of the wave
-  const int i = item_block(p, wid);
+  int64_t bh;
+  const int i = item_of(p, wid, &bh);
   if (i < 0) return;  // not a block index (whole workgroup)
-  const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int M = p.M;
   const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
@@ -687,9 +699,9 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = w >> 1, g = w & 1;  // query half, key half
   const int h2 = lane >> 5;
-  const int i = item_block(p, wid);
+  int64_t bh;
+  const int i = item_of(p, wid, &bh);
   if (i < 0) return;  // not a block index (whole workgroup)
-  const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   constexpr int M = 64;
   const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
@@ -1188,10 +1200,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       break;
     }
-    int i = item_block(p, wid);
+    int64_t bh;
+    int i = item_of(p, wid, &bh);
     const bool out_ok = i >= 0;
     if (!out_ok) i = 0;
-    const int64_t bh = wid / p.J;
     const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
     const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
     const __bf16* qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sB + hh * p.q_sH;
@@ -1463,9 +1475,9 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   __shared__ float Kt[64 * D];
   __shared__ float Vt[64 * D];
   const int64_t wid = blockIdx.x;
-  const int i = item_block(p, wid);
+  int64_t bh;
+  const int i = item_of(p, wid, &bh);
   if (i < 0) return;  // not a block index (whole workgroup)
-  const int64_t bh = wid / p.J;
   const int hh = (int)(bh % p.H), b = (int)(bh / p.H);
   const int32_t* __restrict__ perm = p.perm + bh * p.perm_bh_stride;
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;

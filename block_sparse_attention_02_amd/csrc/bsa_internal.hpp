@@ -104,7 +104,7 @@ hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int
                           bool fill, hipStream_t s);
 // Processing order of the query blocks of every (b, h): Morton order of the
 // quartile entries of their kept lists ([B*H, J] int32 output).
-hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,
+hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax, int num_first,
                              int32_t* order, hipStream_t s);
 
 // ---- Spark-Reweight summaries -------------------------------------------------
@@ -156,6 +156,7 @@ struct VsaAttnParams {
   int64_t perm_bh_stride;  // elements between the perm tables of consecutive (b, h); 0: shared
   void* sched;             // scheduler state of the persistent grid (qouter_sched_bytes(), 256-byte aligned)
   uint32_t* err;           // sticky index-error flag of the device (a kept id >= J sets it)
+  int order_long;          // leading order positions of every (b, h) taken first, across all (b, h)
 };
 // Bytes of the persistent-grid scheduler state the block-mode kernels use.
 size_t qouter_sched_bytes();

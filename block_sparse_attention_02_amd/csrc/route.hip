@@ -535,8 +535,9 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
 // have similar quartile entries read overlapping windows of K/V; listing them
 // next to each other lets the workgroups that run at the same time share L2.
 // One workgroup per (b, h) sorts (Morton code of the three quartiles, 10 bits
-// each; block index) keys with a bitonic network in LDS.  The order changes no
-// attention result.
+// each; block index) keys with a bitonic network in LDS.  Blocks below
+// num_first (the H3 context rows, whose lists hold every block) come first, in
+// index order.  The order changes no attention result.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t spread3_10(uint32_t v) {
   v &= 0x3ffu;
@@ -549,7 +550,7 @@ __device__ __forceinline__ uint32_t spread3_10(uint32_t v) {
 
 __global__ __launch_bounds__(1024) void item_order_kernel(const int32_t* __restrict__ q2k_idx,
                                                           const int32_t* __restrict__ q2k_num, int J, int kmax,
-                                                          int np, int32_t* __restrict__ order) {
+                                                          int num_first, int np, int32_t* __restrict__ order) {
   __shared__ uint64_t key[kRouteMaxJ];
   const int64_t bh = blockIdx.x;
   for (int i = threadIdx.x; i < np; i += blockDim.x) {
@@ -566,6 +567,7 @@ __global__ __launch_bounds__(1024) void item_order_kernel(const int32_t* __restr
           code |= spread3_10((uint32_t)((int64_t)v * 1024 / J)) << c;
         }
       }
+      if (i < num_first) code = 0u;  // key i: below every other block's key
       kk = ((uint64_t)code << 32) | (uint32_t)i;
     }
     key[i] = kk;
@@ -589,11 +591,11 @@ __global__ __launch_bounds__(1024) void item_order_kernel(const int32_t* __restr
 }
 
 hipError_t launch_item_order(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int J, int kmax,
-                             int32_t* order, hipStream_t s) {
+                             int num_first, int32_t* order, hipStream_t s) {
   int np = 1;
   while (np < J) np <<= 1;
   if (np > kRouteMaxJ) return hipErrorInvalidValue;
-  item_order_kernel<<<dim3((unsigned)BH), dim3(1024), 0, s>>>(q2k_idx, q2k_num, J, kmax, np, order);
+  item_order_kernel<<<dim3((unsigned)BH), dim3(1024), 0, s>>>(q2k_idx, q2k_num, J, kmax, num_first, np, order);
   return hipGetLastError();
 }
 

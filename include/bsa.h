@@ -214,8 +214,10 @@ bsa_status h3_tile_index(const bsa_segment* seg, int nseg, int bT, int bH, int b
  * With no_fill set, entries at or past a row's count are left as they are
  * (bsa_forward_qouter and the item order read only the first q2k_num[row]
  * entries of a row); this saves rewriting the fill, most of the table's
- * bytes, on every call.  The attention over the union is bsa_forward_qouter
- * in block mode.
+ * bytes, on every call.  item_order (optional) is as in vsa_pool_route_topk
+ * with the num_prefix context blocks first in every (b, h), so that
+ * bsa_forward_qouter with order_long = num_prefix takes them first.  The
+ * attention over the union is bsa_forward_qouter in block mode.
  *   spans, budgets   host arrays [2*nregions], [nregions]: the regions must
  *                    tile [num_prefix, J) in order; 1 <= budgets[r] <= size
  *   kmax             >= J when num_prefix > 0, and >= num_prefix + sum budgets
@@ -329,6 +331,14 @@ typedef struct {
   /* optional, BSA_SEL_BLOCK: per-(b, h) tables, as in vsa_route_args (0:
    * shared); not with summaries. */
   int64_t perm_bh_stride;
+  /* optional, BSA_SEL_BLOCK, 0 <= order_long <= J: the first order_long
+   * positions of every (b, h)'s processing order (item_order, or block index
+   * order) are processed before every other item, across all (b, h); the rest
+   * follow (b, h) by (b, h).  For query blocks with far longer kept lists than
+   * the others (the H3 context rows keep every block), so that none of them
+   * starts late and runs alone at the end.  0: (b, h) by (b, h).  Results do
+   * not depend on it. */
+  int order_long;
 } bsa_qouter_args;
 
 bsa_status bsa_qouter_ws(const bsa_qouter_args* a, size_t* bytes);

@@ -104,6 +104,8 @@ def _qouter_args(**kw):
     ("q", ctypes.c_void_p(258), L.BSA_ERR_SHAPE),
     ("dt", 3, L.BSA_ERR_ARG),
     ("scale", float("inf"), L.BSA_ERR_ARG),
+    ("order_long", -1, L.BSA_ERR_ARG),
+    ("order_long", 2, L.BSA_ERR_ARG),   # > J = 1
 ])
 def test_qouter_validation(field, value, status):
     a = _qouter_args(**{field: value})

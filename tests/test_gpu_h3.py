@@ -164,6 +164,32 @@ def test_no_fill_leaves_padding_and_changes_nothing_else():
     assert torch.equal(fout.view(torch.int16), nout.view(torch.int16))
 
 
+def test_long_items_first_changes_no_result():
+    """The item order lists every head's context blocks first, and taking
+    them first across all heads (order_long = num_prefix) gives bitwise the
+    same output and LSE as the head-by-head order."""
+    cfg = ATTN_CFGS["two_refs_d64"]
+    geom = bsa.H3Geometry(cfg["segments"], cfg["block"], device=DEV)
+    budgets = geom.budgets(1.0 - cfg["keep"])
+    x = h3_inputs(cfg, device=DEV)
+    B, _, H, _ = x["q"].shape
+    P = geom.num_prefix
+    order = torch.empty((B, H, geom.J), dtype=torch.int32, device=DEV)
+    idx, num = bsa.h3_pool_route_topk(x["q"], x["k"], geom, budgets, item_order=order, fill=False)
+    res = {}
+    for nl in (0, P, geom.J):
+        out, lse = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, geom.J, geom.M, idx, num,
+                                     need_lse=True, item_order=order, order_long=nl)
+        torch.cuda.synchronize()
+        res[nl] = (out.clone(), lse.clone())
+    o = order.cpu().numpy()
+    assert P > 0 and (o[:, :, :P] == np.arange(P)).all()
+    assert (np.sort(o, axis=-1) == np.arange(geom.J)).all()
+    for nl in (P, geom.J):
+        assert torch.equal(res[nl][0].view(torch.int16), res[0][0].view(torch.int16))
+        assert torch.equal(res[nl][1], res[0][1])
+
+
 def test_h3_full_size_sampled():
     """The H3 workload at full size (146676 tokens, J = 2412, 24 heads) in the
     launch configuration of bench.py: grouped routing of heads 0, 7, 15, 23

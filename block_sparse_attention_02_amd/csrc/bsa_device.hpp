@@ -84,8 +84,6 @@ __device__ __forceinline__ float xor32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Round two floats to bf16 (one packed conversion, nearest even) and return

@@ -119,6 +119,24 @@ def test_kvouter_index_matches_reference(name):
     assert_attn_close(out, np.nan_to_num(ref_o), name + " combined (sampled)", mask=mask)
 
 
+def test_kvouter_no_selected_block():
+    """Every selection entry is -1: the reverse index is empty (no chunk, K1
+    writes nothing), nslot is 0 and the combine gives zeros with LSE -inf,
+    as the oracle does."""
+    B, N, Hq, Hkv, D, BK, ks = 1, 300, 4, 2, 64, 64, 4
+    q, k, v = _bf16_inputs(B, N, Hq, Hkv, D, seed=21)
+    q2k = torch.full((B, N, Hkv, ks), -1, dtype=torch.int32, device=DEV)
+    o_buf, lse_buf, nslot, ix = bsa.kvouter(q, k, v, q2k, BK, index=True)
+    out, lse = bsa.combine(o_buf, lse_buf, nslot, Hkv, need_lse=True)
+    torch.cuda.synchronize()
+    assert int(ix["nchunk"].item()) == 0 and int(ix["rowptr"][-1].item()) == 0
+    assert not ix["count"].any() and not nslot.any()
+    _check_index(ix, q2k, BK, True)
+    assert not out.float().any() and torch.isneginf(lse).all()
+    ref, ref_lse = oracle.nsa_attention(to64(q), to64(k), to64(v), q2k.cpu().numpy(), None, BK, causal=True)
+    assert not ref.any() and np.isneginf(ref_lse).all()
+
+
 CASES = {
     "msa_g16_bk128": (scaled("msa", N=2048, Hq=32, Hkv=2), True),
     "msa_g8_bk64_d64": (scaled("msa", N=1500, Hq=16, Hkv=2, BK=64, D=64, k=8), True),

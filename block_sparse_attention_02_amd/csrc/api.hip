@@ -1,5 +1,6 @@
 // C-ABI entry points of libbsa: argument validation on the host, then
 // stream-ordered kernel launches.  The contract is documented in include/bsa.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -152,6 +153,8 @@ static bsa_status check_route(const vsa_route_args* a) {
   bsa_status st = check_desc(a->d, "q/k", 1, false);
   if (st != BSA_OK) return st;
   if (a->d.D > 256) return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: D must be <= 256");
+  if ((a->qbar && !aligned16(a->qbar)) || (a->kbar && !aligned16(a->kbar)))
+    return fail(BSA_ERR_ARG, "vsa_pool_route_topk: qbar and kbar must be 16-byte aligned");
   if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "vsa_pool_route_topk: J and M must be positive");
   if (a->J > bsa::kRouteMaxJ)
     return fail(BSA_ERR_UNSUPPORTED, "vsa_pool_route_topk: J=%d exceeds %d blocks", a->J, bsa::kRouteMaxJ);
@@ -170,7 +173,8 @@ bsa_status vsa_pool_route_topk_ws(const vsa_route_args* a, size_t* bytes) {
   bsa_status st = check_route(a);
   if (st != BSA_OK) return st;
   const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
-  *bytes = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  *bytes = (a->qbar ? 0 : one) + (a->kbar ? 0 : one) +
+           round_up(bsa::route_planes_bytes((int)(a->d.B * a->d.H), a->J, (int)a->d.D));
   return ok();
 }
 
@@ -180,12 +184,14 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
   if (st != BSA_OK) return st;
   if (need && (!ws || ws_bytes < need))
     return fail(BSA_ERR_WORKSPACE, "vsa_pool_route_topk: workspace of %zu bytes required", need);
+  if (need && !aligned16(ws)) return fail(BSA_ERR_WORKSPACE, "vsa_pool_route_topk: workspace must be 16-byte aligned");
   const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
   char* w = static_cast<char*>(ws);
   float* qbar = a->qbar;
   float* kbar = a->kbar;
   if (!qbar) { qbar = reinterpret_cast<float*>(w); w += one; }
   if (!kbar) { kbar = reinterpret_cast<float*>(w); w += one; }
+  __bf16* kplanes = reinterpret_cast<__bf16*>(w);
   const int vec = 16 / elem_bytes(a->dt);
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
                       aligned16(a->q) && aligned16(a->k);
@@ -195,7 +201,7 @@ bsa_status vsa_pool_route_topk(const vsa_route_args* a, void* ws, size_t ws_byte
   hipError_t e = bsa::launch_pool(pp, a->dt == BSA_F32, vec_ok, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   bsa::RouteParams rp{qbar, kbar, (int)a->d.B, (int)a->d.H, a->J, (int)a->d.D, a->R, a->kmax, a->scale,
-                      a->q2k_idx, a->q2k_num, a->E, 0, a->J, 0, a->J, 0, 1};
+                      a->q2k_idx, a->q2k_num, a->E, 0, a->J, 0, a->J, 0, 1, kplanes};
   e = bsa::launch_route_topk(rp, s);
   if (e != hipSuccess || !a->item_order) return hip_status(e, "route/topk launch");
   return hip_status(bsa::launch_item_order(a->q2k_idx, a->q2k_num, (int)(a->d.B * a->d.H), a->J, a->kmax, 0,
@@ -300,6 +306,8 @@ static bsa_status check_h3_route(const h3_route_args* a, int* nsel) {
   bsa_status st = check_desc(a->d, "q/k", 1, false);
   if (st != BSA_OK) return st;
   if (a->d.D > 256) return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: D must be <= 256");
+  if ((a->qbar && !aligned16(a->qbar)) || (a->kbar && !aligned16(a->kbar)))
+    return fail(BSA_ERR_ARG, "h3_pool_route_topk: qbar and kbar must be 16-byte aligned");
   if (a->J < 1 || a->M < 1) return fail(BSA_ERR_SHAPE, "h3_pool_route_topk: J and M must be positive");
   if (a->J > bsa::kRouteMaxJ)
     return fail(BSA_ERR_UNSUPPORTED, "h3_pool_route_topk: J=%d exceeds %d blocks", a->J, bsa::kRouteMaxJ);
@@ -331,13 +339,23 @@ static bsa_status check_h3_route(const h3_route_args* a, int* nsel) {
   return BSA_OK;
 }
 
+// Pooled means (unless the caller takes them) and the key planes of the widest
+// region; the arguments are already checked.
+static size_t h3_route_ws_bytes(const h3_route_args* a) {
+  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
+  size_t planes = 0;
+  for (int r = 0; r < a->nregions; ++r)
+    planes = std::max(planes, bsa::route_planes_bytes((int)(a->d.B * a->d.H), a->spans[2 * r + 1] - a->spans[2 * r],
+                                                      (int)a->d.D));
+  return (a->qbar ? 0 : one) + (a->kbar ? 0 : one) + round_up(planes);
+}
+
 bsa_status h3_pool_route_topk_ws(const h3_route_args* a, size_t* bytes) {
   if (!bytes) return fail(BSA_ERR_ARG, "h3_pool_route_topk_ws: null output");
   int nsel = 0;
   bsa_status st = check_h3_route(a, &nsel);
   if (st != BSA_OK) return st;
-  const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
-  *bytes = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  *bytes = h3_route_ws_bytes(a);
   return ok();
 }
 
@@ -346,14 +364,16 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
   bsa_status st = check_h3_route(a, &nsel);
   if (st != BSA_OK) return st;
   const size_t one = round_up((size_t)a->d.B * a->d.H * a->J * a->d.D * sizeof(float));
-  const size_t need = (a->qbar ? 0 : one) + (a->kbar ? 0 : one);
+  const size_t need = h3_route_ws_bytes(a);
   if (need && (!ws || ws_bytes < need))
     return fail(BSA_ERR_WORKSPACE, "h3_pool_route_topk: workspace of %zu bytes required", need);
+  if (need && !aligned16(ws)) return fail(BSA_ERR_WORKSPACE, "h3_pool_route_topk: workspace must be 16-byte aligned");
   char* w = static_cast<char*>(ws);
   float* qbar = a->qbar;
   float* kbar = a->kbar;
   if (!qbar) { qbar = reinterpret_cast<float*>(w); w += one; }
   if (!kbar) { kbar = reinterpret_cast<float*>(w); w += one; }
+  __bf16* kplanes = reinterpret_cast<__bf16*>(w);  // shared by the regions' launches, in stream order
   const int vec = 16 / elem_bytes(a->dt);
   const bool vec_ok = a->d.D % vec == 0 && a->d.sB % vec == 0 && a->d.sN % vec == 0 && a->d.sH % vec == 0 &&
                       aligned16(a->q) && aligned16(a->k);
@@ -366,7 +386,7 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
   for (int r = 0; r < a->nregions; ++r) {
     const int b0 = a->spans[2 * r], b1 = a->spans[2 * r + 1];
     bsa::RouteParams rp{qbar, kbar, B, H, J, D, a->budgets[r], a->kmax, a->scale, a->q2k_idx, a->q2k_num, nullptr,
-                        P, J - P, b0, b1 - b0, out_off, 0};
+                        P, J - P, b0, b1 - b0, out_off, 0, kplanes};
     e = bsa::launch_route_topk(rp, s);
     if (e != hipSuccess) return hip_status(e, "grouped route/topk launch");
     out_off += a->budgets[r];

@@ -52,9 +52,14 @@ struct RouteParams {
   // entries [out_off, out_off + R) of each row; `tail` also writes the -1
   // fill and q2k_num = R.  The whole square: 0, J, 0, J, 0, 1.
   int row0, nrows, col0, ncols, out_off, tail;
+  // Scratch of route_planes_bytes(B*H, ncols, D) bytes (D = 64, 128, 256):
+  // the launch first writes the pooled keys of the column range there as bf16
+  // hi/lo planes in matrix-core operand order.
+  __bf16* kplanes;
 };
 // Largest J the fused route + TopK kernel handles.
 constexpr int kRouteMaxJ = 4096;
+size_t route_planes_bytes(int BH, int ncols, int D);
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s);
 
 // ---- Spark-Reblock ------------------------------------------------------------------

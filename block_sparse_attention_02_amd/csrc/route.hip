@@ -160,12 +160,16 @@ hipError_t launch_pool(const PoolParams& p, bool f32_input, bool vec, hipStream_
 // 16x16x32 bf16 matrix cores with every fp32 operand split as hi + lo bf16
 // (hi*hi + hi*lo + lo*hi), which keeps E at fp32 accuracy.  In the output
 // layout lane l owns query rows 16*rt + l%16 and columns 4*(l/16) + v of each
-// 16-column tile.
+// 16-column tile.  For D = 64, 128, 256 the pooled keys are split once per
+// launch (route_split_kernel) into hi/lo planes laid out as the operand
+// registers of each (16-column tile, 32-channel step): every band then reads
+// 1 KiB contiguous per load instead of re-splitting the fp32 means.
 //
-// TopK per row: an exact search for the R-th largest order-preserving key,
-// one bit per round (count keys >= candidate across the row), then every key
-// above the threshold is kept plus the lowest-index keys equal to it, and the
-// kept ids are emitted in increasing order from per-row bit masks.
+// TopK per row: an exact search for the R-th largest order-preserving key (a
+// radix select over LDS digit histograms for the top 16 bits, then a ballot
+// search among the few keys that share them), then every key above the
+// threshold is kept plus the lowest-index keys equal to it, and the kept ids
+// are emitted in increasing order from per-row bit masks.
 // ============================================================================
 constexpr int kRouteWaves = 8;
 constexpr int kBucket = 64;  // bucket keys gathered per row (more: plain rounds)
@@ -185,6 +189,35 @@ __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
+}
+
+// Radix-select step over one row's 256-bin digit histogram (whole wave, bins
+// 4*lane .. 4*lane+3): the digit d that holds the need-th largest key, so that
+// count(digit > d) < need <= count(digit >= d), and count(digit > d).  The
+// caller guarantees need <= the histogram's total.
+__device__ __forceinline__ void hist_select(const uint32_t* h, int need, int* digit, int* above) {
+  const int lane = threadIdx.x & 63;
+  const uint4 v = *reinterpret_cast<const uint4*>(h + 4 * lane);
+  const int s = (int)(v.x + v.y + v.z + v.w);
+  int incl = s;  // keys in this lane's bins and every higher lane's
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += y;
+  }
+  const int cum = incl - s;  // keys in higher lanes' bins
+  int d = -1, ab = 0;
+  if (cum < need && incl >= need) {
+    const int c3 = cum + (int)v.w, c2 = c3 + (int)v.z, c1 = c2 + (int)v.y;
+    if (c3 >= need) { d = 4 * lane + 3; ab = cum; }
+    else if (c2 >= need) { d = 4 * lane + 2; ab = c3; }
+    else if (c1 >= need) { d = 4 * lane + 1; ab = c2; }
+    else { d = 4 * lane; ab = c1; }
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(d >= 0);
+  const int src = m ? __ffsll((long long)m) - 1 : 0;
+  *digit = max(__shfl(d, src, 64), 0);
+  *above = __shfl(ab, src, 64);
 }
 
 // KD: D when it is a multiple of 32 (compile-time fast path), else 0.
@@ -207,6 +240,12 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   uint32_t* gtm = reinterpret_cast<uint32_t*>(qlo + BM * DP);
   uint32_t* eqm = gtm + BM * MW;
   int* red = reinterpret_cast<int*>(eqm + BM * MW);  // [2][8][BM]
+  int* bcnt = red + 2 * kRouteWaves * BM;                  // [BM] bucket sizes
+  int* res = bcnt + BM;                                    // [BM] thresholds
+  int* flag = res + BM;                                    // [4]: some bucket overflowed
+  uint32_t* bkey = reinterpret_cast<uint32_t*>(flag + 4);  // [BM][kBucket]
+  uint32_t* hist = bkey + BM * kBucket;                    // [BM][256] digit counts
+  int* above = reinterpret_cast<int*>(hist + BM * 256);    // [2][BM] keys above each digit
 
   const float* __restrict__ qb = p.qbar + ((int64_t)bh * JT + p.row0) * D;
   const float* __restrict__ kb = p.kbar + ((int64_t)bh * JT + p.col0) * D;
@@ -221,6 +260,9 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
     qlo[r * DP + d] = (__bf16)(x - (float)hi);
   }
   for (int e = threadIdx.x; e < 2 * BM * MW; e += 512) gtm[e] = 0u;
+  for (int e = threadIdx.x; e < BM * 256; e += 512) hist[e] = 0u;
+  for (int e = threadIdx.x; e < BM; e += 512) bcnt[e] = 0;
+  if (threadIdx.x == 0) *flag = 0;
   __syncthreads();
 
   // ---- scores: E^T tiles for this wave's columns -----------------------------
@@ -229,44 +271,39 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   uint32_t key[RT][NT][4];
   const int g = lane >> 4, l16 = lane & 15;
   if constexpr (KD > 0) {
-    // D is a multiple of 32: unconditional loads (rows past J clamped), and the
-    // next column tile's operands are fetched before this tile's products.
+    // D = 64, 128, 256: operands from the hi/lo planes (one 16-byte load per
+    // lane per plane and 32-channel step, tiles past the last one clamped),
+    // the next column tile's fetched before this tile's products.
     constexpr int KS = KD / 32;
-    f32x4 kbuf[2][2 * KS];
-    auto fetch = [&](f32x4* dst, int t) {
-      const int jr = min(w * CW + 16 * t + l16, J - 1);
-      const float* src = kb + (int64_t)jr * KD + 8 * g;
+    const int nT = (J + 15) / 16;
+    const int64_t plane = (int64_t)p.B * p.H * nT * KS * 512;  // bf16 elements per plane
+    bf16x8 kh[2][KS], kl[2][KS];
+    auto fetch = [&](int b, int t) {
+      const int T = min(w * NT + t, nT - 1);
+      const __bf16* src = p.kplanes + ((int64_t)bh * nT + T) * KS * 512 + lane * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        dst[2 * s] = *reinterpret_cast<const f32x4*>(src + 32 * s);
-        dst[2 * s + 1] = *reinterpret_cast<const f32x4*>(src + 32 * s + 4);
+        kh[b][s] = *reinterpret_cast<const bf16x8*>(src + s * 512);
+        kl[b][s] = *reinterpret_cast<const bf16x8*>(src + plane + s * 512);
       }
     };
-    fetch(kbuf[0], 0);
+    fetch(0, 0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t + 1 < NT) fetch(kbuf[(t + 1) & 1], t + 1);
+      if (t + 1 < NT) fetch((t + 1) & 1, t + 1);
       f32x4 acc[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const f32x4 a = kbuf[t & 1][2 * s], c = kbuf[t & 1][2 * s + 1];
-        const float kv[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-        bf16x8 khi, klo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          khi[e] = (__bf16)kv[e];
-          klo[e] = (__bf16)(kv[e] - (float)khi[e]);
-        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int row = 16 * rt + l16;
           const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi + row * DP + 32 * s + 8 * g);
           const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo + row * DP + 32 * s + 8 * g);
-          acc[rt] = mfma16(klo, qh, acc[rt]);
-          acc[rt] = mfma16(khi, ql, acc[rt]);
-          acc[rt] = mfma16(khi, qh, acc[rt]);
+          acc[rt] = mfma16(kl[t & 1][s], qh, acc[rt]);
+          acc[rt] = mfma16(kh[t & 1][s], ql, acc[rt]);
+          acc[rt] = mfma16(kh[t & 1][s], qh, acc[rt]);
         }
       }
 #pragma unroll
@@ -276,6 +313,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
           const float e = acc[rt][v] * p.scale;
           const int j = w * CW + 16 * t + 4 * g + v;
           key[rt][t][v] = (j < J) ? float_key(e) : 0u;
+          if (j < J) atomicAdd(&hist[(16 * rt + l16) * 256 + (key[rt][t][v] >> 24)], 1u);
         }
     }
   } else {
@@ -317,6 +355,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
           const float e = acc[rt][v] * p.scale;
           const int j = w * CW + 16 * t + 4 * g + v;
           key[rt][t][v] = (j < J) ? float_key(e) : 0u;
+          if (j < J) atomicAdd(&hist[(16 * rt + l16) * 256 + (key[rt][t][v] >> 24)], 1u);
         }
     }
   }
@@ -334,14 +373,50 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
   }
 
   // ---- exact threshold: the R-th largest key of every row ------------------------
-  // Rounds over bits 31..16 fix the threshold's top half.  The keys that share
-  // it (the row's "bucket", a handful for continuous scores) are then gathered
-  // in LDS and one wave finds the exact rank among them with ballots.  When
-  // some row's bucket holds more than kBucket keys the workgroup finishes with
-  // the plain rounds over bits 15..0 instead; both give the same threshold.
+  // Radix select: the top byte from the histogram built with the scores, then
+  // the next byte from a histogram of the keys that share the top byte; that
+  // fixes the threshold's top 16 bits.  The keys that share them (the row's
+  // "bucket", a handful for continuous scores) are gathered in LDS and one
+  // wave finds the exact rank among them with ballots.  When some row's bucket
+  // holds more than kBucket keys the workgroup finishes with rounds over bits
+  // 15..0 instead (count keys >= candidate across the row); both give the same
+  // threshold.
+  __syncthreads();
+  for (int row = w; row < BM; row += kRouteWaves) {
+    int d, ab;
+    hist_select(hist + row * 256, p.R, &d, &ab);
+    *reinterpret_cast<uint4*>(hist + row * 256 + 4 * lane) = uint4{0u, 0u, 0u, 0u};  // reused below
+    if (lane == 0) { res[row] = d; above[row] = ab; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + l16;
+    const uint32_t d1 = (uint32_t)res[row];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t k = key[rt][t][v];
+        if ((k >> 24) == d1 && (w * CW + 16 * t + 4 * g + v) < J)
+          atomicAdd(&hist[row * 256 + ((k >> 16) & 255u)], 1u);
+      }
+  }
+  __syncthreads();
+  for (int row = w; row < BM; row += kRouteWaves) {
+    const int d1 = res[row], ab1 = above[row];
+    int d2, ab2;
+    hist_select(hist + row * 256, p.R - ab1, &d2, &ab2);
+    if (lane == 0) {
+      above[BM + row] = ab1 + ab2;
+      if (hist[row * 256 + d2] > (uint32_t)kBucket) *flag = 1;
+      res[row] = (int)(((uint32_t)d1 << 24) | ((uint32_t)d2 << 16));
+    }
+  }
+  __syncthreads();
   uint32_t thr[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) thr[rt] = 0u;
+  for (int rt = 0; rt < RT; ++rt) thr[rt] = (uint32_t)res[16 * rt + l16];
   int par = 0;
   auto round_bit = [&](int bit) {
     int cnt[RT];
@@ -371,71 +446,43 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
     }
     par ^= 1;
   };
-  for (int bit = 31; bit >= 16; --bit) round_bit(bit);
-
-  // bucket of each row: keys whose top 16 bits equal the threshold's
-  {
-    int* bcnt = red + 2 * kRouteWaves * BM;                   // [BM] bucket sizes
-    int* res = bcnt + BM;                                     // [BM] final thresholds
-    int* flag = res + BM;                                     // [1] some bucket overflowed
-    uint32_t* bkey = reinterpret_cast<uint32_t*>(flag + 4);   // [BM][kBucket]
-    for (int e = threadIdx.x; e < BM; e += 512) bcnt[e] = 0;
-    if (threadIdx.x == 0) *flag = 0;
-    __syncthreads();
-    int above[RT];
+  if (*flag) {
+    for (int bit = 15; bit >= 0; --bit) round_bit(bit);
+  } else {
+    // bucket of each row: keys whose top 16 bits equal the threshold's
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = 16 * rt + l16;
       const uint32_t hi = thr[rt] >> 16;
-      int c = 0;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint32_t k = key[rt][t][v];  // padding columns hold 0, never in a bucket above 0
-          c += ((k >> 16) > hi) ? 1 : 0;
+          const uint32_t k = key[rt][t][v];
           if ((k >> 16) == hi && (w * CW + 16 * t + 4 * g + v) < J) {
             const int slot = atomicAdd(&bcnt[row], 1);
             if (slot < kBucket) bkey[row * kBucket + slot] = k;
           }
         }
-      c += __shfl_xor(c, 16, 64);
-      c += __shfl_xor(c, 32, 64);
-      above[rt] = c;
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) red[(par * kRouteWaves + w) * BM + 16 * rt + lane] = above[rt];
     }
     __syncthreads();
-    for (int row = threadIdx.x; row < BM; row += 512)
-      if (bcnt[row] > kBucket) *flag = 1;
-    __syncthreads();
-    if (*flag) {
-      for (int bit = 15; bit >= 0; --bit) round_bit(bit);
-    } else {
-      // the need-th largest bucket key, need = R - #keys above the bucket;
-      // one wave per row, one bucket key per lane, ballots over the low 16 bits
-      for (int row = w; row < BM; row += kRouteWaves) {
-        int ab = 0;
-        for (int ww = 0; ww < kRouteWaves; ++ww) ab += red[(par * kRouteWaves + ww) * BM + row];
-        const int need = p.R - ab;
-        const int nb = bcnt[row];
-        const uint32_t mine = lane < nb ? bkey[row * kBucket + lane] : 0u;
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(
-                                (int)(lane < nb ? mine : 0u)) & 0xffff0000u;
-        uint32_t t32 = hi;
-        for (int bit = 15; bit >= 0; --bit) {
-          const uint32_t cand = t32 | (1u << bit);
-          const int c = __popcll(__builtin_amdgcn_ballot_w64(lane < nb && mine >= cand));
-          if (c >= need) t32 = cand;
-        }
-        if (lane == 0) res[row] = (int)t32;
+    // the need-th largest bucket key, need = R - #keys above the bucket;
+    // one wave per row, one bucket key per lane, ballots over the low 16 bits
+    for (int row = w; row < BM; row += kRouteWaves) {
+      const int need = p.R - above[BM + row];
+      const int nb = bcnt[row];
+      const uint32_t mine = lane < nb ? bkey[row * kBucket + lane] : 0u;
+      uint32_t t32 = (uint32_t)res[row];
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t cand = t32 | (1u << bit);
+        const int c = __popcll(__builtin_amdgcn_ballot_w64(lane < nb && mine >= cand));
+        if (c >= need) t32 = cand;
       }
-      __syncthreads();
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) thr[rt] = (uint32_t)res[16 * rt + l16];
+      if (lane == 0) res[row] = (int)t32;
     }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) thr[rt] = (uint32_t)res[16 * rt + l16];
   }
 
   // ---- bit masks of keys above / equal to the threshold ------------------------
@@ -521,7 +568,8 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
   constexpr int MW = kRouteWaves * 16 * NT / 32;
   const int KS = (p.D + 31) / 32, DP = KS * 32 + 8;
   const size_t smem = (size_t)2 * BM * DP * sizeof(__bf16) + (size_t)2 * BM * MW * 4 +
-                      (size_t)2 * kRouteWaves * BM * 4 + (size_t)(2 * BM + 4) * 4 + (size_t)BM * kBucket * 4;
+                      (size_t)2 * kRouteWaves * BM * 4 + (size_t)(2 * BM + 4) * 4 + (size_t)BM * kBucket * 4 +
+                      (size_t)BM * 256 * 4 + (size_t)2 * BM * 4;
   switch (p.D) {
     case 64: return launch_route_k<NT, RT, 64>(p, smem, s);
     case 128: return launch_route_k<NT, RT, 128>(p, smem, s);
@@ -675,7 +723,56 @@ hipError_t launch_h3_fill(int32_t* q2k_idx, int32_t* q2k_num, int BH, int J, int
   return hipGetLastError();
 }
 
+// hi/lo planes of the pooled keys of columns [col0, col0 + ncols): for each
+// (b*h, 16-column tile T, 32-channel step s) 64 lanes x 8 bf16, lane l holding
+// channels 32s + 8(l/16) .. +7 of column 16T + l%16 (zero past ncols), the
+// hi plane then the lo plane (lo = x - hi, both rounded to nearest).  One
+// thread per lane slot.
+__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ kbar, __bf16* __restrict__ out,
+                                                          int64_t slots, int JT, int col0, int ncols, int nT, int KS,
+                                                          int D) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= slots) return;
+  const int lane = (int)(id & 63);
+  const int64_t u = id >> 6;
+  const int s = (int)(u % KS);
+  const int64_t T = (u / KS) % nT, bh = u / KS / nT;
+  const int j = (int)(16 * T) + (lane & 15);
+  const int d0 = 32 * s + 8 * (lane >> 4);
+  f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, c = a;
+  if (j < ncols) {
+    const float* src = kbar + (bh * JT + col0 + j) * D + d0;
+    a = *reinterpret_cast<const f32x4*>(src);
+    c = *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+  *reinterpret_cast<bf16x8*>(out + id * 8) = h;
+  *reinterpret_cast<bf16x8*>(out + (slots + id) * 8) = l;
+}
+
+static bool route_uses_planes(int D) { return D == 64 || D == 128 || D == 256; }
+
+size_t route_planes_bytes(int BH, int ncols, int D) {
+  if (!route_uses_planes(D)) return 0;
+  return (size_t)BH * ((ncols + 15) / 16) * (D / 32) * 64 * 8 * sizeof(__bf16) * 2;
+}
+
 hipError_t launch_route_topk(const RouteParams& p, hipStream_t s) {
+  if (route_uses_planes(p.D)) {
+    if (!p.kplanes) return hipErrorInvalidValue;
+    const int nT = (p.ncols + 15) / 16, KS = p.D / 32;
+    const int64_t slots = (int64_t)p.B * p.H * nT * KS * 64;
+    route_split_kernel<<<dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s>>>(p.kbar, p.kplanes, slots, p.J,
+                                                                                   p.col0, p.ncols, nT, KS, p.D);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int cols_per_wave = (p.ncols + kRouteWaves - 1) / kRouteWaves;
   if (cols_per_wave <= 16) return launch_route_t<1, 2>(p, s);
   if (cols_per_wave <= 32) return launch_route_t<2, 2>(p, s);

@@ -146,8 +146,10 @@ int vsa_budget(double drop_ratio, int J);
  *           (b, h) has its own table at perm + (b*H + h) * perm_bh_stride
  *           (>= J*M; per-head layouts such as spark_reblock's), block_len is
  *           shared.
- * Supported: 1 <= R <= J <= 4096, D <= 256, any N.  The workspace holds the
- * pooled means: vsa_pool_route_topk_ws() bytes.
+ * Supported: 1 <= R <= J <= 4096, D <= 256, any N.  qbar, kbar and the
+ * workspace must be 16-byte aligned.  The workspace holds the pooled means
+ * and, for D = 64, 128 or 256, the pooled keys split into bf16 hi/lo planes
+ * for the score products: vsa_pool_route_topk_ws() bytes.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* q;
@@ -223,7 +225,8 @@ bsa_status h3_tile_index(const bsa_segment* seg, int nseg, int bT, int bH, int b
  *   kmax             >= J when num_prefix > 0, and >= num_prefix + sum budgets
  * Supported as vsa_pool_route_topk (J <= 4096, D <= 256, B*H <= 65535),
  * nregions <= BSA_H3_MAX_SEGMENTS; nregions = 0 only with num_prefix = J.
- * The workspace holds the pooled means: h3_pool_route_topk_ws() bytes. */
+ * The workspace holds the pooled means and the key planes of the widest
+ * region: h3_pool_route_topk_ws() bytes (alignment as vsa_pool_route_topk). */
 typedef struct {
   const void* q;
   const void* k;

@@ -64,6 +64,7 @@ def _route_args(**kw):
     ("R", 0, L.BSA_ERR_SHAPE),
     ("kmax", 1, L.BSA_ERR_SHAPE),
     ("J", 5000, L.BSA_ERR_UNSUPPORTED),
+    ("kbar", 260, L.BSA_ERR_ARG),   # not 16-byte aligned
     ("dt", 7, L.BSA_ERR_ARG),
 ])
 def test_route_validation(field, value, status):
@@ -80,7 +81,9 @@ def test_route_workspace_size_and_short_workspace():
     a = _route_args()
     n = ctypes.c_size_t()
     assert lib.vsa_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
-    assert n.value == 2 * 1024   # two [1,1,4,64] fp32 pooled-mean buffers
+    # two [1,1,4,64] fp32 pooled-mean buffers, then the key planes: one
+    # 16-column tile x 2 channel steps x 64 lanes x 16 bytes, hi and lo
+    assert n.value == 2 * 1024 + 1 * 2 * 64 * 16 * 2
     assert lib.vsa_pool_route_topk(ctypes.byref(a), None, 0, None) == L.BSA_ERR_WORKSPACE
 
 
@@ -254,7 +257,10 @@ def test_h3_route_validation(spans, budgets, kw, status):
     n = ctypes.c_size_t()
     assert L.load().h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == status
     if status == L.BSA_OK:
-        assert n.value == 2 * 10 * 64 * 4
+        # pooled means, plus the key planes of the widest region (at most 16
+        # columns: one tile x 2 channel steps x 64 lanes x 16 bytes, hi and lo)
+        planes = 1 * 2 * 64 * 16 * 2 if budgets else 0
+        assert n.value == 2 * 10 * 64 * 4 + planes
 
 
 def _kv_args(**kw):

@@ -107,27 +107,31 @@ def test_hand_example_d2(golden):
     assert num[0, 0].tolist() == [2] * 4
 
 
-@pytest.mark.parametrize("R,kmax", [(8, 8), (5, 11), (1, 1), (31, 32)])
-def test_exact_ties_go_to_the_lower_block(R, kmax):
+@pytest.mark.parametrize("grid,nch,R,kmax", [((8, 16, 16), 4, 8, 8), ((8, 16, 16), 4, 5, 11), ((8, 16, 16), 4, 1, 1),
+                                              ((8, 16, 16), 4, 31, 32), ((16, 32, 32), 2, 100, 100),
+                                              ((16, 32, 32), 2, 200, 256), ((32, 64, 64), 2, 1000, 1000)])
+def test_exact_ties_go_to_the_lower_block(grid, nch, R, kmax):
     """Scores with exact ties: every token of key block j is the unit vector
-    of channel j % 4 and every token of query block i an integer vector, so
+    of channel j % nch and every token of query block i an integer vector, so
     pooled means, products and scores are exact in fp32 and each row holds
-    only four distinct values, each taken by eight blocks.  The kept lists
-    must equal the oracle's (ties to the lower index) on every row, with no
-    exemption."""
-    geom_args = ((8, 16, 16), (4, 4, 4))
-    geom = bsa.VsaGeometry(*geom_args, device=DEV)
-    tab = oracle.tile_index(8, 16, 16, 4, 4, 4)
+    at most nch distinct values, each taken by J / nch blocks (all J in the
+    rows whose query vector is zero).  The kept lists must equal the oracle's
+    (ties to the lower index) on every row, with no exemption.  With two
+    channels (J = 256 and 2048) a tie group holds J / 2 or J keys, more than
+    the kernel gathers for its final search, so these rows take its other
+    path."""
+    geom = bsa.VsaGeometry(grid, (4, 4, 4), device=DEV)
+    tab = oracle.tile_index(*grid, 4, 4, 4)
     J, M, h, D = geom.J, geom.M, 2, 64
     rng = np.random.default_rng(123)
-    qv = rng.integers(0, 4, size=(h, J, 4)).astype(np.float32)
-    q = np.zeros((1, 8 * 16 * 16, h, D), dtype=np.float32)
+    qv = rng.integers(0, 4, size=(h, J, nch)).astype(np.float32)
+    q = np.zeros((1, grid[0] * grid[1] * grid[2], h, D), dtype=np.float32)
     k = np.zeros_like(q)
     for j in range(J):
         toks = tab["perm"][j * M:(j + 1) * M]
         for hh in range(h):
-            q[0, toks, hh, :4] = qv[hh, j]
-            k[0, toks, hh, (j + hh) % 4] = 1.0
+            q[0, toks, hh, :nch] = qv[hh, j]
+            k[0, toks, hh, (j + hh) % nch] = 1.0
     qt = torch.from_numpy(q).to(torch.bfloat16).to(DEV)
     kt = torch.from_numpy(k).to(torch.bfloat16).to(DEV)
     idx, num, qbar, kbar, E = bsa.pool_route_topk(qt, kt, geom.perm, geom.block_len, J, M, R, kmax=kmax, debug=True)

@@ -409,7 +409,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(RouteParams p) {
     hist_select(hist + row * 256, p.R - ab1, &d2, &ab2);
     if (lane == 0) {
       above[BM + row] = ab1 + ab2;
-      if (hist[row * 256 + d2] > (uint32_t)kBucket) *flag = 1;
+      if (i0 + row < NR && hist[row * 256 + d2] > (uint32_t)kBucket) *flag = 1;  // rows past NR are not emitted
       res[row] = (int)(((uint32_t)d1 << 24) | ((uint32_t)d2 << 16));
     }
   }

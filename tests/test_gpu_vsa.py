@@ -54,6 +54,9 @@ ROUTE_CFGS = {
     "video_edge_30x16x16": scaled("video", grid=(30, 16, 16), h=2, R=13),
     "video_full_grid_h2": scaled("video", h=2),
     "video_d64_odd": scaled("video", grid=(9, 12, 20), h=3, D=64, R=5, block=(4, 4, 4)),
+    # J = 105 and 1881: the last band of query blocks is partial and J > 64
+    "video_partial_band": scaled("video", grid=(12, 20, 28), h=2, R=11),
+    "video_partial_band_wide": scaled("video", grid=(36, 44, 76), h=1, R=150),
 }
 
 

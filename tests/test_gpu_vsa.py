@@ -57,6 +57,10 @@ ROUTE_CFGS = {
     # J = 105 and 1881: the last band of query blocks is partial and J > 64
     "video_partial_band": scaled("video", grid=(12, 20, 28), h=2, R=11),
     "video_partial_band_wide": scaled("video", grid=(36, 44, 76), h=1, R=150),
+    # head dims with the widest operand planes (D = 256) and with no planes
+    # (D = 96 splits the fp32 means inside the kernel)
+    "video_d256": scaled("video", grid=(12, 16, 20), h=2, D=256, R=7),
+    "video_d96": scaled("video", grid=(12, 16, 20), h=2, D=96, R=7),
 }
 
 

@@ -55,6 +55,7 @@ COARSE_CFGS = {
     "ragged_blocks": scaled("video", grid=(6, 22, 30), h=2, R=9),   # partial blocks on every axis
     "d64_odd": scaled("video", grid=(9, 12, 20), h=3, D=64, R=5),
     "odd_two_chunks": scaled("video", grid=(12, 20, 28), h=2, R=7),  # J = 105: unaligned rows, 64 + 41 columns
+    "two_batches": scaled("video", B=2, grid=(8, 24, 28), h=2, R=6),
 }
 
 
@@ -108,6 +109,7 @@ ATTN_CFGS = {
     "small_d64": workload("small"),                                          # M = 64, D = 64
     "video_ragged": scaled("video", grid=(6, 22, 30), h=2, R=9),            # M = 64, D = 128
     "video_m32": scaled("video", grid=(8, 12, 16), h=2, block=(2, 4, 4), R=10),  # M = 32 kernel
+    "video_ragged_b2": scaled("video", B=2, grid=(6, 22, 30), h=2, R=9),   # two batch entries
 }
 
 

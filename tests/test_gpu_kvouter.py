@@ -141,6 +141,7 @@ CASES = {
     "msa_g16_bk128": (scaled("msa", N=2048, Hq=32, Hkv=2), True),
     "msa_g8_bk64_d64": (scaled("msa", N=1500, Hq=16, Hkv=2, BK=64, D=64, k=8), True),
     "msa_noncausal": (scaled("msa", N=1024, Hq=16, Hkv=1, k=6), False),
+    "msa_b2": (scaled("msa", B=2, N=1100, Hq=16, Hkv=2, k=6), True),
 }
 
 

@@ -30,6 +30,7 @@ def _setup(cfg):
 SUM_CFGS = {
     "ragged_d128": scaled("video", grid=(6, 12, 20), h=2, R=4),
     "ragged_d64": scaled("video", grid=(7, 9, 13), h=3, D=64, R=3),
+    "ragged_d128_b2": scaled("video", B=2, grid=(6, 12, 20), h=2, R=4),
 }
 
 
@@ -64,6 +65,7 @@ ATTN_CFGS = {
     "two_tiles": scaled("video", grid=(8, 24, 28), h=2, R=6),
     "ragged_blocks": scaled("video", grid=(6, 22, 30), h=2, R=9),
     "d64": scaled("video", grid=(5, 16, 16), h=2, D=64, R=3),
+    "two_tiles_b2": scaled("video", B=2, grid=(8, 24, 28), h=2, R=6),
 }
 
 

@@ -61,6 +61,8 @@ ROUTE_CFGS = {
     # (D = 96 splits the fp32 means inside the kernel)
     "video_d256": scaled("video", grid=(12, 16, 20), h=2, D=256, R=7),
     "video_d96": scaled("video", grid=(12, 16, 20), h=2, D=96, R=7),
+    # two batch entries: every batch stride and (b, h) item mapping
+    "video_b2": scaled("video", B=2, grid=(12, 16, 20), h=3, R=6),
 }
 
 
@@ -160,6 +162,8 @@ ATTN_CFGS = {
     "video_edge_30x16x16": scaled("video", grid=(30, 16, 16), h=2, R=13),
     "video_d64": scaled("video", grid=(9, 12, 20), h=2, D=64, R=5),
     "video_m32": scaled("video", grid=(8, 12, 16), h=2, block=(2, 4, 4), R=10),
+    "video_b2": scaled("video", B=2, grid=(12, 16, 20), h=3, R=6),
+    "video_m32_b2": scaled("video", B=2, grid=(8, 12, 16), h=2, block=(2, 4, 4), R=10),
 }
 
 
@@ -188,7 +192,7 @@ def test_attention_with_oracle_indices(name):
     assert np.abs(to64(lse) - ref_lse).max() <= 1e-3
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "video_12x16x20", "video_edge_30x16x16"])
+@pytest.mark.parametrize("name", ["tiny", "small", "video_12x16x20", "video_edge_30x16x16", "video_b2"])
 def test_full_pipeline(name):
     """Pool -> route -> TopK -> attention on the device, checked against the
     oracle's attention over the device's own index table."""

@@ -583,9 +583,12 @@ static hipError_t launch_route_t(const RouteParams& p, hipStream_t s) {
 // have similar quartile entries read overlapping windows of K/V; listing them
 // next to each other lets the workgroups that run at the same time share L2.
 // One workgroup per (b, h) sorts (Morton code of the three quartiles, 10 bits
-// each; block index) keys with a bitonic network in LDS.  Blocks below
-// num_first (the H3 context rows, whose lists hold every block) come first, in
-// index order.  The order changes no attention result.
+// each; block index) keys with a bitonic network: the compare-exchange stages
+// between elements less than 64 apart run inside a wave on registers (one
+// LDS load and store per element for all of them), the wider ones through LDS
+// with a barrier each.  Blocks below num_first (the H3 context rows, whose
+// lists hold every block) come first, in index order.  The order changes no
+// attention result.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t spread3_10(uint32_t v) {
   v &= 0x3ffu;
@@ -621,20 +624,50 @@ __global__ __launch_bounds__(1024) void item_order_kernel(const int32_t* __restr
     key[i] = kk;
   }
   __syncthreads();
-  for (int k = 2; k <= np; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < np; i += blockDim.x) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint64_t a = key[i], b = key[l];
-          if ((a > b) == ((i & k) == 0)) {
-            key[i] = b;
-            key[l] = a;
-          }
+  // compare-exchange of elements i and i ^ j, ascending where (i & k) == 0
+  auto lds_stage = [&](int k, int j) {
+    for (int i = threadIdx.x; i < np; i += blockDim.x) {
+      const int l = i ^ j;
+      if (l > i) {
+        const uint64_t a = key[i], b = key[l];
+        if ((a > b) == ((i & k) == 0)) {
+          key[i] = b;
+          key[l] = a;
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
+  };
+  if (np < 64) {
+    for (int k = 2; k <= np; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) lds_stage(k, j);
+  } else {
+    // stages k0..k1 (merge sizes) with j < 64 on 64-element chunks, one per wave
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    auto wave_stages = [&](int k0, int k1) {
+      for (int c = threadIdx.x >> 6; c < np / 64; c += nw) {
+        const int i = c * 64 + lane;
+        uint64_t v = key[i];
+        for (int k = k0; k <= k1; k <<= 1) {
+          const bool up = (i & k) == 0;
+          for (int j = min(k >> 1, 32); j > 0; j >>= 1) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, j, 64);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j, 64);
+            const uint64_t o = ((uint64_t)hi << 32) | lo;
+            const bool take_min = ((lane & j) == 0) == up;
+            v = (take_min == (o < v)) ? o : v;
+          }
+        }
+        key[i] = v;
+      }
+      __syncthreads();
+    };
+    wave_stages(2, 64);
+    for (int k = 128; k <= np; k <<= 1) {
+      for (int j = k >> 1; j >= 64; j >>= 1) lds_stage(k, j);
+      wave_stages(k, k);
+    }
+  }
   for (int i = threadIdx.x; i < J; i += blockDim.x) order[bh * J + i] = (int32_t)(uint32_t)key[i];
 }
 

@@ -73,3 +73,32 @@ def check_topk(got_idx, E, R, ref_idx, gap, cols=None, what="topk"):
     assert invalid == 0, "%s: %d exempt rows are not a valid top-%d" % (what, invalid, R)
     assert ok[~exempt].all(), what + ": a non-exempt row fails the validity check"
     return int(exempt.sum())
+
+
+def _spread3_10(v):
+    """Bits 0..9 of v moved to bits 0, 3, 6, ..., 27 (a Morton interleave)."""
+    out = np.zeros_like(v, dtype=np.uint64)
+    for t in range(10):
+        out |= ((v >> t) & 1).astype(np.uint64) << np.uint64(3 * t)
+    return out
+
+
+def expected_item_order(idx, num, num_first=0):
+    """The processing order the routing calls document, from an index table
+    (host arrays [B, H, J, kmax] and [B, H, J]): per (b, h), blocks sorted by
+    the Morton code of the entries at positions (n-1)//4, (n-1)//2 and
+    3(n-1)//4 of their kept list (each clamped to [0, J) and scaled to 10 bits
+    as v * 1024 // J; code bit 3t + c is bit t of entry c), ties by block
+    index, with blocks below num_first first in index order."""
+    B, H, J, kmax = idx.shape
+    n = np.minimum(num, kmax).astype(np.int64)
+    code = np.zeros((B, H, J), dtype=np.uint64)
+    pos = [np.maximum(n - 1, 0) // 4, np.maximum(n - 1, 0) // 2, 3 * np.maximum(n - 1, 0) // 4]
+    for c in range(3):
+        v = np.take_along_axis(idx, pos[c][..., None], axis=-1)[..., 0].astype(np.int64)
+        v = np.clip(v, 0, J - 1) * 1024 // J
+        code |= _spread3_10(v.astype(np.uint64)) << np.uint64(c)
+    code[n == 0] = 0
+    code[:, :, :num_first] = 0
+    keys = (code << np.uint64(32)) | np.arange(J, dtype=np.uint64)
+    return np.argsort(keys, axis=-1, kind="stable").astype(np.int32)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_attn_close, check_topk, to64
+from gpu_util import assert_attn_close, check_topk, expected_item_order, to64
 from workloads import h3_inputs, scaled, workload
 
 pytestmark = pytest.mark.gpu
@@ -186,6 +186,7 @@ def test_long_items_first_changes_no_result():
     o = order.cpu().numpy()
     assert P > 0 and (o[:, :, :P] == np.arange(P)).all()
     assert (np.sort(o, axis=-1) == np.arange(geom.J)).all()
+    assert np.array_equal(o, expected_item_order(idx.cpu().numpy(), num.cpu().numpy(), num_first=P))
     for nl in (P, geom.J):
         assert torch.equal(res[nl][0].view(torch.int16), res[0][0].view(torch.int16))
         assert torch.equal(res[nl][1], res[0][1])

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_attn_close, check_topk, to64
+from gpu_util import assert_attn_close, check_topk, expected_item_order, to64
 from workloads import scaled, vsa_inputs, workload
 
 pytestmark = pytest.mark.gpu
@@ -235,6 +235,7 @@ def test_item_order_is_permutation_and_changes_nothing():
     for b in range(B):
         for h in range(H):
             assert np.array_equal(np.sort(o_np[b, h]), np.arange(J))
+    assert np.array_equal(o_np, expected_item_order(idx.cpu().numpy(), num.cpu().numpy()))
     plain = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num)
     ordered = bsa.attention_vsa(x["q"], x["k"], x["v"], geom.perm, geom.block_len, J, geom.M, idx, num,
                                 item_order=order)
@@ -258,6 +259,21 @@ def test_item_order_is_permutation_and_changes_nothing():
     keep = torch.ones(N, dtype=torch.bool)
     keep[torch.as_tensor(toks, dtype=torch.long)] = False
     assert torch.equal(part[0, keep.to(DEV), 0].view(torch.int16), plain[0, keep.to(DEV), 0].view(torch.int16))
+
+
+@pytest.mark.parametrize("grid,R", [((30, 48, 80), 192), ((36, 48, 80), 200), ((8, 8, 8), 3)])
+def test_item_order_is_the_documented_sort(grid, R):
+    """The order equals the documented key sort computed on the host from the
+    device's own index table, for J = 1920 and 2160 (sort sizes 2048 and
+    4096) and J = 8 (below one wave's 64 elements)."""
+    cfg = scaled("video", grid=grid, h=2, R=R)
+    x = vsa_inputs(cfg, device=DEV)
+    geom = bsa.VsaGeometry(cfg["grid"], cfg["block"], device=DEV)
+    B, _, H, _ = x["q"].shape
+    order = torch.full((B, H, geom.J), -7, dtype=torch.int32, device=DEV)
+    idx, num = bsa.pool_route_topk(x["q"], x["k"], geom.perm, geom.block_len, geom.J, geom.M, R, item_order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), expected_item_order(idx.cpu().numpy(), num.cpu().numpy()))
 
 
 def test_edge_cases_index_table():

@@ -63,6 +63,9 @@ ROUTE_CFGS = {
     "video_d96": scaled("video", grid=(12, 16, 20), h=2, D=96, R=7),
     # two batch entries: every batch stride and (b, h) item mapping
     "video_b2": scaled("video", B=2, grid=(12, 16, 20), h=3, R=6),
+    # degenerate budgets: every block kept (R = J = 24) and a single block
+    "keep_all": scaled("video", grid=(8, 12, 16), h=2, R=24),
+    "one_block": scaled("video", grid=(4, 4, 4), h=2, R=1),
 }
 
 

@@ -160,3 +160,27 @@ def test_reblock_is_deterministic():
     p2, l2 = bsa.spark_reblock(x["q"], x["k"], M=M)
     torch.cuda.synchronize()
     assert torch.equal(p1, p2) and torch.equal(l1, l2)
+
+
+def test_two_batch_entries_equal_single_batch_runs():
+    """Batch strides and the per-(batch, head) tables: with two batch entries
+    the layout of entry b and the routed attention over it are bitwise those
+    of a run on entry b alone (which the tests above check against the
+    oracle)."""
+    cfg, M = scaled("video", B=2, grid=(8, 16, 16), h=2), 64
+    x = vsa_inputs(cfg, device=DEV)
+    B, N, H, D = x["q"].shape
+    J = -(-N // M)
+    R = max(1, J // 4)
+    perm2, len2 = bsa.spark_reblock(x["q"], x["k"], M=M)
+    out2, _, idx2, num2 = bsa.reblock_forward(x["q"], x["k"], x["v"], R, M=M)
+    torch.cuda.synchronize()
+    for b in range(B):
+        xb = {n: t[b:b + 1] for n, t in x.items()}
+        perm1, len1 = bsa.spark_reblock(xb["q"], xb["k"], M=M)
+        out1, _, idx1, num1 = bsa.reblock_forward(xb["q"], xb["k"], xb["v"], R, M=M)
+        torch.cuda.synchronize()
+        assert torch.equal(perm2[b * H:(b + 1) * H], perm1), "batch %d: layout differs" % b
+        assert torch.equal(len2, len1)
+        assert torch.equal(idx2[b], idx1[0]) and torch.equal(num2[b], num1[0]), "batch %d: index table" % b
+        assert torch.equal(out2[b].view(torch.int16), out1[0].view(torch.int16)), "batch %d: output" % b

@@ -428,10 +428,14 @@ static bsa_status check_qouter(const bsa_qouter_args* a) {
     if (!a->perm || !a->block_len || !a->q2k_idx || !a->q2k_num)
       return fail(BSA_ERR_ARG, "bsa_forward_qouter: perm, block_len, q2k_idx, q2k_num are required");
     if (a->J < 1 || a->kmax < 1) return fail(BSA_ERR_SHAPE, "bsa_forward_qouter: J and kmax must be positive");
-    if (a->M != 16 && a->M != 32 && a->M != 64)
-      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block capacity M must be 16, 32 or 64");
-    if ((int64_t)a->dq.B * a->dq.H * a->J >= (int64_t)1 << 31)
-      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks");
+    if (a->M != 16 && a->M != 32 && a->M != 64 && a->M != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block capacity M must be 16, 32, 64 or 128");
+    // capacity 128 runs as 64-token halves: twice the query blocks and kept entries
+    const int64_t halves = a->M == 128 ? 2 : 1;
+    if ((int64_t)a->dq.B * a->dq.H * a->J * halves >= (int64_t)1 << 31 || a->kmax * halves >= (int64_t)1 << 30)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks or kept entries");
+    if (a->M == 128 && (a->coarse || a->gate))
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: the coarse branch needs block capacity <= 64");
     if (a->dt == BSA_BF16) {  // the kernels address one (batch, head) K/V slice with 32-bit offsets
       const int64_t slice = (a->dkv.N - 1) * a->dkv.sN * 2 + a->dkv.D * 2;
       if (slice >= (int64_t)1 << 32 || a->dkv.N >= (int64_t)1 << 24 || a->dkv.sN * 2 >= (int64_t)1 << 24)
@@ -465,8 +469,8 @@ static bsa_status check_qouter(const bsa_qouter_args* a) {
     if (a->dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: token mode needs bf16");
     if (!a->blk_idx) return fail(BSA_ERR_ARG, "bsa_forward_qouter: blk_idx is required");
     if (a->S < 1 || a->S > 64) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: S must lie in [1, 64]");
-    if (a->BS != 32 && a->BS != 64 && a->BS != 128)
-      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block size BS must be 32, 64 or 128");
+    if (a->BS != 16 && a->BS != 32 && a->BS != 64 && a->BS != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: block size BS must be 16, 32, 64 or 128");
     const int64_t G = a->dq.H / a->dkv.H;
     const int64_t items = a->dq.B * a->dq.N * a->dkv.H * ((G + 15) / 16);
     if (items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many tokens");
@@ -475,17 +479,59 @@ static bsa_status check_qouter(const bsa_qouter_args* a) {
   return fail(BSA_ERR_ARG, "bsa_forward_qouter: unknown mode %d", a->mode);
 }
 
+// Index tables of a capacity-128 call rewritten for 64-token halves:
+// kept lists, counts, half lengths and (when given) the processing order.
+struct HalfTables {
+  size_t idx, num, len, order;
+  size_t total() const { return idx + num + len + order; }
+};
+static HalfTables half_tables(const bsa_qouter_args* a) {
+  HalfTables t{0, 0, 0, 0};
+  if (a->mode != BSA_SEL_BLOCK || a->M != 128) return t;
+  const size_t rows = (size_t)a->dq.B * a->dq.H * 2 * a->J;
+  t.idx = round_up(rows * 2 * a->kmax * sizeof(int32_t));
+  t.num = round_up(rows * sizeof(int32_t));
+  t.len = round_up((size_t)2 * a->J * sizeof(int32_t));
+  t.order = a->item_order ? round_up(rows * sizeof(int32_t)) : 0;
+  return t;
+}
+
 // Workspace of bsa_forward_qouter: the scheduler state of the block-mode
-// persistent grid (bf16); none for the fp32 and token modes.
-static size_t qouter_ws_need(const bsa_qouter_args* a) {
+// persistent grid (bf16; none for the fp32 and token modes), then the half
+// tables of a capacity-128 call.
+static size_t qouter_sched_need(const bsa_qouter_args* a) {
   return (a->mode == BSA_SEL_BLOCK && a->dt == BSA_BF16) ? bsa::qouter_sched_bytes() : 0;
 }
+static size_t qouter_ws_need(const bsa_qouter_args* a) { return qouter_sched_need(a) + half_tables(a).total(); }
 
 // Launches a validated call with `sched` as the scheduler state (nullptr when
 // the mode needs none).
 static bsa_status launch_qouter(const bsa_qouter_args* a, void* sched, void* stream) {
   const float scale_log2 = a->scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
+  if (a->mode == BSA_SEL_BLOCK && a->M == 128) {
+    // the same attention over 64-token halves: rewrite the tables behind the
+    // scheduler state, then run the capacity-64 kernels on them
+    const HalfTables t = half_tables(a);
+    char* w = static_cast<char*>(sched) + qouter_sched_need(a);
+    int32_t* idx2 = reinterpret_cast<int32_t*>(w);
+    int32_t* num2 = reinterpret_cast<int32_t*>(w + t.idx);
+    int32_t* len2 = reinterpret_cast<int32_t*>(w + t.idx + t.num);
+    int32_t* ord2 = a->item_order ? reinterpret_cast<int32_t*>(w + t.idx + t.num + t.len) : nullptr;
+    hipError_t e = bsa::launch_expand_halves(a->q2k_idx, a->q2k_num, a->block_len, a->item_order,
+                                             (int)(a->dq.B * a->dq.H), a->J, a->kmax, idx2, num2, len2, ord2, s);
+    if (e != hipSuccess) return hip_status(e, "half-block tables launch");
+    bsa_qouter_args h = *a;
+    h.M = 64;
+    h.J = 2 * a->J;
+    h.kmax = 2 * a->kmax;
+    h.q2k_idx = idx2;
+    h.q2k_num = num2;
+    h.block_len = len2;
+    h.item_order = ord2;
+    h.order_long = 2 * a->order_long;
+    return launch_qouter(&h, qouter_sched_need(a) ? sched : nullptr, stream);
+  }
   if (a->mode == BSA_SEL_BLOCK) {
     bsa::VsaAttnParams p{a->q, a->k, a->v, a->out,
                          a->dq.sB, a->dq.sN, a->dq.sH, a->dkv.sB, a->dkv.sN, a->dkv.sH,

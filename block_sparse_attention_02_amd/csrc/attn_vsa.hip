@@ -243,7 +243,7 @@ __device__ __forceinline__ void vsa_attn_item(const VsaAttnParams& p, int wid_in
 
   // ---- query rows: B operand of S^T, lane l holds row 32w + l%32 ----
   const int qrow = 32 * w + (lane & 31);
-  const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
+  const int qtok = max(perm[(int64_t)i * M + max(min(qrow, ni - 1), 0)], 0);  // empty block: token 0, no output
   bf16x8 qop[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
@@ -779,7 +779,7 @@ __device__ __forceinline__ void vsa4_item(const VsaAttnParams& p, int wid_in, __
 
   // ---- query rows: B operand of S^T, lane l holds row 32hq + l%32 ----
   const int qrow = 32 * hq + (lane & 31);
-  const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
+  const int qtok = max(perm[(int64_t)i * M + max(min(qrow, ni - 1), 0)], 0);  // empty block: token 0, no output
   bf16x8 qop[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qop[s] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * s + 8 * h2);
@@ -1213,7 +1213,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const auto sel = as_const(p.q2k_idx) + (bh * p.J + i) * p.kmax;
     const int T = out_ok ? min(as_const(p.q2k_num)[bh * p.J + i], p.kmax) : 0;
     const int ni = blen[i];
-    const int qtok = perm[(int64_t)i * M + min(qrow, ni - 1)];
+    const int qtok = max(perm[(int64_t)i * M + max(min(qrow, ni - 1), 0)], 0);  // empty block: token 0, no output
     bf16x8 qop[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) qop[k] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * k + 8 * h2);
@@ -1487,7 +1487,7 @@ __global__ __launch_bounds__(128) void vsa_attn_f32_kernel(VsaAttnParams p) {
   const float* qg = reinterpret_cast<const float*>(p.q) + b * p.q_sB + hh * p.q_sH;
   const float* kg = reinterpret_cast<const float*>(p.k) + b * p.kv_sB + hh * p.kv_sH;
   const float* vg = reinterpret_cast<const float*>(p.v) + b * p.kv_sB + hh * p.kv_sH;
-  const int qtok = perm[(int64_t)i * p.M + min(row, ni - 1)];
+  const int qtok = max(perm[(int64_t)i * p.M + max(min(row, ni - 1), 0)], 0);  // empty block: token 0, no output
   float qv[HD], ov[HD];
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
@@ -1586,6 +1586,54 @@ static hipError_t launch_vsa_d(const VsaAttnParams& p, hipStream_t s) {
   if (p.M <= 32) return launch_vsa_mt<D, 32>(p, s);
   if (p.k_sum) return p.lse ? launch_vsa4<D, true, true>(p, s) : launch_vsa4<D, false, true>(p, s);
   return p.lse ? launch_vsa_pp<D, true>(p, s) : launch_vsa_pp<D, false>(p, s);
+}
+
+// Index tables of block capacity 128 rewritten for 64-token halves (see
+// launch_expand_halves).  One thread per entry of the new kept lists; the
+// first threads also write the half lengths and the processing order.  A
+// negative kept id stays -1 in both halves, an id at or beyond J becomes 2J
+// (still out of range, so the attention kernels skip and report it).
+__global__ __launch_bounds__(256) void expand_halves_kernel(const int32_t* __restrict__ q2k,
+                                                            const int32_t* __restrict__ num,
+                                                            const int32_t* __restrict__ blen,
+                                                            const int32_t* __restrict__ order, int BH, int J,
+                                                            int kmax, int32_t* __restrict__ q2k2,
+                                                            int32_t* __restrict__ num2, int32_t* __restrict__ blen2,
+                                                            int32_t* __restrict__ order2) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t J2 = 2 * (int64_t)J, K2 = 2 * (int64_t)kmax;
+  if (id < (int64_t)BH * J2 * K2) {
+    const int e2 = (int)(id % K2);
+    const int64_t row2 = id / K2;  // bh * 2J + i2
+    const int64_t bh = row2 / J2;
+    const int i = (int)((row2 % J2) >> 1), e = e2 >> 1;
+    const int n = max(min(num[bh * J + i], kmax), 0);
+    int out = -1;
+    if (e < n) {
+      const int v = q2k[(bh * J + i) * kmax + e];
+      out = v < 0 ? -1 : (v >= J ? (int)J2 : 2 * v + (e2 & 1));
+    }
+    q2k2[id] = out;
+    if (e2 == 0) num2[row2] = 2 * n;
+  }
+  if (id < J2) {
+    const int n = blen[id >> 1], lo = max(min(n, 64), 0);
+    blen2[id] = (id & 1) ? max(n - lo, 0) : lo;
+  }
+  if (order && id < (int64_t)BH * J2) {
+    const int64_t bh = id / J2;
+    const int o = order[bh * J + ((id % J2) >> 1)];
+    order2[id] = (o >= 0 && o < J) ? 2 * o + (int)(id & 1) : -1;
+  }
+}
+
+hipError_t launch_expand_halves(const int32_t* q2k, const int32_t* num, const int32_t* blen, const int32_t* order,
+                                int BH, int J, int kmax, int32_t* q2k2, int32_t* num2, int32_t* blen2,
+                                int32_t* order2, hipStream_t s) {
+  const int64_t n = std::max<int64_t>((int64_t)BH * 2 * J * 2 * kmax, 2 * (int64_t)J);
+  expand_halves_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(q2k, num, blen, order, BH, J, kmax,
+                                                                              q2k2, num2, blen2, order2);
+  return hipGetLastError();
 }
 
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s) {

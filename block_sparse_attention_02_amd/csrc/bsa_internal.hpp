@@ -166,6 +166,14 @@ struct VsaAttnParams {
 // Bytes of the persistent-grid scheduler state the block-mode kernels use.
 size_t qouter_sched_bytes();
 hipError_t launch_vsa_attention(const VsaAttnParams& p, bool f32_io, hipStream_t s);
+// Block capacity 128 as pairs of 64-token halves (same tokens, same perm
+// table): query block i becomes halves 2i and 2i+1, both with the kept list
+// of i, and kept block j becomes halves 2j and 2j+1; half lengths min(n, 64)
+// and n - min(n, 64).  Writes q2k2 [BH, 2J, 2*kmax], num2 [BH, 2J],
+// blen2 [2J] and, when order is given, order2 [BH, 2J].
+hipError_t launch_expand_halves(const int32_t* q2k, const int32_t* num, const int32_t* blen, const int32_t* order,
+                                int BH, int J, int kmax, int32_t* q2k2, int32_t* num2, int32_t* blen2,
+                                int32_t* order2, hipStream_t s);
 
 struct NsaAttnParams {
   const void* q;

@@ -280,17 +280,22 @@ bsa_status h3_pool_route_topk(const h3_route_args* a, void* ws, size_t ws_bytes,
  * Supported: D in {64, 128}.  dt = BF16 runs on the matrix cores (bf16
  * products, fp32 accumulation and softmax, bf16 output); dt = F32 (block mode
  * only) is computed entirely in fp32 on the vector ALUs and meant for small
- * problems.  VSA block capacity M in {16, 32, 64}; NSA (bf16 only) block size
- * BS in {32, 64, 128}, S <= 64.  Block mode in bf16 addresses one (batch,
+ * problems.  VSA block capacity M in {16, 32, 64, 128}; NSA (bf16 only) block
+ * size BS in {16, 32, 64, 128}, S <= 64.  Capacity 128 runs as 64-token
+ * halves of every block (the same keys per query, so the same attention; the
+ * halves' index tables go in the workspace) and takes no summaries and no
+ * coarse branch.  Block mode in bf16 addresses one (batch,
  * head) K/V slice with 32-bit byte offsets: it needs N < 2^24, a token stride
  * (dkv.sN) below 2^23 elements and (N - 1) * dkv.sN + D below 2^31 elements;
  * anything larger returns BSA_ERR_UNSUPPORTED.
  *
  * Workspace: bsa_qouter_ws() bytes (256-byte aligned, caller-owned, contents
- * undefined after the call; 0 bytes in token mode and for fp32).  Block mode
- * in bf16 keeps the work counters of its persistent grid there (cleared by a
- * kernel on `stream` before every launch), so two calls with different
- * workspaces can run concurrently on different streams.
+ * undefined after the call; 0 bytes in token mode and for fp32 at capacity
+ * <= 64).  Block mode in bf16 keeps the work counters of its persistent grid
+ * there (cleared by a kernel on `stream` before every launch), so two calls
+ * with different workspaces can run concurrently on different streams;
+ * capacity 128 adds its half tables (B*H*2J*(2*kmax + 2) + 2J int32), so its
+ * size depends on the shapes.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* q;

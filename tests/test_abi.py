@@ -101,7 +101,7 @@ def _qouter_args(**kw):
 @pytest.mark.parametrize("field,value,status", [
     ("v", None, L.BSA_ERR_ARG),
     ("perm", None, L.BSA_ERR_ARG),
-    ("M", 128, L.BSA_ERR_UNSUPPORTED),
+    ("M", 256, L.BSA_ERR_UNSUPPORTED),
     ("M", 48, L.BSA_ERR_UNSUPPORTED),
     ("mode", 9, L.BSA_ERR_ARG),
     ("q", ctypes.c_void_p(258), L.BSA_ERR_SHAPE),
@@ -138,6 +138,37 @@ def test_qouter_workspace():
     assert lib.bsa_qouter_ws(ctypes.byref(f32), ctypes.byref(n)) == L.BSA_OK and n.value == 0
     tok = _qouter_args(mode=L.BSA_SEL_TOKEN, blk_idx=ctypes.c_void_p(256), S=16, BS=64)
     assert lib.bsa_qouter_ws(ctypes.byref(tok), ctypes.byref(n)) == L.BSA_OK and n.value == 0
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_qouter_capacity_128_workspace_and_limits():
+    """Capacity 128 runs as 64-token halves: the workspace adds the halves'
+    kept lists (B*H*2J rows of 2*kmax), counts (B*H*2J), lengths (2J) and,
+    with an item order, the halves' order (B*H*2J), each rounded up to 256
+    bytes; it takes no coarse branch."""
+    lib = L.load()
+    n = ctypes.c_size_t()
+    sched = ctypes.c_size_t()
+    assert lib.bsa_qouter_ws(ctypes.byref(_qouter_args()), ctypes.byref(sched)) == L.BSA_OK
+    d = L.TDesc(2, 4096, 3, 64, 4096 * 3 * 64, 3 * 64, 64)
+    a = _qouter_args(dq=d, dkv=d, dout=d, J=32, M=128, kmax=5)
+    rows = 2 * 3 * 2 * 32
+    tables = _r256(rows * 10 * 4) + _r256(rows * 4) + _r256(64 * 4)
+    assert lib.bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    assert n.value == sched.value + tables
+    a.item_order = ctypes.c_void_p(256)
+    assert lib.bsa_qouter_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    assert n.value == sched.value + tables + _r256(rows * 4)
+    f32 = _qouter_args(dq=d, dkv=d, dout=d, J=32, M=128, kmax=5, dt=L.BSA_F32)
+    assert lib.bsa_qouter_ws(ctypes.byref(f32), ctypes.byref(n)) == L.BSA_OK and n.value == tables
+    co = _qouter_args(M=128, coarse=ctypes.c_void_p(256), gate=ctypes.c_void_p(256))
+    assert lib.bsa_qouter_ws(ctypes.byref(co), ctypes.byref(n)) == L.BSA_ERR_UNSUPPORTED
+    assert b"coarse" in lib.bsa_last_error()
+    big = _qouter_args(M=128, kmax=1 << 29)
+    assert lib.bsa_qouter_ws(ctypes.byref(big), ctypes.byref(n)) == L.BSA_ERR_UNSUPPORTED
 
 
 def test_check_without_a_device_is_an_error_not_a_crash():

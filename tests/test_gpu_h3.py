@@ -105,6 +105,8 @@ ATTN_CFGS = {
     "r2v_m32": scaled("h3", segments=[77, (4, 8, 12), 30, (6, 16, 20)], block=(2, 4, 4), h=2, keep=0.25),
     "two_refs_d64": scaled("h3", segments=[40, (4, 8, 8), (4, 8, 12), 19, (8, 12, 16)], h=2, D=64, keep=0.2),
     "r2v_m64_b2": scaled("h3", B=2, segments=[77, (4, 8, 12), 30, (6, 16, 20)], h=2, keep=0.25),
+    # tiles of 128 tokens, the capacity of the page's own layout example
+    "r2v_m128": scaled("h3", segments=[300, (8, 16, 12), 90, (12, 16, 20)], block=(4, 8, 4), h=2, keep=0.25),
 }
 
 

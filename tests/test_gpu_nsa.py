@@ -22,6 +22,7 @@ CASES = {
     "g16_bs128": scaled("nsa", T=1100, HQ=16, H=1, BS=128, S=6),
     "g4_d64_ragged": scaled("nsa", T=999, HQ=8, H=2, D=64, S=12),
     "g16_bs64_b2": scaled("nsa", B=2, T=600, HQ=32, H=2),
+    "g16_bs16": scaled("nsa", T=400, HQ=16, H=2, BS=16, S=10),
 }
 
 

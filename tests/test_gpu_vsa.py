@@ -167,6 +167,11 @@ ATTN_CFGS = {
     "video_m32": scaled("video", grid=(8, 12, 16), h=2, block=(2, 4, 4), R=10),
     "video_b2": scaled("video", B=2, grid=(12, 16, 20), h=3, R=6),
     "video_m32_b2": scaled("video", B=2, grid=(8, 12, 16), h=2, block=(2, 4, 4), R=10),
+    # capacity 128 (4 x 8 x 4 blocks) runs as 64-token halves; ragged edges give
+    # blocks of at most 64 tokens, whose second half is empty
+    "video_m128_ragged": scaled("video", grid=(10, 20, 18), block=(4, 8, 4), h=2, R=5),
+    "video_m128_b2": scaled("video", B=2, grid=(8, 16, 16), block=(4, 8, 4), h=2, R=4),
+    "tiny_f32_m128": scaled("tiny", grid=(8, 8, 8), block=(4, 8, 4), R=2),
 }
 
 
@@ -195,7 +200,8 @@ def test_attention_with_oracle_indices(name):
     assert np.abs(to64(lse) - ref_lse).max() <= 1e-3
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "video_12x16x20", "video_edge_30x16x16", "video_b2"])
+@pytest.mark.parametrize("name", ["tiny", "small", "video_12x16x20", "video_edge_30x16x16", "video_b2",
+                                  "video_m128_ragged"])
 def test_full_pipeline(name):
     """Pool -> route -> TopK -> attention on the device, checked against the
     oracle's attention over the device's own index table."""

@@ -840,7 +840,8 @@ static bsa_status check_kvouter(const bsa_kvouter_args* a, bsa::KvOuterParams* o
     return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: D must be 64 or 128 for q and k/v");
   if (a->dq.B != a->dkv.B || a->dq.N != a->dkv.N) return fail(BSA_ERR_SHAPE, "bsa_forward_kvouter: B/N mismatch");
   if (a->dq.H % a->dkv.H) return fail(BSA_ERR_SHAPE, "bsa_forward_kvouter: Hq must be a multiple of Hkv");
-  if (a->BK != 64 && a->BK != 128) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: BK must be 64 or 128");
+  if (a->BK != 16 && a->BK != 32 && a->BK != 64 && a->BK != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: BK must be 16, 32, 64 or 128");
   if (a->k_sel < 1 || a->k_sel > 64) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_kvouter: k_sel must lie in [1, 64]");
   if (a->chunk_cap < 0) return fail(BSA_ERR_ARG, "bsa_forward_kvouter: chunk_cap must be >= 0");
   if (!std::isfinite(a->scale)) return fail(BSA_ERR_ARG, "bsa_forward_kvouter: scale must be finite");

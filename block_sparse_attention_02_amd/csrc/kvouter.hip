@@ -345,8 +345,9 @@ __global__ __launch_bounds__(512) void kv_k1w_kernel(KvOuterParams p, int NB, co
   const int r = (rid / NB) % p.Hkv;
   const int b = rid / (NB * p.Hkv);
   const int G = p.Hq / p.Hkv;
-  const int64_t k0 = (int64_t)blk * BK;
-  const int nkeys = (int)min((int64_t)BK, p.N - k0);
+  // block size p.BK <= BK (16 and 32 run in 64-key tiles with the rest masked)
+  const int64_t k0 = (int64_t)blk * p.BK;
+  const int nkeys = (int)min((int64_t)p.BK, p.N - k0);
 
   const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(p.k) + b * p.kv_sB + r * p.kv_sH;
   const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(p.v) + b * p.kv_sB + r * p.kv_sH;

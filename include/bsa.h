@@ -519,7 +519,8 @@ bsa_status spark_reblock(const spark_reblock_args* a, void* ws, size_t ws_bytes,
  *      go to the preassigned slot: o_buf[b,s,i,hq,:] (bf16) and
  *      lse_buf[b,s,i,hq] (fp32), so no accumulation and no atomics touch them.
  *      An empty J_s gives L_s = -inf and O_s = 0.
- *   q [B,N,Hq,D] and k/v [B,N,Hkv,D] strided, bf16, D = 128 or 64, BK in {64, 128}.
+ *   q [B,N,Hq,D] and k/v [B,N,Hkv,D] strided, bf16, D = 128 or 64, BK in {16, 32, 64, 128}
+ *   (16 and 32 run in 64-key tiles with the keys past the block masked).
  *   o_buf bf16 [B, k_sel, N, Hq, D], lse_buf fp32 [B, k_sel, N, Hq] and
  *   nslot int32 [B, N, Hkv], all contiguous, live until bsa_combine.  Slots at
  *   or beyond nslot are left untouched.

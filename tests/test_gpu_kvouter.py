@@ -89,6 +89,7 @@ INDEX_CASES = {
     # Hkv * NB = 8 * 1025 exceeds the 8192 bins of the LDS histogram: the
     # global count / scatter kernels build the index
     "global_count_scatter": (1, 65600, 8, 8, 64, 64, 2, True, 0, True),
+    "bk16_counts": (1, 800, 4, 2, 64, 16, 6, True, 0, True),
 }
 
 
@@ -142,6 +143,9 @@ CASES = {
     "msa_g8_bk64_d64": (scaled("msa", N=1500, Hq=16, Hkv=2, BK=64, D=64, k=8), True),
     "msa_noncausal": (scaled("msa", N=1024, Hq=16, Hkv=1, k=6), False),
     "msa_b2": (scaled("msa", B=2, N=1100, Hq=16, Hkv=2, k=6), True),
+    # blocks smaller than the 64-key tile: the rest of the tile is masked
+    "msa_bk32": (scaled("msa", N=700, Hq=16, Hkv=2, BK=32, k=8), True),
+    "msa_bk16_d64_noncausal": (scaled("msa", N=500, Hq=16, Hkv=1, BK=16, D=64, k=10), False),
 }
 
 

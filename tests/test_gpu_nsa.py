@@ -23,6 +23,7 @@ CASES = {
     "g4_d64_ragged": scaled("nsa", T=999, HQ=8, H=2, D=64, S=12),
     "g16_bs64_b2": scaled("nsa", B=2, T=600, HQ=32, H=2),
     "g16_bs16": scaled("nsa", T=400, HQ=16, H=2, BS=16, S=10),
+    "g1_mha": scaled("nsa", T=500, HQ=3, H=3, S=6),          # one query head per KV head
 }
 
 

@@ -436,6 +436,8 @@ static bsa_status check_qouter(const bsa_qouter_args* a) {
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: too many query blocks or kept entries");
     if (a->M == 128 && (a->coarse || a->gate))
       return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: the coarse branch needs block capacity <= 64");
+    if (a->M == 128 && (int64_t)a->dq.B * a->dq.H * 2 * a->J * 2 * a->kmax >= (int64_t)1 << 37)
+      return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_qouter: the half tables of capacity 128 would be too large");
     if (a->dt == BSA_BF16) {  // the kernels address one (batch, head) K/V slice with 32-bit offsets
       const int64_t slice = (a->dkv.N - 1) * a->dkv.sN * 2 + a->dkv.D * 2;
       if (slice >= (int64_t)1 << 32 || a->dkv.N >= (int64_t)1 << 24 || a->dkv.sN * 2 >= (int64_t)1 << 24)

@@ -1284,6 +1284,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // ---------------- S_s: copies for later blocks, softmax of block s ----------------
       wait_vmcnt<2 * LPT>();  // the ids at the head of the last batch (own copies only)
       phase();
+      // A block of at most 32 tokens leaves key half 1 with masked keys only:
+      // its weights are exact zeros, so those waves skip the block's products.
+      const bool idle_s = g == 1 && nj <= 32;
       {
         // batch: ids(s+3), K(s+2) with the rows of block s+2, V(s+1) with those of s+1
         stage_ids(prs, max(jc, 0), M, ring_lds((s + 3) & 3), lane);
@@ -1353,7 +1356,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // ---------------- M_{s+1}: PV(s), then S^T of block s+1 ----------------
       wait_vmcnt<2 * LPT + 1>();  // every batch but the last one
       phase();
-      {
+      if (!idle_s) {
         const uint32_t vb = (s & 1) ? (uint32_t)(TILE * 2) : 0u;
         bf16x8 va[NP];
 #pragma unroll
@@ -1375,7 +1378,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < T) qk(s + 1);
+      if (s + 1 < T && !(g == 1 && nj <= 32)) qk(s + 1);  // nj: length of block s+1 here
     }
 
     // ---------------- E0: key half 1 hands its state to key half 0 ----------------

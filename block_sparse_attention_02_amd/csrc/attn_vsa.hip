@@ -1214,6 +1214,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int T = out_ok ? min(as_const(p.q2k_num)[bh * p.J + i], p.kmax) : 0;
     const int ni = blen[i];
     const int qtok = max(perm[(int64_t)i * M + max(min(qrow, ni - 1), 0)], 0);  // empty block: token 0, no output
+    // a query block of at most 32 tokens leaves query half 1 with no row to
+    // write: those waves only copy tiles and pass the barriers
+    const bool qidle = hq == 1 && ni <= 32;
     bf16x8 qop[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) qop[k] = load8_bf16<__bf16>(qg + (int64_t)qtok * p.q_sN + 16 * k + 8 * h2);
@@ -1279,7 +1282,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---------------- M_0: S^T of block 0 ----------------
     wait_vmcnt<2 * LPT>();  // K(0) of the prologue batch K(0), V(0), K(1)
     phase();
-    if (T > 0) qk(0);
+    if (T > 0 && !qidle) qk(0);
     for (int s = 0; s < T; ++s) {
       // ---------------- S_s: copies for later blocks, softmax of block s ----------------
       wait_vmcnt<2 * LPT>();  // the ids at the head of the last batch (own copies only)
@@ -1304,46 +1307,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int njn = (ja >= 0) ? blen[max(ja, 0)] : 0;
       __builtin_amdgcn_sched_barrier(0);
 
-      if (nj < M) {  // edge / short block: mask keys at or beyond its true length
+      // the softmax of block s: skipped by waves whose rows are never written
+      // or whose keys of block s are all masked
+      if (!qidle && !idle_s) {
+        if (nj < M) {  // edge / short block: mask keys at or beyond its true length
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
-          sacc[r] = (key < nj) ? sacc[r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int key = TM::key_of_row(32 * g + 8 * (r >> 2) + 4 * h2 + (r & 3));
+            sacc[r] = (key < nj) ? sacc[r] : -INFINITY;
+          }
         }
-      }
-      float mx = -INFINITY;
+        float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
-      // lazy rescale (as in the four-wave kernel): the reference moves only
-      // when some row's maximum grew by more than 8 in log2 units
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-        if constexpr (LSE) lx_run *= alpha;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+        // lazy rescale (as in the four-wave kernel): the reference moves only
+        // when some row's maximum grew by more than 8 in log2 units
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = fast_exp2(m_run - m_new);
+          l_run *= alpha;
+          if constexpr (LSE) lx_run *= alpha;
 #pragma unroll
-        for (int d = 0; d < DT; ++d)
+          for (int d = 0; d < DT; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f, rsx = 0.f;
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * hlf + 2 * e;
-          const float a = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -m_use));
-          const float c = fast_exp2(__builtin_fmaf(sacc[r + 1], p.scale_log2, -m_use));
-          pk[e] = pack2_bf16_sum<LSE>(a, c, &rs, &rsx);
+            for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+          m_run = m_new;
         }
-        pop[hlf] = __builtin_bit_cast(bf16x8, pk);
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float rs = 0.f, rsx = 0.f;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * hlf + 2 * e;
+            const float a = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -m_use));
+            const float c = fast_exp2(__builtin_fmaf(sacc[r + 1], p.scale_log2, -m_use));
+            pk[e] = pack2_bf16_sum<LSE>(a, c, &rs, &rsx);
+          }
+          pop[hlf] = __builtin_bit_cast(bf16x8, pk);
+        }
+        l_run += rs;
+        if constexpr (LSE) lx_run += rsx;
       }
-      l_run += rs;
-      if constexpr (LSE) lx_run += rsx;
       nj = njn;
       ja = jb;
       jb = jc;
@@ -1356,7 +1363,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // ---------------- M_{s+1}: PV(s), then S^T of block s+1 ----------------
       wait_vmcnt<2 * LPT + 1>();  // every batch but the last one
       phase();
-      if (!idle_s) {
+      if (!idle_s && !qidle) {
         const uint32_t vb = (s & 1) ? (uint32_t)(TILE * 2) : 0u;
         bf16x8 va[NP];
 #pragma unroll
@@ -1378,7 +1385,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < T && !(g == 1 && nj <= 32)) qk(s + 1);  // nj: length of block s+1 here
+      if (s + 1 < T && !(g == 1 && nj <= 32) && !qidle) qk(s + 1);  // nj: length of block s+1 here
     }
 
     // ---------------- E0: key half 1 hands its state to key half 0 ----------------

@@ -64,10 +64,12 @@ def test_concurrent_streams_match_serial_runs():
     assert _check_status() == L.BSA_OK
 
 
-@pytest.mark.parametrize("case", ["m64", "m32", "f32"])
+@pytest.mark.parametrize("case", ["m64", "m32", "f32", "m128"])
 def test_block_id_past_J_is_skipped_and_reported(case):
     if case == "m64":
         cfg, x, geom, idx, num = _video_case((8, 16, 20), 2, 6)
+    elif case == "m128":  # capacity 128 runs as halves: an id past J stays past the halves' count
+        cfg, x, geom, idx, num = _video_case((10, 20, 18), 2, 5, block=(4, 8, 4))
     elif case == "m32":
         cfg, x, geom, idx, num = _video_case((8, 12, 16), 2, 10, block=(2, 4, 4))
     else:

@@ -620,7 +620,10 @@ __global__ __launch_bounds__(1024) void kv_combine_kernel(CombineParams p) {
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         const int64_t row = row0 + (int64_t)min(s0 + u, n - 1) * sstride;
-        o[u] = *reinterpret_cast<const bf16x8*>(p.o_buf + row * p.D + dc * 8);
+        // each partial is read once: a streaming load keeps it from displacing
+        // the rows the other workgroups still need
+        o[u] = __builtin_bit_cast(
+            bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.o_buf + row * p.D + dc * 8)));
         l[u] = p.lse_buf[row];
       }
 #pragma unroll

@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void moment_partial_kernel(const __bf16* __res
     for (int u = 0; u < LD; ++u) {
       const int e = threadIdx.x + 256 * u, r = e / CPR, cc = e % CPR;
       v[u] = bf16x8{};
-      if (base + r < t1) v[u] = *reinterpret_cast<const bf16x8*>(src + (int64_t)(base + r) * sN + cc * 8);
+      if (base + r < t1)  // streaming load: every row is read once
+        v[u] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(base + r) * sN + cc * 8)));
     }
   };
   // lane's share of the transposing reads: 16-lane group g16, lane jl in it
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(256) void key_feature_kernel(const __bf16* __restri
     for (int q = 0; q < LDT; ++q) {
       const int e = threadIdx.x + 256 * q, r = e / CPR, c = e % CPR;
       v[q] = bf16x8{};
-      if (t0 + r < te) v[q] = *reinterpret_cast<const bf16x8*>(src + (int64_t)(t0 + r) * sN + 8 * c);
+      if (t0 + r < te)  // streaming load: every row is read once
+        v[q] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(t0 + r) * sN + 8 * c)));
     }
   };
   auto swz = [](int r, int c) { return c ^ (r & (CPR - 1)); };

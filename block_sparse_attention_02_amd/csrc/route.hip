@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p, int nsplit) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
           const T* row = xb + (int64_t)members[u][min(r + rr, n - 1)] * p.sN;
-          v[rr][u] = *reinterpret_cast<const Vec*>(row + off[u]);
+          // streaming loads: every row is read once
+          v[rr][u] = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(row + off[u]));
         }
       }
 #pragma unroll

@@ -37,7 +37,8 @@ __global__ __launch_bounds__(1024) void anchor_partial_kernel(const __bf16* __re
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int t = t0; t < t1; ++t) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (int64_t)t * sN);
+      const bf16x8 v =  // streaming load: every row is read once
+          __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)t * sN)));
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
     }
@@ -94,8 +95,9 @@ __global__ __launch_bounds__(256) void summary_kernel(SummaryParams p) {
   for (int st = 0; st < STEPS; ++st) {
     const int r = st * RPI + sub;
     const int64_t tok = members[min(r, n - 1)];
-    kr[st] = *reinterpret_cast<const bf16x8*>(kg + tok * p.sN);
-    vr[st] = *reinterpret_cast<const bf16x8*>(vg + tok * p.sN);
+    // streaming loads: every key and value row is read once
+    kr[st] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + tok * p.sN)));
+    vr[st] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + tok * p.sN)));
   }
 
   // logits of the rows against the anchor (every lane of a row ends with it)

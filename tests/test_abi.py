@@ -294,6 +294,26 @@ def test_h3_route_validation(spans, budgets, kw, status):
         assert n.value == 2 * 10 * 64 * 4 + planes
 
 
+def test_route_alignment_checks():
+    """Pooled means given by the caller, and the workspace, must be 16-byte
+    aligned (the key planes and means are read and written 16 bytes at a
+    time); both calls refuse otherwise before anything is enqueued."""
+    lib = L.load()
+    n = ctypes.c_size_t()
+    a, keep = _h3_args([2, 5, 5, 10], [1, 2])
+    a.kbar = ctypes.c_void_p(264)
+    assert lib.h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_ERR_ARG
+    assert b"aligned" in lib.bsa_last_error()
+    a.kbar = None
+    assert lib.h3_pool_route_topk_ws(ctypes.byref(a), ctypes.byref(n)) == L.BSA_OK
+    assert lib.h3_pool_route_topk(ctypes.byref(a), ctypes.c_void_p(256 + 8), n.value, None) == L.BSA_ERR_WORKSPACE
+    r = _route_args(qbar=ctypes.c_void_p(260))
+    assert lib.vsa_pool_route_topk_ws(ctypes.byref(r), ctypes.byref(n)) == L.BSA_ERR_ARG
+    r = _route_args()
+    assert lib.vsa_pool_route_topk_ws(ctypes.byref(r), ctypes.byref(n)) == L.BSA_OK
+    assert lib.vsa_pool_route_topk(ctypes.byref(r), ctypes.c_void_p(256 + 4), n.value, None) == L.BSA_ERR_WORKSPACE
+
+
 def _kv_args(**kw):
     dq = L.TDesc(1, 256, 8, 128, 256 * 8 * 128, 8 * 128, 128)
     dkv = L.TDesc(1, 256, 2, 128, 256 * 2 * 128, 2 * 128, 128)

@@ -172,6 +172,9 @@ ATTN_CFGS = {
     "video_m128_ragged": scaled("video", grid=(10, 20, 18), block=(4, 8, 4), h=2, R=5),
     "video_m128_b2": scaled("video", B=2, grid=(8, 16, 16), block=(4, 8, 4), h=2, R=4),
     "tiny_f32_m128": scaled("tiny", grid=(8, 8, 8), block=(4, 8, 4), R=2),
+    # bf16 at capacities 16 and 32 with D = 64
+    "video_m16_bf16": scaled("video", grid=(8, 10, 12), block=(2, 2, 4), h=2, R=9),
+    "video_m32_d64": scaled("video", grid=(8, 12, 16), block=(2, 4, 4), h=2, D=64, R=10),
 }
 
 
